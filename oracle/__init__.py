@@ -1,0 +1,321 @@
+"""CPU oracle for the compressed-index matmul -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, float64 numpy statements of what the hot path computes, written
+from the two source pages:
+
+* orka README (github.com/orkait/orka.py), section "How it works": each group of
+  8 weights is replaced by an index into a per-tensor codebook, the indices
+  are stored as 12-bit bit-planes (a low-byte plane plus a plane of packed
+  high nibbles), and a group is decoded as the scale times the sum of the
+  codebook entries it indexes (one entry per residual stage).
+* GLQ PyPI page ("GLQ -- fit larger LLMs on smaller GPUs"), sections
+  "Inference kernels" (the product Y = X dequant(W)^T taken without forming W;
+  each output row walks its K/8 codebook groups), "How it works" (randomized
+  Hadamard transform = random sign flips followed by a fast Walsh-Hadamard
+  transform; block-diagonal for large layers) and "Bit widths" (non-power-of-2
+  sizes use a block-diagonal FHT built from power-of-2 blocks; 16-bit indices
+  into a 65,536-entry codebook).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
+leg may import this package.  It shares no code with the HIP library and
+imports nothing from it.
+
+Every function below is pinned by ``tests/test_oracle_*.py`` against closed
+forms, hand-computed fixtures (``tests/golden/``), exact rational brute force,
+or an independent library routine (``scipy.linalg.hadamard``, Python's
+``struct`` half-float packing).  Where the pages leave a step open, the
+reading taken is stated in the docstring.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Sequence
+
+import numpy as np
+
+__all__ = [
+    "GROUP",
+    "unpack_indices",
+    "pack_indices",
+    "n_scale_blocks",
+    "dequant_exact",
+    "dequant_fp16",
+    "matmul_ref",
+    "within_tolerance",
+    "rht_blocks",
+    "fwht",
+    "rht_ref",
+    "compressed_bytes",
+    "bits_per_weight",
+    "MATMUL_RTOL",
+    "MATMUL_ATOL",
+]
+
+#: Weights per codebook group (orka README, "How it works": groups of 8).
+GROUP = 8
+
+#: Matmul acceptance bound |y - y_ref| <= MATMUL_RTOL * sum|w x| + MATMUL_ATOL.
+MATMUL_RTOL = 2e-3
+MATMUL_ATOL = 1e-6
+
+
+# --------------------------------------------------------------------------
+# c-1  index storage: bit-plane unpack
+# --------------------------------------------------------------------------
+
+def unpack_indices(bits: int, n_groups: int, lo=None, hi=None, idx16=None) -> np.ndarray:
+    """Recover the codebook index of each of ``n_groups`` groups (flat order).
+
+    orka README, "How it works": 12-bit indices are stored as bit-planes, a
+    low-byte plane plus packed high bits.  Readings taken (the page is silent):
+
+    * two planes, not twelve one-bit planes: ``lo`` holds bits 0..7 of every
+      index, one byte per group; ``hi`` holds bits 8..11, two groups per byte;
+    * group ``f`` uses the low nibble of ``hi[f // 2]`` when ``f`` is even and
+      the high nibble when ``f`` is odd;
+    * an 8-bit index is the ``lo`` plane alone;
+    * a 16-bit index (GLQ "How it works": one 16-bit index per 8 weights into
+      a 65,536-entry codebook) is a little-endian uint16 array ``idx16``.
+
+    Groups are numbered row-major: group ``g`` of output row ``r`` is
+    ``f = r * (K // 8) + g``.
+    """
+    out = np.empty(n_groups, dtype=np.int64)
+    if bits == 8:
+        out[:] = np.asarray(lo, dtype=np.uint8)[:n_groups].astype(np.int64)
+    elif bits == 12:
+        lo = np.asarray(lo, dtype=np.uint8)
+        hi = np.asarray(hi, dtype=np.uint8)
+        f = np.arange(n_groups)
+        low = lo[:n_groups].astype(np.int64)
+        hib = hi[f // 2].astype(np.int64)
+        nib = np.where(f % 2 == 0, hib & 0xF, (hib >> 4) & 0xF)
+        out[:] = low + nib * 256
+    elif bits == 16:
+        arr = np.asarray(idx16)
+        if arr.dtype != np.uint16:
+            raise TypeError("16-bit indices must be a uint16 array")
+        out[:] = arr[:n_groups].astype(np.int64)
+    else:
+        raise ValueError(f"unsupported index width {bits}")
+    return out
+
+
+def pack_indices(idx: Sequence[int], bits: int):
+    """Inverse of :func:`unpack_indices` (used to build structured test inputs).
+
+    Returns ``(lo, hi)`` for 8/12-bit (``hi`` is None for 8-bit) or
+    ``(idx16, None)`` for 16-bit.  For an odd number of 12-bit groups the
+    unused high nibble of the last ``hi`` byte is zero.
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    if idx.size and (idx.min() < 0 or idx.max() >= (1 << bits)):
+        raise ValueError("index out of range for the width")
+    if bits == 8:
+        return idx.astype(np.uint8), None
+    if bits == 16:
+        return idx.astype(np.uint16), None
+    if bits != 12:
+        raise ValueError(f"unsupported index width {bits}")
+    n = idx.size
+    lo = (idx % 256).astype(np.uint8)
+    nib = np.zeros(2 * ((n + 1) // 2), dtype=np.int64)
+    nib[:n] = idx // 256
+    hi = (nib[0::2] + 16 * nib[1::2]).astype(np.uint8)   # even group -> low nibble
+    return lo, hi
+
+
+# --------------------------------------------------------------------------
+# c-2  dequant
+# --------------------------------------------------------------------------
+
+def n_scale_blocks(k_in: int, scale_block: int) -> int:
+    """Scales per row: one per ``scale_block`` input columns, the last block
+    possibly short (ceil reading; e.g. K=576 with 128-column blocks gives 5)."""
+    return -(-k_in // scale_block)
+
+
+def dequant_exact(n_out: int, k_in: int, indices: Sequence[np.ndarray],
+                  codebooks: Sequence[np.ndarray], scales: np.ndarray,
+                  scale_block: int) -> np.ndarray:
+    """Exact dequantized weight, float64, shape ``[n_out, k_in]``.
+
+    orka README, "How it works": a group decodes to the scale times the sum of
+    its codebook entries; with residual stages t = 0..S-1 (orka's RVQ, GLQ
+    "Bit widths" residual stages) this is
+
+        w[r, 8g + j] = s[r, (8g) // scale_block] * sum_t cb_t[idx_t[r, g], j].
+
+    Readings: the scale multiplies the stage sum; one block scale is shared by
+    all stages; there is no separate residual scale.  All values are fp16, so
+    the sum of at most four of them and its product with an fp16 scale are
+    exact in float64 -- the result does not depend on summation order (the
+    sign of an exact zero included: it is -0 only when every term is -0).
+    """
+    if k_in % GROUP:
+        raise ValueError("k_in must be a multiple of 8")
+    g_per_row = k_in // GROUP
+    s = np.asarray(scales, dtype=np.float16).astype(np.float64).reshape(n_out, -1)
+    acc = None
+    for idx, cb in zip(indices, codebooks):
+        cb64 = np.asarray(cb, dtype=np.float16).astype(np.float64).reshape(-1, GROUP)
+        ix = np.asarray(idx, dtype=np.int64).reshape(n_out, g_per_row)
+        term = cb64[ix]
+        # The sum starts from stage 0's entry itself (not from +0), so a lone
+        # -0.0 entry stays -0.0; an exact zero sum of mixed-sign terms is +0.
+        acc = term if acc is None else acc + term
+    if acc is None:
+        raise ValueError("at least one stage is required")
+    w = np.empty((n_out, k_in), dtype=np.float64)
+    for g in range(g_per_row):
+        blk = (GROUP * g) // scale_block
+        w[:, GROUP * g:GROUP * (g + 1)] = s[:, blk:blk + 1] * acc[:, g, :]
+    return w
+
+
+def dequant_fp16(n_out, k_in, indices, codebooks, scales, scale_block) -> np.ndarray:
+    """fp16 dequantized weight: the exact value rounded once to nearest-even.
+
+    Reading: the pages fix no rounding; the result is the exact float64 value
+    of :func:`dequant_exact` converted once to IEEE binary16 with
+    round-to-nearest-even (numpy's float64 -> float16 cast rounds once; the
+    tests check it against Python's own half-float packing).  Subnormals are
+    kept, overflow gives +/-inf, a zero result keeps the sign IEEE gives it.
+    """
+    return dequant_exact(n_out, k_in, indices, codebooks, scales, scale_block).astype(np.float16)
+
+
+# --------------------------------------------------------------------------
+# c-3  matmul
+# --------------------------------------------------------------------------
+
+def matmul_ref(w64: np.ndarray, x: np.ndarray):
+    """``Y = X dequant(W)^T`` (GLQ "Inference kernels") in float64.
+
+    ``w64`` is the exact dequantized weight [N, K]; ``x`` is [B, K] (any float
+    dtype; bf16/fp32 inputs are exact in float64).  Returns ``(y, bound)``
+    where ``bound[b, r] = sum_k |w[r, k] * x[b, k]|`` is the scale of the
+    acceptance test of :func:`within_tolerance`.
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    if x64.ndim == 1:
+        x64 = x64[None, :]
+    w64 = np.asarray(w64, dtype=np.float64)
+    y = x64 @ w64.T
+    bound = np.abs(x64) @ np.abs(w64).T
+    return y, bound
+
+
+def within_tolerance(y, y_ref, bound, rtol: float = MATMUL_RTOL, atol: float = MATMUL_ATOL):
+    """Per-output acceptance: |y - y_ref| <= rtol * bound + atol.  Returns a
+    boolean array and the worst ratio |y - y_ref| / (rtol * bound + atol)."""
+    y = np.asarray(y, dtype=np.float64)
+    lim = rtol * np.asarray(bound, dtype=np.float64) + atol
+    err = np.abs(y - np.asarray(y_ref, dtype=np.float64))
+    ok = err <= lim
+    worst = float(np.max(err / lim)) if err.size else 0.0
+    return ok, worst
+
+
+# --------------------------------------------------------------------------
+# c-4  randomized Hadamard transform on the input
+# --------------------------------------------------------------------------
+
+def rht_blocks(n: int, max_block: int):
+    """Block sizes of the block-diagonal transform for a length-``n`` vector.
+
+    GLQ "Bit widths": a size that is not a power of two is split into
+    power-of-two blocks (their example: 2688 = 2048 + 512 + 128).  Reading:
+    greedy largest-first decomposition with every block capped at
+    ``max_block`` (so 28672 with an 8192 cap is 8192, 8192, 8192, 4096).
+    """
+    if n <= 0:
+        raise ValueError("n must be positive")
+    if max_block <= 0 or (max_block & (max_block - 1)):
+        raise ValueError("max_block must be a power of two")
+    blocks = []
+    rest = n
+    while rest:
+        b = min(max_block, 1 << (rest.bit_length() - 1))
+        blocks.append(b)
+        rest -= b
+    return blocks
+
+
+def fwht(v: np.ndarray) -> np.ndarray:
+    """Orthonormal fast Walsh-Hadamard transform of a length-2^m vector,
+    float64, natural (Sylvester) order: H_1 = [1], H_2n = [[H, H], [H, -H]],
+    scaled by 1/sqrt(n) so that the transform is its own inverse."""
+    a = np.array(v, dtype=np.float64, copy=True)
+    n = a.size
+    if n & (n - 1):
+        raise ValueError("length must be a power of two")
+    h = 1
+    while h < n:
+        a = a.reshape(-1, 2, h)
+        top = a[:, 0, :] + a[:, 1, :]
+        bot = a[:, 0, :] - a[:, 1, :]
+        a = np.stack([top, bot], axis=1).reshape(n)
+        h *= 2
+    return a / math.sqrt(n)
+
+
+def rht_ref(x: np.ndarray, signs: np.ndarray, max_block: int) -> np.ndarray:
+    """Randomized Hadamard transform of each row of ``x`` [B, n], float64.
+
+    GLQ "How it works": random sign flips, then a fast Walsh-Hadamard
+    transform, block-diagonal for large sizes.  Readings: signs are applied
+    first (x' = blockdiag(H_n1, ..., H_nm) (sigma * x)); each block uses the
+    orthonormal Sylvester-order transform of :func:`fwht`; blocks follow
+    :func:`rht_blocks`.
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    if x64.ndim == 1:
+        x64 = x64[None, :]
+    sg = np.asarray(signs, dtype=np.float64)
+    n = x64.shape[1]
+    out = np.empty_like(x64)
+    for b in range(x64.shape[0]):
+        v = x64[b] * sg
+        off = 0
+        for blk in rht_blocks(n, max_block):
+            out[b, off:off + blk] = fwht(v[off:off + blk])
+            off += blk
+    return out
+
+
+# --------------------------------------------------------------------------
+# c-5  storage cost
+# --------------------------------------------------------------------------
+
+def compressed_bytes(n_out: int, k_in: int, n_stages: int, bits: int, scale_block: int,
+                     include_codebooks: bool = True) -> int:
+    """Bytes of the stored weight: index planes, fp16 scales and (optionally)
+    the fp16 codebooks, each counted once.
+
+    Per stage: 12-bit = one byte per group plus one byte per two groups
+    (ceil), 8-bit = one byte per group, 16-bit = two bytes per group.
+    """
+    groups = n_out * (k_in // GROUP)
+    if bits == 8:
+        per_stage = groups
+    elif bits == 12:
+        per_stage = groups + (groups + 1) // 2
+    elif bits == 16:
+        per_stage = 2 * groups
+    else:
+        raise ValueError(f"unsupported index width {bits}")
+    total = n_stages * per_stage + 2 * n_out * n_scale_blocks(k_in, scale_block)
+    if include_codebooks:
+        total += n_stages * (1 << bits) * GROUP * 2
+    return total
+
+
+def bits_per_weight(n_out: int, k_in: int, n_stages: int, bits: int, scale_block: int,
+                    include_codebooks: bool = False) -> float:
+    """Stored bits per weight: S*b/8 for the indices (12 bits per 8 weights is
+    1.5 per stage) plus 16 bits per scale block, plus optionally the
+    codebooks spread over the tensor."""
+    return 8.0 * compressed_bytes(n_out, k_in, n_stages, bits, scale_block,
+                                  include_codebooks) / (n_out * k_in)
