@@ -1,0 +1,85 @@
+// Standalone bit-plane unpack + exact dequant to fp16 (orka README, "How it
+// works": indices stored as a low-byte plane plus packed high nibbles; a
+// group decodes to scale x sum of its stages' codebook entries).
+//
+// One thread per group.  The stage sum and the product with the scale are
+// formed in float64, where they are exact (at most four fp16 terms and an
+// fp16 factor need < 53 significant bits), and rounded once to fp16 with
+// integer arithmetic on the bit pattern, so the result is the correctly
+// rounded value whatever the summation order.  Write-bandwidth bound.
+#include "vqmm_device.h"
+#include "vqmm_internal.h"
+
+namespace vqmm {
+
+struct DequantArgs {
+  const uint8_t *lo[VQ_MAX_STAGES];
+  const uint8_t *hi[VQ_MAX_STAGES];
+  const uint16_t *i16[VQ_MAX_STAGES];
+  const uint16_t *cb[VQ_MAX_STAGES];
+  const uint16_t *sc;
+  uint16_t *idx_out;  // [S][N*G] or null
+  uint16_t *w_out;    // [N][K] or null
+  int64_t total;      // N * G
+  int G, S, bits, bs, nblk, k;
+};
+
+template <int BITS>
+__global__ __launch_bounds__(256) void k_unpack_dequant(DequantArgs a) {
+  const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (f >= a.total) return;
+  const int64_t r = f / a.G;
+  const int g = (int)(f - r * a.G);
+  double acc[8];
+  for (int t = 0; t < a.S; ++t) {
+    uint32_t idx = load_index(BITS, a.lo[t], a.hi[t], a.i16[t], (size_t)f);
+    if (a.idx_out) a.idx_out[(int64_t)t * a.total + f] = (uint16_t)idx;
+    if (a.w_out) {
+      const uint4 v = reinterpret_cast<const uint4 *>(a.cb[t])[idx];
+      const uint32_t h[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        double c = (double)h2f((h[j >> 1] >> ((j & 1) * 16)) & 0xffffu);
+        acc[j] = (t == 0) ? c : acc[j] + c;  // exact: sum starts at stage 0
+      }
+    }
+  }
+  if (!a.w_out) return;
+  const double s = (double)h2f(a.sc[r * a.nblk + (8 * g) / a.bs]);
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    o[j] = f64_to_f16_rne(s * acc[2 * j]) | (f64_to_f16_rne(s * acc[2 * j + 1]) << 16);
+  }
+  reinterpret_cast<uint4 *>(a.w_out + r * (int64_t)a.k)[g] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+hipError_t launch_unpack_dequant(const WView &w, uint16_t *idx_out, uint16_t *w_out, hipStream_t s) {
+  DequantArgs a{};
+  for (int t = 0; t < VQ_MAX_STAGES; ++t) {
+    a.lo[t] = w.lo[t];
+    a.hi[t] = w.hi[t];
+    a.i16[t] = w.i16[t];
+    a.cb[t] = w.cb[t];
+  }
+  a.sc = w.sc;
+  a.idx_out = idx_out;
+  a.w_out = w_out;
+  a.total = (int64_t)w.n * w.G;
+  a.G = w.G;
+  a.S = w.S;
+  a.bits = w.bits;
+  a.bs = w.bs;
+  a.nblk = w.nblk;
+  a.k = w.k;
+  const unsigned blocks = (unsigned)((a.total + 255) / 256);
+  if (w.bits == 8)
+    hipLaunchKernelGGL(k_unpack_dequant<8>, dim3(blocks), dim3(256), 0, s, a);
+  else if (w.bits == 12)
+    hipLaunchKernelGGL(k_unpack_dequant<12>, dim3(blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_unpack_dequant<16>, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace vqmm

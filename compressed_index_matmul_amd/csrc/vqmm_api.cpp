@@ -1,0 +1,172 @@
+// C ABI of libvqmm: argument validation (host only, before any HIP call),
+// dispatch to the kernel launchers, status mapping.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <mutex>
+
+#include "vqmm_internal.h"
+
+namespace vqmm {
+
+// Launchers that live in other translation units.
+hipError_t launch_gemv_token(const WView &w, const void *x, int xt, float *y, hipStream_t s);
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_cu_once[kMaxDevices];
+int g_cu_count[kMaxDevices];
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Full descriptor check; fills `v` on success.  Touches no device state.
+int check_weight(const vq_weight *w, WView *v) {
+  if (!w) return VQ_ERR_NULL;
+  if (w->n_out < 1 || w->k_in < 8 || (w->k_in % 8) != 0) return VQ_ERR_SHAPE;
+  if ((int64_t)w->n_out * w->k_in >= ((int64_t)1 << 31)) return VQ_ERR_SHAPE;
+  if (w->n_stages < 1 || w->n_stages > VQ_MAX_STAGES) return VQ_ERR_SHAPE;
+  if (w->idx_bits != 8 && w->idx_bits != 12 && w->idx_bits != 16) return VQ_ERR_UNSUPPORTED;
+  if (w->scale_block < 8 || (w->scale_block % 8) != 0) return VQ_ERR_SHAPE;
+  for (int t = 0; t < w->n_stages; ++t) {
+    if (!w->codebook[t]) return VQ_ERR_NULL;
+    if (!aligned16(w->codebook[t])) return VQ_ERR_ALIGN;
+    if (w->idx_bits == 16) {
+      if (!w->idx16[t]) return VQ_ERR_NULL;
+      if (!aligned16(w->idx16[t])) return VQ_ERR_ALIGN;
+    } else {
+      if (!w->idx_lo[t]) return VQ_ERR_NULL;
+      if (!aligned16(w->idx_lo[t])) return VQ_ERR_ALIGN;
+      if (w->idx_bits == 12) {
+        if (!w->idx_hi[t]) return VQ_ERR_NULL;
+        if (!aligned16(w->idx_hi[t])) return VQ_ERR_ALIGN;
+      }
+    }
+  }
+  if (!w->scales) return VQ_ERR_NULL;
+  if (!aligned16(w->scales)) return VQ_ERR_ALIGN;
+  if (v) {
+    *v = WView{};
+    v->n = w->n_out;
+    v->k = w->k_in;
+    v->G = w->k_in / 8;
+    v->S = w->n_stages;
+    v->bits = w->idx_bits;
+    v->bs = w->scale_block > w->k_in ? w->k_in : w->scale_block;
+    v->nblk = (w->k_in + v->bs - 1) / v->bs;
+    for (int t = 0; t < w->n_stages; ++t) {
+      v->lo[t] = w->idx_lo[t];
+      v->hi[t] = w->idx_hi[t];
+      v->i16[t] = w->idx16[t];
+      v->cb[t] = w->codebook[t];
+    }
+    v->sc = w->scales;
+  }
+  return VQ_OK;
+}
+
+int map_hip(hipError_t e) { return e == hipSuccess ? VQ_OK : VQ_ERR_HIP; }
+
+}  // namespace
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  std::call_once(g_cu_once[dev], [dev]() {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    g_cu_count[dev] = n;
+  });
+  return g_cu_count[dev];
+}
+
+}  // namespace vqmm
+
+using namespace vqmm;
+
+extern "C" {
+
+int vq_version(void) { return VQMM_VERSION; }
+
+const char *vq_status_string(int status) {
+  switch (status) {
+    case VQ_OK: return "ok";
+    case VQ_ERR_NULL: return "a required pointer is NULL";
+    case VQ_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case VQ_ERR_DTYPE: return "unsupported element type";
+    case VQ_ERR_UNSUPPORTED: return "request outside what the kernels implement";
+    case VQ_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
+    case VQ_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int vq_validate(const vq_weight *w) { return check_weight(w, nullptr); }
+
+int64_t vq_compressed_bytes(const vq_weight *w) {
+  WView v;
+  const int st = check_weight(w, &v);
+  if (st != VQ_OK) return st;
+  const int64_t groups = (int64_t)v.n * v.G;
+  int64_t per_stage;
+  if (v.bits == 8) per_stage = groups;
+  else if (v.bits == 12) per_stage = groups + (groups + 1) / 2;
+  else per_stage = 2 * groups;
+  return v.S * per_stage + 2 * (int64_t)v.n * v.nblk + (int64_t)v.S * ((int64_t)1 << v.bits) * 16;
+}
+
+int vq_unpack_dequant(const vq_weight *w, uint16_t *idx_out, uint16_t *w_out, void *stream) {
+  WView v;
+  int st = check_weight(w, &v);
+  if (st != VQ_OK) return st;
+  if (!idx_out && !w_out) return VQ_ERR_NULL;
+  if ((idx_out && !aligned16(idx_out)) || (w_out && !aligned16(w_out))) return VQ_ERR_ALIGN;
+  return map_hip(launch_unpack_dequant(v, idx_out, w_out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, float *y, void *stream) {
+  WView v;
+  int st = check_weight(w, &v);
+  if (st != VQ_OK) return st;
+  if (!x || !y) return VQ_ERR_NULL;
+  if (x_dtype != VQ_F32 && x_dtype != VQ_BF16) return VQ_ERR_DTYPE;
+  if (batch < 1 || batch > 16) return VQ_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(y)) return VQ_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (batch > 1 && x_dtype == VQ_BF16) {
+    return map_hip(launch_gemm(v, reinterpret_cast<const uint16_t *>(x), batch, y, s));
+  }
+  const size_t esz = x_dtype == VQ_F32 ? 4 : 2;
+  for (int b = 0; b < batch; ++b) {
+    const void *xb = reinterpret_cast<const char *>(x) + (size_t)b * v.k * esz;
+    st = map_hip(launch_gemv_token(v, xb, x_dtype, y + (size_t)b * v.n, s));
+    if (st != VQ_OK) return st;
+  }
+  return VQ_OK;
+}
+
+int vq_gemm(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float *y, void *stream) {
+  WView v;
+  int st = check_weight(w, &v);
+  if (st != VQ_OK) return st;
+  if (!x_bf16 || !y) return VQ_ERR_NULL;
+  if (m < 1) return VQ_ERR_SHAPE;
+  if ((int64_t)m * v.k >= ((int64_t)1 << 31) || (int64_t)m * v.n >= ((int64_t)1 << 31)) return VQ_ERR_SHAPE;
+  if (!aligned16(x_bf16) || !aligned16(y)) return VQ_ERR_ALIGN;
+  return map_hip(launch_gemm(v, x_bf16, m, y, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int rht_apply(const void *x, int32_t x_dtype, int32_t batch, int32_t n, const int8_t *signs,
+              int32_t max_block, float *out, void *stream) {
+  if (!x || !signs || !out) return VQ_ERR_NULL;
+  if (x_dtype != VQ_F32 && x_dtype != VQ_BF16) return VQ_ERR_DTYPE;
+  if (batch < 1 || n < 1) return VQ_ERR_SHAPE;
+  if (max_block < 1 || max_block > 16384 || (max_block & (max_block - 1)) != 0) return VQ_ERR_SHAPE;
+  if ((int64_t)batch * n >= ((int64_t)1 << 31)) return VQ_ERR_SHAPE;
+  const int64_t nblocks = n / max_block + __builtin_popcount((unsigned)(n % max_block));
+  if (nblocks * batch >= ((int64_t)1 << 31)) return VQ_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(out)) return VQ_ERR_ALIGN;
+  return map_hip(launch_rht(x, x_dtype, batch, n, signs, max_block, out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

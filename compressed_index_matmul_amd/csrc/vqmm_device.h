@@ -1,0 +1,87 @@
+// Device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace vqmm {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float h2f(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+
+// Exact double -> IEEE binary16 bits with one rounding to nearest, ties to
+// even.  Subnormal results are kept, magnitudes that round past 65504 give
+// infinity, the sign of zero is kept.  Integer arithmetic on the bit pattern,
+// so there is no intermediate rounding.
+__device__ __forceinline__ uint32_t f64_to_f16_rne(double d) {
+  uint64_t b = (uint64_t)__double_as_longlong(d);
+  uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
+  b &= 0x7fffffffffffffffull;
+  if (b >= 0x7ff0000000000000ull) {  // inf or NaN
+    return sign | 0x7c00u | (b > 0x7ff0000000000000ull ? 0x200u : 0u);
+  }
+  int e = (int)(b >> 52) - 1023;
+  if (e < -25) return sign;  // |d| < 2^-25: rounds to zero
+  if (e > 15) return sign | 0x7c00u;
+  uint64_t m = (b & 0x000fffffffffffffull) | 0x0010000000000000ull;
+  int E = e < -14 ? -14 : e;
+  int shift = 42 + (E - e);  // keep units of 2^(E-10)
+  uint64_t n = m >> shift;
+  uint64_t rem = m & ((1ull << shift) - 1);
+  uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (n & 1ull))) ++n;
+  if (n == 2048) {
+    n = 1024;
+    ++E;
+  }
+  if (E > 15) return sign | 0x7c00u;
+  if (n < 1024) return sign | (uint32_t)n;  // subnormal
+  return sign | ((uint32_t)(E + 15) << 10) | (uint32_t)(n - 1024);
+}
+
+// Sum over the 64 lanes of a wave in a fixed order (DPP within rows of 16,
+// then the four row totals added lane 0 + 16 + 32 + 48).  Result valid in
+// every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));  // quad_perm [2,3,0,1]
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true)); // row_half_mirror
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true)); // row_mirror
+  float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// Index of flat group f of stage planes (any width).
+__device__ __forceinline__ uint32_t load_index(int bits, const uint8_t *lo, const uint8_t *hi,
+                                               const uint16_t *i16, size_t f) {
+  if (bits == 16) return i16[f];
+  uint32_t v = lo[f];
+  if (bits == 12) v |= ((uint32_t)(hi[f >> 1] >> ((f & 1) * 4)) & 0xfu) << 8;
+  return v;
+}
+
+}  // namespace vqmm

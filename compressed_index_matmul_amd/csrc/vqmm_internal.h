@@ -1,0 +1,38 @@
+// Internal interface between the C-ABI layer (vqmm_api.cpp) and the kernel
+// launchers.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/vqmm.h"
+
+namespace vqmm {
+
+// Validated, flattened view of a vq_weight.
+struct WView {
+  int n;      // n_out
+  int k;      // k_in
+  int G;      // groups per row = k / 8
+  int S;      // stages
+  int bits;   // 8, 12, 16
+  int bs;     // scale_block (clamped to k when larger)
+  int nblk;   // scales per row
+  const uint8_t *lo[VQ_MAX_STAGES];
+  const uint8_t *hi[VQ_MAX_STAGES];
+  const uint16_t *i16[VQ_MAX_STAGES];
+  const uint16_t *cb[VQ_MAX_STAGES];
+  const uint16_t *sc;
+};
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+hipError_t launch_unpack_dequant(const WView &w, uint16_t *idx_out, uint16_t *w_out, hipStream_t s);
+hipError_t launch_rht(const void *x, int xt, int batch, int n, const int8_t *signs, int max_block,
+                      float *out, hipStream_t s);
+hipError_t launch_gemv(const WView &w, const void *x, int xt, int batch, float *y, hipStream_t s);
+hipError_t launch_gemm(const WView &w, const uint16_t *x, int m, float *y, hipStream_t s);
+
+}  // namespace vqmm

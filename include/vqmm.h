@@ -1,0 +1,165 @@
+/*
+ * vqmm.h -- C ABI of libvqmm, the MI355X (gfx950) compressed-index matmul.
+ *
+ * A linear layer's weight W [n_out, k_in] (nn.Linear layout) is stored as
+ * vector-quantization codebook indices: every group of 8 consecutive
+ * input-dim weights of a row is one index per residual stage into that
+ * stage's per-tensor codebook of 8-wide fp16 vectors, and a group decodes to
+ *
+ *     w[r, 8g + j] = s[r, (8g) / scale_block] * sum_t codebook_t[idx_t[r, g]][j]
+ *
+ * (orka README, "How it works": groups of 8 weights, per-tensor codebooks,
+ * indices stored as 12-bit bit-planes, decode = scale times the sum of the
+ * indexed codebook entries; GLQ page, "How it works" / "Bit widths": 16-bit
+ * indices into a 65,536-entry codebook, residual stages).  The products below
+ * take Y = X dequant(W)^T without writing the dense W to memory (GLQ page,
+ * "Inference kernels").
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are device pointers owned by the caller; the library
+ *    never frees them and keeps no reference after the call returns.  Base
+ *    pointers must be 16-byte aligned (VQ_ERR_ALIGN otherwise).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *    is enqueued asynchronously on it; the call returns before it finishes.
+ *    Inputs and outputs must not alias.
+ *  - Every argument is validated on the host before any HIP call, so invalid
+ *    arguments return an error with nothing enqueued and no device touched.
+ *    A failed launch returns VQ_ERR_HIP.  No C++ exception crosses the ABI.
+ *  - The library allocates no device memory and holds no per-call state;
+ *    calls on different streams may run concurrently.
+ *  - Results are deterministic: fixed reduction order, no atomics.
+ */
+#ifndef VQMM_H
+#define VQMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VQMM_VERSION 1
+#define VQ_MAX_STAGES 4
+
+/* Status codes returned by every entry point. */
+typedef enum vq_status {
+  VQ_OK = 0,
+  VQ_ERR_NULL = -1,        /* a required pointer is NULL */
+  VQ_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+  VQ_ERR_DTYPE = -3,       /* unsupported element type for this argument */
+  VQ_ERR_UNSUPPORTED = -4, /* valid request outside what the kernels implement */
+  VQ_ERR_ALIGN = -5,       /* a base pointer is not 16-byte aligned */
+  VQ_ERR_HIP = -6          /* the HIP runtime reported an error */
+} vq_status;
+
+/* Element types of activations. */
+typedef enum vq_dtype { VQ_F32 = 0, VQ_BF16 = 1 } vq_dtype;
+
+/*
+ * Descriptor of one compressed weight (all pointers device memory).
+ *
+ * Groups are numbered row-major: group g of output row r is f = r*(k_in/8)+g.
+ * Per stage t < n_stages, by idx_bits:
+ *   8  : idx_lo[t]  uint8  [n_out*k_in/8]        index = idx_lo[t][f]
+ *   12 : idx_lo[t]  uint8  [n_out*k_in/8]        bits 0..7 of index f
+ *        idx_hi[t]  uint8  [ceil(n_out*k_in/16)] bits 8..11: low nibble of
+ *                   idx_hi[t][f/2] for even f, high nibble for odd f
+ *        (orka README, "How it works": 12-bit bit-planes, a low byte plus
+ *        packed high bits; the nibble order is this library's reading)
+ *   16 : idx16[t]   uint16 [n_out*k_in/8]        little-endian index
+ *        (GLQ page, "How it works": one 16-bit index per 8 weights)
+ * codebook[t] : fp16 bits [2^idx_bits][8], row-major.
+ * scales      : fp16 bits [n_out][ceil(k_in/scale_block)]; column c of row r
+ *               uses scales[r][c / scale_block].  scale_block >= k_in means
+ *               one scale per row.
+ * Unused pointer slots are ignored.
+ */
+typedef struct vq_weight {
+  int32_t n_out;       /* N >= 1 */
+  int32_t k_in;        /* K >= 8, K % 8 == 0; n_out*k_in < 2^31 */
+  int32_t n_stages;    /* 1..4 */
+  int32_t idx_bits;    /* 8, 12 or 16, the same for every stage */
+  int32_t scale_block; /* columns per scale, >= 8 and a multiple of 8 */
+  int32_t reserved;    /* set to 0 */
+  const uint8_t *idx_lo[VQ_MAX_STAGES];
+  const uint8_t *idx_hi[VQ_MAX_STAGES];
+  const uint16_t *idx16[VQ_MAX_STAGES];
+  const uint16_t *codebook[VQ_MAX_STAGES];
+  const uint16_t *scales;
+} vq_weight;
+
+/* Library version (VQMM_VERSION).  Host only. */
+int vq_version(void);
+
+/* Static text for a status code.  Host only. */
+const char *vq_status_string(int status);
+
+/* Validate a descriptor without touching the device.  Returns VQ_OK or the
+ * error the compute entry points would return for it.  Host only. */
+int vq_validate(const vq_weight *w);
+
+/* Stored bytes of the weight: index planes + fp16 scales + fp16 codebooks,
+ * each counted once (12-bit: 1.5 bytes per group per stage, rounded up per
+ * plane; 8-bit: 1; 16-bit: 2).  Negative vq_status on an invalid
+ * descriptor.  Host only. */
+int64_t vq_compressed_bytes(const vq_weight *w);
+
+/*
+ * Unpack and/or dequantize the whole weight (orka README, "How it works":
+ * bit-plane storage and the scale-times-sum decode).  Not on the matmul path;
+ * it exists to check the format and for callers that want the dense weight.
+ *   idx_out : uint16 [n_stages][n_out][k_in/8] unpacked indices, or NULL
+ *   w_out   : fp16 bits [n_out][k_in], or NULL.  Each weight is the exact
+ *             value of the decode formula rounded once to fp16 (nearest,
+ *             ties to even; subnormals kept, overflow to +-inf).
+ * At least one output must be non-NULL.  Bit-exact.
+ */
+int vq_unpack_dequant(const vq_weight *w, uint16_t *idx_out, uint16_t *w_out, void *stream);
+
+/*
+ * Decode-style product y = x dequant(W)^T for 1..16 tokens (GLQ page,
+ * "Inference kernels": each output row walks its k_in/8 groups, gathering
+ * codebook vectors; B = 1 is a matrix-vector product).
+ *   x     : [batch][k_in], VQ_F32 (float) or VQ_BF16 (bf16 bits)
+ *   batch : 1..16
+ *   y     : float [batch][n_out]
+ * Accumulation is fp32; every output satisfies
+ * |y - y_exact| <= 2e-3 * sum_k |w x| + 1e-6 against the exact product.
+ */
+int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, float *y,
+            void *stream);
+
+/*
+ * Many-token product y = x dequant(W)^T (GLQ page, "Inference kernels":
+ * tensor-core path for batched inputs).  Decoded weight tiles are rounded to
+ * bf16 on chip and multiplied on bf16 matrix cores with fp32 accumulation.
+ *   x : bf16 bits [m][k_in];  m >= 1
+ *   y : float [m][n_out]
+ * Same per-output error bound as vq_gemv.
+ */
+int vq_gemm(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float *y, void *stream);
+
+/*
+ * Randomized Hadamard transform of each row of x (GLQ page, "How it works":
+ * random sign flips followed by a fast Walsh-Hadamard transform; "Bit
+ * widths": block-diagonal over power-of-two blocks for other sizes):
+ *   out[b] = blockdiag(H_n1, H_n2, ...) (signs * x[b]),
+ * H_n the orthonormal (1/sqrt(n)) Sylvester-order Hadamard matrix, blocks
+ * taken greedily largest first, each at most max_block (28672 with 8192 ->
+ * 8192, 8192, 8192, 4096).
+ *   x         : [batch][n], VQ_F32 or VQ_BF16
+ *   signs     : int8 [n], each +1 or -1
+ *   max_block : power of two, 1..16384
+ *   out       : float [batch][n]
+ * fp32 butterflies; |out - exact| <= (log2(nb) + 2) 2^-24 ||x_block||_2 * 1.01
+ * elementwise within each block of size nb.
+ */
+int rht_apply(const void *x, int32_t x_dtype, int32_t batch, int32_t n, const int8_t *signs,
+              int32_t max_block, float *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VQMM_H */

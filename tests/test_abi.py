@@ -1,0 +1,170 @@
+"""The C-ABI library loads without a GPU, exports every symbol the header
+declares, and rejects every invalid argument on the host before touching the
+device (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import vqsynth
+from vqtest import ROOT, ensure_built
+
+HEADER = os.path.join(ROOT, "include", "vqmm.h")
+
+VQ_OK, VQ_ERR_NULL, VQ_ERR_SHAPE, VQ_ERR_DTYPE, VQ_ERR_UNSUPPORTED, VQ_ERR_ALIGN, VQ_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
+FAKE = 0x10000  # 16-byte aligned stand-in address, never dereferenced by validation
+
+
+@pytest.fixture(scope="module")
+def L():
+    ensure_built()
+    import compressed_index_matmul_amd as vq
+    return vq.lib()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z0-9_]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    fns = header_functions()
+    for name in ("vq_unpack_dequant", "vq_gemv", "vq_gemm", "rht_apply", "vq_version",
+                 "vq_status_string", "vq_validate", "vq_compressed_bytes"):
+        assert name in fns
+
+
+def test_exports_every_declared_symbol(L):
+    import compressed_index_matmul_amd as vq
+    for name in header_functions():
+        assert hasattr(L, name), name
+    assert set(header_functions()) == set(vq.EXPORTS)
+
+
+def test_version_matches_header(L):
+    m = re.search(r"#define VQMM_VERSION (\d+)", open(HEADER).read())
+    assert L.vq_version() == int(m.group(1))
+
+
+def test_status_strings(L):
+    for st in (VQ_OK, VQ_ERR_NULL, VQ_ERR_SHAPE, VQ_ERR_DTYPE, VQ_ERR_UNSUPPORTED, VQ_ERR_ALIGN, VQ_ERR_HIP):
+        s = L.vq_status_string(st).decode()
+        assert s and s != "unknown status"
+    assert L.vq_status_string(12345).decode() == "unknown status"
+
+
+def fake_desc(n=64, k=64, stages=1, bits=12, bs=32):
+    from compressed_index_matmul_amd import VQWeightDesc
+    d = VQWeightDesc()
+    d.n_out, d.k_in, d.n_stages, d.idx_bits, d.scale_block = n, k, stages, bits, bs
+    for t in range(stages):
+        d.codebook[t] = FAKE
+        if bits == 16:
+            d.idx16[t] = FAKE
+        else:
+            d.idx_lo[t] = FAKE
+            if bits == 12:
+                d.idx_hi[t] = FAKE
+    d.scales = FAKE
+    return d
+
+
+def test_valid_descriptors(L):
+    for bits in (8, 12, 16):
+        for st in (1, 2, 3, 4):
+            d = fake_desc(stages=st, bits=bits)
+            assert L.vq_validate(ctypes.byref(d)) == VQ_OK
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda d: setattr(d, "n_out", 0), VQ_ERR_SHAPE),
+    (lambda d: setattr(d, "k_in", 12), VQ_ERR_SHAPE),
+    (lambda d: setattr(d, "k_in", 0), VQ_ERR_SHAPE),
+    (lambda d: setattr(d, "n_stages", 0), VQ_ERR_SHAPE),
+    (lambda d: setattr(d, "n_stages", 5), VQ_ERR_SHAPE),
+    (lambda d: setattr(d, "idx_bits", 10), VQ_ERR_UNSUPPORTED),
+    (lambda d: setattr(d, "scale_block", 4), VQ_ERR_SHAPE),
+    (lambda d: setattr(d, "scale_block", 20), VQ_ERR_SHAPE),
+    (lambda d: d.codebook.__setitem__(0, None), VQ_ERR_NULL),
+    (lambda d: d.idx_hi.__setitem__(0, None), VQ_ERR_NULL),
+    (lambda d: d.idx_lo.__setitem__(0, None), VQ_ERR_NULL),
+    (lambda d: setattr(d, "scales", None), VQ_ERR_NULL),
+    (lambda d: d.codebook.__setitem__(0, FAKE + 8), VQ_ERR_ALIGN),
+    (lambda d: d.idx_lo.__setitem__(0, FAKE + 4), VQ_ERR_ALIGN),
+    (lambda d: setattr(d, "scales", FAKE + 2), VQ_ERR_ALIGN),
+    (lambda d: (setattr(d, "n_out", 1 << 20), setattr(d, "k_in", 1 << 12)), VQ_ERR_SHAPE),
+])
+def test_invalid_descriptor(L, mutate, code):
+    d = fake_desc()
+    mutate(d)
+    assert L.vq_validate(ctypes.byref(d)) == code
+    # every compute entry point returns the same code, before any HIP call
+    assert L.vq_gemv(ctypes.byref(d), FAKE, 1, 1, FAKE, None) == code
+    assert L.vq_gemm(ctypes.byref(d), FAKE, 64, FAKE, None) == code
+    assert L.vq_unpack_dequant(ctypes.byref(d), FAKE, FAKE, None) == code
+    assert L.vq_compressed_bytes(ctypes.byref(d)) == code
+
+
+def test_null_descriptor(L):
+    assert L.vq_validate(None) == VQ_ERR_NULL
+    assert L.vq_gemv(None, FAKE, 1, 1, FAKE, None) == VQ_ERR_NULL
+
+
+def test_gemv_argument_checks(L):
+    d = ctypes.byref(fake_desc())
+    assert L.vq_gemv(d, None, 1, 1, FAKE, None) == VQ_ERR_NULL
+    assert L.vq_gemv(d, FAKE, 1, 1, None, None) == VQ_ERR_NULL
+    assert L.vq_gemv(d, FAKE, 7, 1, FAKE, None) == VQ_ERR_DTYPE
+    assert L.vq_gemv(d, FAKE, 1, 0, FAKE, None) == VQ_ERR_UNSUPPORTED
+    assert L.vq_gemv(d, FAKE, 1, 17, FAKE, None) == VQ_ERR_UNSUPPORTED
+    assert L.vq_gemv(d, FAKE + 2, 1, 1, FAKE, None) == VQ_ERR_ALIGN
+    assert L.vq_gemv(d, FAKE, 0, 1, FAKE + 4, None) == VQ_ERR_ALIGN
+
+
+def test_gemm_argument_checks(L):
+    d = ctypes.byref(fake_desc())
+    assert L.vq_gemm(d, None, 4, FAKE, None) == VQ_ERR_NULL
+    assert L.vq_gemm(d, FAKE, 4, None, None) == VQ_ERR_NULL
+    assert L.vq_gemm(d, FAKE, 0, FAKE, None) == VQ_ERR_SHAPE
+    assert L.vq_gemm(d, FAKE, 1 << 30, FAKE, None) == VQ_ERR_SHAPE
+    assert L.vq_gemm(d, FAKE + 2, 4, FAKE, None) == VQ_ERR_ALIGN
+
+
+def test_unpack_argument_checks(L):
+    d = ctypes.byref(fake_desc())
+    assert L.vq_unpack_dequant(d, None, None, None) == VQ_ERR_NULL
+    assert L.vq_unpack_dequant(d, FAKE + 2, None, None) == VQ_ERR_ALIGN
+    assert L.vq_unpack_dequant(d, None, FAKE + 8, None) == VQ_ERR_ALIGN
+
+
+def test_rht_argument_checks(L):
+    assert L.rht_apply(None, 0, 1, 64, FAKE, 64, FAKE, None) == VQ_ERR_NULL
+    assert L.rht_apply(FAKE, 0, 1, 64, None, 64, FAKE, None) == VQ_ERR_NULL
+    assert L.rht_apply(FAKE, 0, 1, 64, FAKE, 64, None, None) == VQ_ERR_NULL
+    assert L.rht_apply(FAKE, 5, 1, 64, FAKE, 64, FAKE, None) == VQ_ERR_DTYPE
+    assert L.rht_apply(FAKE, 0, 0, 64, FAKE, 64, FAKE, None) == VQ_ERR_SHAPE
+    assert L.rht_apply(FAKE, 0, 1, 0, FAKE, 64, FAKE, None) == VQ_ERR_SHAPE
+    assert L.rht_apply(FAKE, 0, 1, 64, FAKE, 48, FAKE, None) == VQ_ERR_SHAPE
+    assert L.rht_apply(FAKE, 0, 1, 64, FAKE, 32768, FAKE, None) == VQ_ERR_SHAPE
+    assert L.rht_apply(FAKE, 0, 1, 64, FAKE, 0, FAKE, None) == VQ_ERR_SHAPE
+    assert L.rht_apply(FAKE + 4, 0, 1, 64, FAKE, 64, FAKE, None) == VQ_ERR_ALIGN
+
+
+@pytest.mark.parametrize("wl", list(vqsynth.WORKLOADS))
+def test_compressed_bytes_match_oracle(L, wl):
+    """The library's byte count equals the oracle's closed form for every
+    workload shape (two independent implementations of the same arithmetic)."""
+    cfg = vqsynth.WORKLOADS[wl]
+    for _, n, k in cfg["shapes"]:
+        bs = k if cfg["scale_block"] is None else cfg["scale_block"]
+        d = fake_desc(n, k, cfg["stages"], cfg["bits"], bs)
+        assert L.vq_compressed_bytes(ctypes.byref(d)) == oracle.compressed_bytes(n, k, cfg["stages"], cfg["bits"], bs)
+
+
+@pytest.mark.parametrize("n,k,st,bits,bs", [(3, 24, 1, 12, 24), (5, 72, 2, 12, 16), (1, 8, 4, 8, 8), (7, 40, 3, 16, 4096)])
+def test_compressed_bytes_ragged(L, n, k, st, bits, bs):
+    d = fake_desc(n, k, st, bits, bs)
+    assert L.vq_compressed_bytes(ctypes.byref(d)) == oracle.compressed_bytes(n, k, st, bits, min(bs, k) if bs > k else bs)

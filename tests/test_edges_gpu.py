@@ -1,0 +1,173 @@
+"""Edge cases on the GPU: ragged shapes (partial tiles, odd group counts, short
+last scale block), every index width and stage count, both activation types,
+batch sizes 1..16, extreme fp16 values for the bit-exact dequant, ragged
+GEMM, transform sizes, determinism and streams."""
+import numpy as np
+import pytest
+
+import oracle
+import vqsynth
+from vqtest import assert_within, device_weight, ensure_built, oracle_indices, oracle_w16, oracle_w64, x_to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def vq():
+    ensure_built()
+    import compressed_index_matmul_amd as m
+    m.lib()
+    return m
+
+
+# (n, k, stages, bits, scale_block)
+SHAPES = [
+    (1, 8, 1, 12, 8),          # a single group: odd count, padded high nibble
+    (3, 24, 2, 12, 8),         # odd groups per row: rows start mid-byte in the hi plane
+    (37, 72, 1, 12, 16),       # K % 32 != 0 -> general path
+    (576, 576, 1, 12, 128),    # last scale block 64 columns (fast path)
+    (100, 160, 3, 12, 32),     # three 12-bit stages: codebooks do not fit LDS
+    (64, 96, 4, 8, 32),        # four 8-bit stages in LDS
+    (130, 256, 2, 16, 64),     # two 16-bit stages
+    (33, 16384, 2, 12, 128),   # eight chunks per lane on the fast path
+    (17, 8200, 1, 12, 8),      # long ragged K, per-group scales
+    (5, 40000, 1, 8, 40000),   # K beyond the LDS-staged x of the general path
+    (256, 512, 1, 8, 512),     # the tiny workload's format
+    (4097, 4096, 2, 12, 128),  # one row past a multiple of the grid
+]
+
+
+def _x(batch, k, dtype, seed):
+    return vqsynth.make_x(batch, k, dtype, np.random.SeedSequence(seed))
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("batch", [1, 3])
+def test_gemv_ragged(vq, shape, dtype, batch):
+    import torch
+    n, k, st, bits, bs = shape
+    sw = vqsynth.random_weight(n, k, st, bits, bs, seed=n * 131 + k + st + bits)
+    xs, x64 = _x(batch, k, dtype, n + k)
+    y = vq.vq_gemv(device_weight(sw), x_to_device(xs, dtype))
+    torch.cuda.synchronize()
+    rows = None if n <= 600 else np.array([0, 1, 2, n // 2, n - 2, n - 1])
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw, rows), x64)
+    got = y.cpu().numpy()
+    assert_within(got if rows is None else got[:, rows], y_ref, bound, f"{shape} {dtype} B={batch}")
+
+
+@pytest.mark.parametrize("batch", [2, 5, 16])
+def test_gemv_small_batch_mfma(vq, batch):
+    import torch
+    sw = vqsynth.random_weight(300, 1024, 2, 12, 128, seed=batch)
+    xs, x64 = _x(batch, 1024, "bf16", 77 + batch)
+    y = vq.vq_gemv(device_weight(sw), x_to_device(xs, "bf16"))
+    torch.cuda.synchronize()
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
+    assert_within(y.cpu().numpy(), y_ref, bound, f"B={batch}")
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_unpack_dequant_ragged(vq, shape):
+    import torch
+    n, k, st, bits, bs = shape
+    sw = vqsynth.random_weight(n, k, st, bits, bs, seed=n + 7 * k)
+    idx_d, w_d = vq.vq_unpack_dequant(device_weight(sw))
+    torch.cuda.synchronize()
+    idx = oracle_indices(sw)
+    got = idx_d.cpu().numpy().view(np.uint16).reshape(st, -1)
+    for t in range(st):
+        assert np.array_equal(got[t].astype(np.int64), idx[t])
+    assert np.array_equal(w_d.cpu().numpy().view(np.uint16), oracle_w16(sw, None, idx).view(np.uint16))
+
+
+def _extreme_weight(seed, n=64, k=64, st=3, bits=8):
+    rng = np.random.default_rng(seed)
+    pool = np.array([0.0, -0.0, 6e-8, -6e-8, 1.2e-7, 3.1e-5, -6.1e-5, 1e-3, 0.5, -1.0, 3.0, 100.0, -2500.0,
+                     30000.0, 65504.0, -65504.0, 0.333, 2.005859375], dtype=np.float16)
+    sw = vqsynth.random_weight(n, k, st, bits, 16, seed=seed)
+    sw.codebooks = [rng.choice(pool, ((1 << bits), 8)).astype(np.float16) for _ in range(st)]
+    sw.scales = rng.choice(np.array([0.75, -2.0, 1.5, 6e-8, 1024.0, -0.0, 0.999], np.float16),
+                           sw.scales.shape).astype(np.float16)
+    return sw
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_dequant_extreme_values(vq, seed):
+    """Subnormals, overflow to inf, signed zeros, negative scales, mixed
+    magnitudes across three stages: every weight bit-exact."""
+    import torch
+    sw = _extreme_weight(seed)
+    _, w_d = vq.vq_unpack_dequant(device_weight(sw), want_idx=False)
+    torch.cuda.synchronize()
+    with np.errstate(over="ignore", invalid="ignore"):
+        want = oracle_w16(sw)
+    assert np.array_equal(w_d.cpu().numpy().view(np.uint16), want.view(np.uint16))
+
+
+def test_dequant_double_rounding_trap(vq):
+    """The hand-derived trap (s=0.75, cb0=2+3*2^-9, cb1=2^-24) rounds once."""
+    import json
+    import os
+    import torch
+    from conftest import GOLDEN
+    d = json.load(open(os.path.join(GOLDEN, "double_rounding.json")))
+    sw = vqsynth.random_weight(4, 64, 2, 8, 64, seed=9)
+    sw.codebooks[0][:] = d["c0"]
+    sw.codebooks[1][:] = d["c1"]
+    sw.scales[:] = d["scale"]
+    _, w_d = vq.vq_unpack_dequant(device_weight(sw), want_idx=False)
+    torch.cuda.synchronize()
+    assert np.all(w_d.cpu().numpy().view(np.uint16) == d["w_fp16_bits"])
+
+
+@pytest.mark.parametrize("m,n,k,st,bits", [(17, 130, 72, 2, 12), (300, 257, 256, 1, 12), (1, 64, 4096, 2, 12),
+                                          (40, 96, 8, 1, 8), (33, 200, 512, 1, 16), (513, 129, 160, 3, 12)])
+def test_gemm_ragged(vq, m, n, k, st, bits):
+    import torch
+    sw = vqsynth.random_weight(n, k, st, bits, 8 if k % 32 else 32, seed=m + n + k)
+    xs, x64 = _x(m, k, "bf16", m * 7 + n)
+    y = vq.vq_gemm(device_weight(sw), x_to_device(xs, "bf16"))
+    torch.cuda.synchronize()
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
+    assert_within(y.cpu().numpy(), y_ref, bound, f"gemm {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("n,max_block", [(1, 8192), (2, 8192), (3, 8192), (2688, 8192), (28672, 16384),
+                                         (28672, 8192), (100, 1), (4096, 64)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rht_sizes(vq, n, max_block, dtype):
+    import torch
+    from test_parity_gpu import rht_bound
+    xs, x64 = _x(3, n, dtype, n + max_block)
+    signs = vqsynth.make_signs(n, np.random.SeedSequence(n))
+    out = vq.rht_apply(x_to_device(xs, dtype), torch.from_numpy(signs).cuda(), max_block)
+    torch.cuda.synchronize()
+    ref = oracle.rht_ref(x64, signs, max_block)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= rht_bound(x64, signs, n, max_block)), err.max()
+
+
+def test_deterministic_and_stream_independent(vq):
+    """Bitwise-identical results on rerun and on a non-default stream (fixed
+    reduction order, no atomics)."""
+    import torch
+    cases = [(vqsynth.random_weight(4096, 4096, 2, 12, 128, seed=5), "gemv", 1),
+             (vqsynth.random_weight(1000, 2048, 1, 16, 2048, seed=6), "gemv", 1),
+             (vqsynth.random_weight(700, 1024, 2, 12, 128, seed=7), "gemv", 16),
+             (vqsynth.random_weight(640, 512, 2, 12, 128, seed=8), "gemm", 600)]
+    for sw, op, b in cases:
+        w = device_weight(sw)
+        xs, _ = _x(b, sw.k_in, "bf16", b)
+        x = x_to_device(xs, "bf16")
+        f = vq.vq_gemv if op == "gemv" else vq.vq_gemm
+        y1 = f(w, x)
+        y2 = f(w, x)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            y3 = f(w, x, stream=s)
+        s.synchronize()
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2) and torch.equal(y1, y3), op

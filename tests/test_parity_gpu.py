@@ -1,0 +1,161 @@
+"""Parity of the HIP path with the CPU oracle at the workloads' full sizes.
+
+Indices and the fp16 dequant must match bit for bit; matmul outputs must lie
+within |y - y_ref| <= 2e-3 * sum|w x| + 1e-6 of the exact float64 product;
+the Hadamard transform within its fp32 forward-error bound.  Large outputs
+are checked on sampled rows that the oracle computes one by one (first, last
+and random rows), small ones completely.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import vqsynth
+from vqtest import (assert_within, device_weight, ensure_built, oracle_indices, oracle_w16,
+                    oracle_w64, sample_rows, x_to_device)
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def workload(wl):
+    if wl not in _CACHE:
+        ws, act_ss = vqsynth.workload_weights(wl)
+        _CACHE[wl] = (ws, act_ss)
+    return _CACHE[wl]
+
+
+@pytest.fixture(scope="module")
+def vq():
+    ensure_built()
+    import compressed_index_matmul_amd as m
+    m.lib()
+    return m
+
+
+def _rows_for(n, k, seed):
+    return None if n * k <= (1 << 22) else sample_rows(n, 48, seed)
+
+
+def rht_bound(x64, signs, n, max_block):
+    """Elementwise forward-error bound of an fp32 orthonormal FWHT, per block:
+    (log2(nb) + 2) * 2^-24 * ||x_block||_2 * 1.01 (one rounding per butterfly
+    stage plus the final scale and its rounded constant)."""
+    out = np.empty_like(x64)
+    off = 0
+    for nb in oracle.rht_blocks(n, max_block):
+        nrm = np.linalg.norm(x64[:, off:off + nb], axis=1, keepdims=True)
+        out[:, off:off + nb] = (np.log2(nb) + 2) * 2.0 ** -24 * nrm * 1.01
+        off += nb
+    return out
+
+
+@pytest.mark.parametrize("wl", ["tiny", "smollm", "llama8b", "mlp70b", "prefill"])
+def test_unpack_dequant_bitexact(vq, wl):
+    import torch
+    ws, _ = workload(wl)
+    for i, sw in enumerate(ws):
+        w = device_weight(sw)
+        idx_d, w_d = vq.vq_unpack_dequant(w)
+        torch.cuda.synchronize()
+        idx = oracle_indices(sw)
+        got_idx = idx_d.cpu().numpy().view(np.uint16).reshape(sw.n_stages, -1)
+        for t in range(sw.n_stages):
+            assert np.array_equal(got_idx[t].astype(np.int64), idx[t]), f"{wl}/{sw.name} stage {t} indices"
+        rows = _rows_for(sw.n_out, sw.k_in, 100 + i)
+        want = oracle_w16(sw, rows, idx)
+        got = w_d.cpu().numpy()
+        if rows is not None:
+            got = got[rows]
+        assert np.array_equal(got.view(np.uint16), want.view(np.uint16)), f"{wl}/{sw.name} fp16 weights"
+        del w, idx_d, w_d
+
+
+@pytest.mark.parametrize("wl", ["tiny", "smollm", "llama8b"])
+def test_gemv_batch1(vq, wl):
+    import torch
+    ws, act_ss = workload(wl)
+    cfg = vqsynth.WORKLOADS[wl]
+    kids = act_ss.spawn(len(ws))
+    for i, sw in enumerate(ws):
+        xs, x64 = vqsynth.make_x(1, sw.k_in, cfg["x_dtype"], kids[i])
+        w = device_weight(sw)
+        y = vq.vq_gemv(w, x_to_device(xs, cfg["x_dtype"]))
+        torch.cuda.synchronize()
+        rows = _rows_for(sw.n_out, sw.k_in, 200 + i)
+        w64 = oracle_w64(sw, rows)
+        y_ref, bound = oracle.matmul_ref(w64, x64)
+        got = y.cpu().numpy()
+        if rows is not None:
+            got = got[:, rows]
+        assert_within(got, y_ref, bound, f"{wl}/{sw.name}")
+
+
+def test_gemv_batch16_llama8b(vq):
+    import torch
+    ws, act_ss = workload("llama8b")
+    kids = act_ss.spawn(2 * len(ws))
+    for i, sw in enumerate(ws):
+        xs, x64 = vqsynth.make_x(16, sw.k_in, "bf16", kids[len(ws) + i])
+        w = device_weight(sw)
+        y = vq.vq_gemv(w, x_to_device(xs, "bf16"))
+        torch.cuda.synchronize()
+        rows = sample_rows(sw.n_out, 48, 300 + i)
+        y_ref, bound = oracle.matmul_ref(oracle_w64(sw, rows), x64)
+        assert_within(y.cpu().numpy()[:, rows], y_ref, bound, f"llama8b/{sw.name} B=16")
+
+
+def test_rht_mlp70b_inputs(vq):
+    import torch
+    ws, act_ss = workload("mlp70b")
+    kids = act_ss.spawn(2 * len(ws))
+    for i, sw in enumerate(ws):
+        xs, x64 = vqsynth.make_x(1, sw.k_in, "bf16", kids[i])
+        signs = vqsynth.make_signs(sw.k_in, kids[len(ws) + i])
+        xr = vq.rht_apply(x_to_device(xs, "bf16"), torch.from_numpy(signs).cuda(), 8192)
+        torch.cuda.synchronize()
+        ref = oracle.rht_ref(x64, signs, 8192)
+        err = np.abs(xr.cpu().numpy().astype(np.float64) - ref)
+        assert np.all(err <= rht_bound(x64, signs, sw.k_in, 8192)), f"{sw.name}: max err {err.max()}"
+
+
+def test_rht_gemv_mlp70b(vq):
+    """Input transform then 16-bit-index GEMV (1 MiB codebook): the result is
+    checked against the oracle's exact transform and exact product."""
+    import torch
+    ws, act_ss = workload("mlp70b")
+    kids = act_ss.spawn(2 * len(ws))
+    for i, sw in enumerate(ws):
+        xs, x64 = vqsynth.make_x(1, sw.k_in, "bf16", kids[i])
+        signs = vqsynth.make_signs(sw.k_in, kids[len(ws) + i])
+        w = device_weight(sw)
+        xr = vq.rht_apply(x_to_device(xs, "bf16"), torch.from_numpy(signs).cuda(), 8192)
+        y = vq.vq_gemv(w, xr)
+        torch.cuda.synchronize()
+        rows = sample_rows(sw.n_out, 48, 400 + i)
+        xr_ref = oracle.rht_ref(x64, signs, 8192)
+        y_ref, bound = oracle.matmul_ref(oracle_w64(sw, rows), xr_ref)
+        assert_within(y.cpu().numpy()[:, rows], y_ref, bound, f"mlp70b/{sw.name}")
+
+
+def test_gemm_prefill(vq):
+    """2048-token GEMM: sampled token rows against every W row, and sampled W
+    rows against every token."""
+    import torch
+    ws, act_ss = workload("prefill")
+    kids = act_ss.spawn(len(ws))
+    for i, sw in enumerate(ws):
+        xs, x64 = vqsynth.make_x(2048, sw.k_in, "bf16", kids[i])
+        w = device_weight(sw)
+        y = vq.vq_gemm(w, x_to_device(xs, "bf16"))
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        toks = sample_rows(2048, 24, 500 + i)
+        w64_all = oracle_w64(sw)
+        y_ref, bound = oracle.matmul_ref(w64_all, x64[toks])
+        assert_within(got[toks], y_ref, bound, f"prefill/{sw.name} token rows")
+        rows = sample_rows(sw.n_out, 24, 600 + i)
+        y_ref2, bound2 = oracle.matmul_ref(w64_all[rows], x64)
+        assert_within(got[:, rows], y_ref2, bound2, f"prefill/{sw.name} W rows")
+        del w64_all

@@ -1,0 +1,77 @@
+"""Test helpers: move synthetic weights to the device and build oracle
+references for the same inputs.  The oracle and the HIP library only meet
+here, in the tests."""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+
+import oracle
+import vqsynth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def ensure_built():
+    """Build the library if no built copy exists (tests load what is built)."""
+    from compressed_index_matmul_amd import LIB_PATH
+    if not os.path.exists(LIB_PATH):
+        from compressed_index_matmul_amd.build import build
+        build()
+
+
+def device_weight(sw: vqsynth.SynthWeight, device="cuda"):
+    from compressed_index_matmul_amd import VQWeight
+    return VQWeight(sw.n_out, sw.k_in, sw.n_stages, sw.idx_bits, sw.scale_block,
+                    codebooks=sw.codebooks, scales=sw.scales, lo=sw.lo, hi=sw.hi,
+                    idx16=sw.idx16, device=device)
+
+
+def oracle_indices(sw: vqsynth.SynthWeight):
+    return [oracle.unpack_indices(sw.idx_bits, sw.n_groups, lo=sw.lo[t], hi=sw.hi[t], idx16=sw.idx16[t])
+            for t in range(sw.n_stages)]
+
+
+def oracle_w64(sw: vqsynth.SynthWeight, rows=None, idx=None):
+    """Exact float64 dequant of the selected rows (all rows if None)."""
+    idx = oracle_indices(sw) if idx is None else idx
+    g = sw.k_in // 8
+    if rows is None:
+        return oracle.dequant_exact(sw.n_out, sw.k_in, idx, sw.codebooks, sw.scales, sw.scale_block)
+    rows = np.asarray(rows)
+    sub = [i.reshape(sw.n_out, g)[rows].reshape(-1) for i in idx]
+    return oracle.dequant_exact(len(rows), sw.k_in, sub, sw.codebooks, sw.scales[rows], sw.scale_block)
+
+
+def oracle_w16(sw: vqsynth.SynthWeight, rows=None, idx=None):
+    idx = oracle_indices(sw) if idx is None else idx
+    g = sw.k_in // 8
+    if rows is None:
+        return oracle.dequant_fp16(sw.n_out, sw.k_in, idx, sw.codebooks, sw.scales, sw.scale_block)
+    rows = np.asarray(rows)
+    sub = [i.reshape(sw.n_out, g)[rows].reshape(-1) for i in idx]
+    return oracle.dequant_fp16(len(rows), sw.k_in, sub, sw.codebooks, sw.scales[rows], sw.scale_block)
+
+
+def sample_rows(n: int, count: int, seed: int):
+    """First, last and `count` random rows (sorted, unique)."""
+    rng = np.random.default_rng(seed)
+    r = set(rng.choice(n, size=min(count, n), replace=False).tolist()) | {0, n - 1}
+    return np.array(sorted(r))
+
+
+def x_to_device(x_stored, dtype: str, device="cuda"):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x_stored).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x_stored, dtype=np.float32)).to(device)
+
+
+def assert_within(y, y_ref, bound, what=""):
+    ok, worst = oracle.within_tolerance(y, y_ref, bound)
+    if not ok.all():
+        bad = np.argwhere(~ok)[:5]
+        raise AssertionError(f"{what}: {int((~ok).sum())} outputs outside the bound "
+                             f"(worst ratio {worst:.3g}); first {bad.tolist()}")
+    return worst
