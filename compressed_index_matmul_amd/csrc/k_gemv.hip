@@ -43,163 +43,175 @@ struct GemvArgs {
 // ---------------------------------------------------------------------------
 // fast path
 // ---------------------------------------------------------------------------
-template <int S, int BITS, int CPL, int WAVES, bool XF16>
+template <int S, int BITS, int CPL, int WAVES, bool XF16, int RB>
 __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
-  __shared__ uint4 s_cb[S << BITS];
+  constexpr int NT = WAVES * 64;
+  constexpr int CBN = S << BITS;                 // codebook rows of all stages
+  constexpr int CB_ITERS = (CBN + NT - 1) / NT;  // 1 KiB LDS-direct loads per wave
+  constexpr int XV = XF16 ? 4 : 8;               // 16-byte x vectors per chunk
+  __shared__ uint4 s_cb[CBN];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int stride = gridDim.x * WAVES;
   int row = blockIdx.x * WAVES + wave;
+  const int last = a.n - 1;
 
-  uint32_t L[CPL][S], H[CPL][S];
-  float SC[CPL];
-
-#define VQ_LOAD_ROW(R_, L_, H_, SC_)                                                         \
-  {                                                                                          \
-    const size_t rb = (size_t)(R_) * a.G;                                                    \
-    _Pragma("unroll") for (int j = 0; j < CPL; ++j) {                                        \
-      const int c = lane + 64 * j;                                                           \
-      if (c < a.C) {                                                                         \
-        _Pragma("unroll") for (int t = 0; t < S; ++t) {                                      \
-          L_[j][t] = *reinterpret_cast<const uint32_t *>(a.lo[t] + rb + 4 * c);              \
-          if (BITS == 12)                                                                    \
-            H_[j][t] = *reinterpret_cast<const uint16_t *>(a.hi[t] + (rb >> 1) + 2 * c);     \
-          else                                                                               \
-            H_[j][t] = 0;                                                                    \
-        }                                                                                    \
-        SC_[j] = h2f(a.sc[(size_t)(R_) * a.nblk + (32 * c) / a.bs]);                         \
-      } else {                                                                               \
-        _Pragma("unroll") for (int t = 0; t < S; ++t) { L_[j][t] = 0; H_[j][t] = 0; }        \
-        SC_[j] = 0.f;                                                                        \
-      }                                                                                      \
-    }                                                                                        \
+  // Global loads are issued oldest-first in the order they are needed:
+  // codebooks, then x, then the first row's indices, so waiting for the
+  // codebooks does not wait for anything else.  Chunks past the end of the
+  // row load a valid duplicate and are masked out of the sum; no branch
+  // surrounds a load, so every load stays in flight until its first use.
+  // Codebooks stream straight into LDS (global_load_lds_dwordx4: lane l of a
+  // wave writes 16 bytes at the wave's LDS base + 16 l), no registers used.
+#pragma unroll
+  for (int r = 0; r < CB_ITERS; ++r) {
+    const int blk = (r * WAVES + wave) * 64;  // first codebook row of this wave's 1 KiB
+    if (blk < CBN) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(a.cb[blk >> BITS]) + (blk & ((1 << BITS) - 1)) + lane;
+      lds_direct_16(src, s_cb + blk);
+    }
+  }
+  int cc[CPL];
+  bool ok[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = lane + 64 * j;
+    ok[j] = c < a.C;
+    cc[j] = ok[j] ? c : a.C - 1;
+  }
+  uint4 xr[CPL][XV];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const uint4 *px = XF16 ? reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.x) + 32 * cc[j])
+                           : reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(a.x) + 32 * cc[j]);
+#pragma unroll
+    for (int v = 0; v < XV; ++v) xr[j][v] = px[v];
   }
 
-  if (row < a.n) VQ_LOAD_ROW(row, L, H, SC);
-
-  // stage the codebooks
-  for (int i = tid; i < (S << BITS); i += WAVES * 64) {
-    s_cb[i] = reinterpret_cast<const uint4 *>(a.cb[i >> BITS])[i & ((1 << BITS) - 1)];
+  // Rows of this wave: row0 + k * stride.  They are processed in batches of
+  // RB rows whose index loads are all in flight together; two register sets
+  // alternate so the next batch loads while the current one is computed.
+  // Guards are wave-uniform (a row exists or not for the whole wave).
+  const int row0 = row;
+  uint32_t L[RB][CPL][S], H[RB][CPL][S], SCb[RB][CPL];
+#define VQ_LOAD_BATCH(B_, L_, H_, SC_)                                                     \
+  _Pragma("unroll") for (int i = 0; i < RB; ++i) {                                         \
+    const int rr = row0 + ((B_) * RB + i) * stride;                                        \
+    if (rr < a.n) {                                                                        \
+      const size_t rb = (size_t)rr * a.G;                                                  \
+      _Pragma("unroll") for (int j = 0; j < CPL; ++j) {                                    \
+        _Pragma("unroll") for (int t = 0; t < S; ++t) {                                    \
+          L_[i][j][t] = *reinterpret_cast<const uint32_t *>(a.lo[t] + rb + 4 * cc[j]);     \
+          if (BITS == 12)                                                                  \
+            H_[i][j][t] = *reinterpret_cast<const uint16_t *>(a.hi[t] + (rb >> 1) + 2 * cc[j]); \
+        }                                                                                  \
+        SC_[i][j] = a.sc[(size_t)rr * a.nblk + (32 * cc[j]) / a.bs];                       \
+      }                                                                                    \
+    }                                                                                      \
   }
+  VQ_LOAD_BATCH(0, L, H, SCb);
 
   // this lane's slice of x, held for the whole launch
   half2_t xh[XF16 ? CPL : 1][16];
   float xf[XF16 ? 1 : CPL][32];
   int xexp = 0;
   if (XF16) {
-    // pass 1: largest |x| of the lane's slice
     float mx = 0.f;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j;
-      if (c < a.C) {
-        const uint4 *px = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.x) + 32 * c);
+    for (int j = 0; j < CPL; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint4 u = px[v];
-          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t w4[4] = {xr[j][v].x, xr[j][v].y, xr[j][v].z, xr[j][v].w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(fabsf(bf2f(w4[e] & 0xffffu)), fabsf(bf2f(w4[e] >> 16))));
+        for (int e = 0; e < 4; ++e) {
+          const float m2 = fmaxf(fabsf(bf2f(w4[e] & 0xffffu)), fabsf(bf2f(w4[e] >> 16)));
+          mx = ok[j] ? fmaxf(mx, m2) : mx;
         }
       }
-    }
     // the largest |x| scaled into [2^14, 2^15): fp16 holds every bf16 value
     // within 2^28 of it exactly
     if (mx > 0.f) xexp = 14 - ilogbf(mx);
-    // pass 2: rescale and convert (reloads hit the cache)
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j;
+    for (int j = 0; j < CPL; ++j)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) xh[j][q] = half2_t{(_Float16)0.f, (_Float16)0.f};
-      if (c < a.C) {
-        const uint4 *px = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.x) + 32 * c);
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t w4[4] = {xr[j][v].x, xr[j][v].y, xr[j][v].z, xr[j][v].w};
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint4 u = px[v];
-          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            xh[j][4 * v + e] = half2_t{(_Float16)ldexpf(bf2f(w4[e] & 0xffffu), xexp),
-                                       (_Float16)ldexpf(bf2f(w4[e] >> 16), xexp)};
-        }
+        for (int e = 0; e < 4; ++e)
+          xh[j][4 * v + e] = half2_t{(_Float16)ldexpf(bf2f(w4[e] & 0xffffu), xexp),
+                                     (_Float16)ldexpf(bf2f(w4[e] >> 16), xexp)};
       }
-    }
   } else {
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j;
+    for (int j = 0; j < CPL; ++j)
 #pragma unroll
-      for (int q = 0; q < 32; ++q) xf[j][q] = 0.f;
-      if (c < a.C) {
-        const float4 *px = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.x) + 32 * c);
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const float4 u = px[v];
-          xf[j][4 * v] = u.x;
-          xf[j][4 * v + 1] = u.y;
-          xf[j][4 * v + 2] = u.z;
-          xf[j][4 * v + 3] = u.w;
-        }
+      for (int v = 0; v < 8; ++v) {
+        xf[j][4 * v] = __uint_as_float(xr[j][v].x);
+        xf[j][4 * v + 1] = __uint_as_float(xr[j][v].y);
+        xf[j][4 * v + 2] = __uint_as_float(xr[j][v].z);
+        xf[j][4 * v + 3] = __uint_as_float(xr[j][v].w);
       }
-    }
   }
+  // the LDS-direct codebook loads of this wave have landed; then the barrier
+  // makes every wave's part visible
+  wait_all_memory();
   __syncthreads();
 
-  while (row < a.n) {
-    const int nrow = row + stride;
-    uint32_t L2[CPL][S], H2[CPL][S];
-    float SC2[CPL];
-    if (nrow < a.n) VQ_LOAD_ROW(nrow, L2, H2, SC2);
-
-    float acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j;
-      if (c < a.C) {
-        float d = 0.f;
-#pragma unroll
-        for (int t = 0; t < S; ++t) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint32_t idx = (L[j][t] >> (8 * q)) & 0xffu;
-            if (BITS == 12) idx |= ((H[j][t] >> (4 * q)) & 0xfu) << 8;
-            const uint4 v = s_cb[(t << BITS) + idx];
-            if (XF16) {
-              d = __builtin_amdgcn_fdot2(as_h2(v.x), xh[j][4 * q + 0], d, false);
-              d = __builtin_amdgcn_fdot2(as_h2(v.y), xh[j][4 * q + 1], d, false);
-              d = __builtin_amdgcn_fdot2(as_h2(v.z), xh[j][4 * q + 2], d, false);
-              d = __builtin_amdgcn_fdot2(as_h2(v.w), xh[j][4 * q + 3], d, false);
-            } else {
-              const uint32_t hv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                d = fmaf(h2f(hv[e] & 0xffffu), xf[j][8 * q + 2 * e], d);
-                d = fmaf(h2f(hv[e] >> 16), xf[j][8 * q + 2 * e + 1], d);
-              }
-            }
-          }
-        }
-        acc = fmaf(SC[j], d, acc);
-      }
-    }
-    if (XF16) acc = ldexpf(acc, -xexp);
-    const float tot = wave_sum(acc);
-    if (lane == 0) a.y[row] = tot;
-
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      SC[j] = SC2[j];
-#pragma unroll
-      for (int t = 0; t < S; ++t) {
-        L[j][t] = L2[j][t];
-        H[j][t] = H2[j][t];
-      }
-    }
-    row = nrow;
+  // One row: gather every codebook row of a chunk first, then its dot
+  // products; scale per chunk; masked chunks add nothing.
+#define VQ_ROW(R_, L_, H_, SC_)                                                              \
+  {                                                                                          \
+    float acc = 0.f;                                                                         \
+    _Pragma("unroll") for (int j = 0; j < CPL; ++j) {                                        \
+      uint4 v[S][4];                                                                         \
+      _Pragma("unroll") for (int t = 0; t < S; ++t)                                          \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                        \
+        uint32_t idx = (L_[j][t] >> (8 * q)) & 0xffu;                                        \
+        if (BITS == 12) idx |= ((H_[j][t] >> (4 * q)) & 0xfu) << 8;                          \
+        v[t][q] = s_cb[(t << BITS) + idx];                                                   \
+      }                                                                                      \
+      float d = 0.f;                                                                         \
+      _Pragma("unroll") for (int t = 0; t < S; ++t)                                          \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                        \
+        if (XF16) {                                                                          \
+          d = __builtin_amdgcn_fdot2(as_h2(v[t][q].x), xh[j][4 * q + 0], d, false);          \
+          d = __builtin_amdgcn_fdot2(as_h2(v[t][q].y), xh[j][4 * q + 1], d, false);          \
+          d = __builtin_amdgcn_fdot2(as_h2(v[t][q].z), xh[j][4 * q + 2], d, false);          \
+          d = __builtin_amdgcn_fdot2(as_h2(v[t][q].w), xh[j][4 * q + 3], d, false);          \
+        } else {                                                                             \
+          const uint32_t hv[4] = {v[t][q].x, v[t][q].y, v[t][q].z, v[t][q].w};               \
+          _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                    \
+            d = fmaf(h2f(hv[e] & 0xffffu), xf[j][8 * q + 2 * e], d);                         \
+            d = fmaf(h2f(hv[e] >> 16), xf[j][8 * q + 2 * e + 1], d);                         \
+          }                                                                                  \
+        }                                                                                    \
+      }                                                                                      \
+      acc = ok[j] ? fmaf(h2f(SC_[j]), d, acc) : acc;                                         \
+    }                                                                                        \
+    if (XF16) acc = ldexpf(acc, -xexp);                                                      \
+    const float tot = wave_sum(acc);                                                         \
+    if (lane == 0) a.y[R_] = tot;                                                            \
   }
-#undef VQ_LOAD_ROW
+#define VQ_BATCH(B_, L_, H_, SC_)                                                            \
+  _Pragma("unroll") for (int i = 0; i < RB; ++i) {                                           \
+    const int rr = row0 + ((B_) * RB + i) * stride;                                          \
+    if (rr < a.n) VQ_ROW(rr, L_[i], H_[i], SC_[i]);                                          \
+  }
+
+  const int nrows = row0 < a.n ? (a.n - 1 - row0) / stride + 1 : 0;  // rows of this wave
+  const int nbatch = (nrows + RB - 1) / RB;
+  uint32_t L2[RB][CPL][S], H2[RB][CPL][S], SC2[RB][CPL];
+  for (int b = 0; b < nbatch; b += 2) {
+    if (b + 1 < nbatch) VQ_LOAD_BATCH(b + 1, L2, H2, SC2);
+    VQ_BATCH(b, L, H, SCb);
+    if (b + 1 >= nbatch) break;
+    if (b + 2 < nbatch) VQ_LOAD_BATCH(b + 2, L, H, SCb);
+    VQ_BATCH(b + 1, L2, H2, SC2);
+  }
+#undef VQ_BATCH
+#undef VQ_ROW
+#undef VQ_LOAD_BATCH
 }
 
 // ---------------------------------------------------------------------------
@@ -322,14 +334,32 @@ bool gemv_fast_eligible(const WView &w, int xt) {
   return cpl <= (xt == VQ_BF16 ? 8 : 4);
 }
 
+template <int S, int BITS, int CPL, int W, int RB, bool XF16>
+static void launch_fast_w(const GemvArgs &a, int nwg, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemv_lds<S, BITS, CPL, W, XF16, RB>), dim3(nwg), dim3(W * 64), 0, s, a);
+}
+
+// Persistent grid of one workgroup per CU slot (two when the codebooks take
+// <= 80 KiB of LDS).  Waves per workgroup and rows in flight per wave (RB) are
+// chosen so that the x slice, two batches of row indices and the gathers fit
+// in the registers a wave gets: 16 waves -> 128 VGPRs, 8 -> 256, 4 -> 512.
 template <int S, int BITS, int CPL, bool XF16>
 static void launch_fast_c(const GemvArgs &a, int cus, hipStream_t s) {
-  constexpr int W = CPL <= 2 ? 16 : 8;
   constexpr size_t lds = (size_t)(S << BITS) * 16;
-  const int per_cu = lds > 81920 ? 1 : 2;
-  int nwg = (a.n + W - 1) / W;
-  if (nwg > cus * per_cu) nwg = cus * per_cu;
-  hipLaunchKernelGGL((k_gemv_lds<S, BITS, CPL, W, XF16>), dim3(nwg), dim3(W * 64), 0, s, a);
+  const int slots = cus * (lds > 81920 ? 1 : 2);
+  constexpr int xload = CPL * (XF16 ? 1 : 2) * (S > 2 ? 2 : 1);
+  auto grid = [&](int w) { const int g = (a.n + w - 1) / w; return g < slots ? g : slots; };
+  auto rows_per_wave = [&](int w) { const int g = grid(w); return (a.n + g * w - 1) / (g * w); };
+  if constexpr (xload <= 2) {
+    if (rows_per_wave(16) <= 1) launch_fast_w<S, BITS, CPL, 16, 1, XF16>(a, grid(16), s);
+    else launch_fast_w<S, BITS, CPL, 8, 4, XF16>(a, grid(8), s);
+  } else if constexpr (xload <= 4) {
+    if (rows_per_wave(8) <= 1) launch_fast_w<S, BITS, CPL, 8, 1, XF16>(a, grid(8), s);
+    else launch_fast_w<S, BITS, CPL, 8, 2, XF16>(a, grid(8), s);
+  } else {
+    if (rows_per_wave(4) <= 1) launch_fast_w<S, BITS, CPL, 4, 1, XF16>(a, grid(4), s);
+    else launch_fast_w<S, BITS, CPL, 4, 2, XF16>(a, grid(4), s);
+  }
 }
 
 template <int S, int BITS, bool XF16>

@@ -75,6 +75,26 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// 16-byte global -> LDS direct load (global_load_lds_dwordx4): lane l writes
+// its 16 bytes at lds_wave_base + 16 l.  `lds_wave_base` must be the same
+// for the whole wave.  The builtin exists only for the GPU target, so the
+// host compilation pass (which never runs device code) sees an empty body.
+__device__ __forceinline__ void lds_direct_16(const void *src, void *lds_wave_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
+#else
+  (void)src;
+  (void)lds_wave_base;
+#endif
+}
+
+// Wait for every outstanding memory operation of the wave.
+__device__ __forceinline__ void wait_all_memory() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt(0);
+#endif
+}
+
 // Index of flat group f of stage planes (any width).
 __device__ __forceinline__ uint32_t load_index(int bits, const uint8_t *lo, const uint8_t *hi,
                                                const uint16_t *i16, size_t f) {

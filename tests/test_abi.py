@@ -30,6 +30,14 @@ def header_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z0-9_]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)))
 
 
+def test_library_resolves_every_symbol():
+    """Load with immediate binding: an undefined symbol (for example a kernel
+    launch stub the compiler dropped) fails here rather than on the GPU."""
+    ensure_built()
+    from compressed_index_matmul_amd import LIB_PATH
+    ctypes.CDLL(LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+
+
 def test_header_declares_the_boundary():
     fns = header_functions()
     for name in ("vq_unpack_dequant", "vq_gemv", "vq_gemm", "rht_apply", "vq_version",
