@@ -308,7 +308,7 @@ def main():
     detail = {"headline_linears": head["linears"], "weight_copies": head["weight_copies"],
               "headline_ms_per_step_eager": head["ms_per_step_eager"]}
     only = set(filter(None, args.only.split(",")))
-    if not args.quick:
+    if only or not args.quick:
         legs = [("mlp70b_rht_gemv_b1", lambda: run_decode_leg(vq, "mlp70b", max(5, args.steps // 5), 3, rht=True)),
                 ("llama8b_gemv_b16", lambda: run_decode_leg(vq, "llama8b", args.steps, args.warmup, batch=16)),
                 ("prefill_gemm_m2048", lambda: run_gemm_leg(vq, max(5, args.steps // 5), 3)),

@@ -32,8 +32,14 @@ struct GemmArgs {
   const uint16_t *x;  // bf16 [m][k]
   float *y;           // [m][n]
   int m, n, k, G, S, nblk, bs;
+  int gshift;  // log2(scale_block / 8) when a power of two, else -1
   int tiles_m, tiles_n, per_xcd;
 };
+
+// Scale block of group g (8 columns): g / (scale_block / 8).
+__device__ __forceinline__ int scale_blk(const GemmArgs &a, int g) {
+  return a.gshift >= 0 ? (g >> a.gshift) : (8 * g) / a.bs;
+}
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -67,12 +73,169 @@ __device__ __forceinline__ uint4 decode_group_bf16(const GemmArgs &a, const uint
 // large M
 // ---------------------------------------------------------------------------
 constexpr int kLM = 256, kLN = 128;
-constexpr int kWP = 40;  // bf16 per W-tile row in LDS: 32 + 8 pad (80 B: conflict-free b128)
+constexpr int kWP = 40;  // bf16 per W-tile row in LDS: 32 + 8 pad (80 B rows: conflict-free b128)
 
-template <int S, int BITS, bool CB_LDS>
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+// fp32 sum of two fp16 values taken from the low (HI=false) or high halves
+// of a and b, rounded once (v_fma_mix_f32: a * 1.0 + b with both sources
+// read as fp16).
+template <bool HI>
+__device__ __forceinline__ float add_f16(uint32_t a, uint32_t b) {
+  float d;
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (HI)
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(d) : "v"(a), "v"(b));
+  else
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,1]" : "=v"(d) : "v"(a), "v"(b));
+#else
+  d = h2f(HI ? a >> 16 : a & 0xffffu) + h2f(HI ? b >> 16 : b & 0xffffu);
+#endif
+  return d;
+}
+
+// 8 weights of one group as bf16: sum of the stage vectors (fp32, each
+// partial sum rounded once), times the scale (fp32), rounded to bf16.
+template <int S>
+__device__ __forceinline__ uint4 group_to_bf16(const uint4 (&v)[S], float sf) {
+  const uint32_t h0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+  float w[8];
+  if (S == 1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w[2 * e] = h2f(h0[e] & 0xffffu);
+      w[2 * e + 1] = h2f(h0[e] >> 16);
+    }
+  } else {
+    const uint32_t h1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w[2 * e] = add_f16<false>(h0[e], h1[e]);
+      w[2 * e + 1] = add_f16<true>(h0[e], h1[e]);
+    }
+#pragma unroll
+    for (int t = 2; t < S; ++t) {
+      const uint32_t ht[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w[2 * e] += h2f(ht[e] & 0xffffu);
+        w[2 * e + 1] += h2f(ht[e] >> 16);
+      }
+    }
+  }
+  uint4 pk;
+  pk.x = pack_bf16(sf * w[0], sf * w[1]);
+  pk.y = pack_bf16(sf * w[2], sf * w[3]);
+  pk.z = pack_bf16(sf * w[4], sf * w[5]);
+  pk.w = pack_bf16(sf * w[6], sf * w[7]);
+  return pk;
+}
+
+// Everything one thread needs from global memory for one K step (4 groups,
+// 32 columns) of the large-M kernel: index bits of its two groups for every
+// stage, their scales, and the wave's A fragments (x) for the step.
+template <int S>
+struct StepRegs {
+  uint32_t lo[S];   // 8/12-bit: 2 low bytes; 16-bit: two indices
+  uint32_t hi[S];   // 12-bit: one byte = two nibbles
+  uint32_t sc[2];   // fp16 bits of the two groups' scales
+  uint4 av[2][2];   // A fragments [kk][i]
+};
+
+// Per-lane constant parts of every address of the large-M kernel (32-bit
+// element offsets); the K step adds a wave-uniform part, so each load is a
+// scalar base plus a 32-bit lane offset and costs no vector address math.
+struct LaneOffsets {
+  uint32_t f;       // flat group index of the thread's first group at step 0
+  uint32_t scrow;   // first scale of the thread's W row
+  uint32_t a[2];    // x byte offset of the lane's A rows (plus its k half)
+  int kh;           // the lane's k half within a 16-column MFMA step: 0 or 8
+};
+
+// A 16-byte load from a wave-uniform base plus a 32-bit lane byte offset.
+__device__ __forceinline__ uint4 ld16(const void *base, uint32_t off) {
+  return *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(base) + off);
+}
+
+template <int S, int BITS, bool ALIGNED>
+__device__ __forceinline__ void gemm_load_step(const GemmArgs &a, int ks, int dg, const LaneOffsets &o,
+                                               StepRegs<S> &R) {
+  const int g0 = ks * 4 + dg;  // first of this thread's two groups
+  if (ALIGNED) {
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+      if (BITS == 16) {
+        R.lo[t] = *reinterpret_cast<const uint32_t *>(a.i16[t] + 4 * ks + o.f);
+      } else {
+        R.lo[t] = *reinterpret_cast<const uint16_t *>(a.lo[t] + 4 * ks + o.f);
+        if (BITS == 12) R.hi[t] = (a.hi[t] + 2 * ks)[o.f >> 1];
+      }
+    }
+    R.sc[0] = a.sc[o.scrow + scale_blk(a, g0)];
+    R.sc[1] = a.sc[o.scrow + scale_blk(a, g0 + 1)];
+  } else {
+    const size_t f = (size_t)o.f + 4 * ks;
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+      uint32_t i0 = 0, i1 = 0;
+      if (g0 < a.G) i0 = load_index(BITS, a.lo[t], a.hi[t], a.i16[t], f);
+      if (g0 + 1 < a.G) i1 = load_index(BITS, a.lo[t], a.hi[t], a.i16[t], f + 1);
+      R.lo[t] = i0 | (i1 << 16);  // unpacked form for the ragged path
+    }
+    R.sc[0] = g0 < a.G ? a.sc[o.scrow + scale_blk(a, g0)] : 0;
+    R.sc[1] = g0 + 1 < a.G ? a.sc[o.scrow + scale_blk(a, g0 + 1)] : 0;
+  }
+  const uint16_t *xs = a.x + 32 * ks;  // wave-uniform
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    // column of the load: 32 ks + 16 kk + the lane's k half (o.a includes it)
+    const bool in = ALIGNED || 32 * ks + 16 * kk + o.kh < a.k;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      R.av[kk][i] = in ? ld16(xs + 16 * kk, o.a[i]) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// Decode the thread's two groups of step ks into the LDS W tile.
+template <int S, int BITS, bool CB_LDS, bool ALIGNED>
+__device__ __forceinline__ void gemm_decode_store(const GemmArgs &a, const uint4 *s_cb, const StepRegs<S> &R,
+                                                  int ks, int dg, bool wok, uint16_t *wt, int drow) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int g = ks * 4 + dg + u;
+    uint4 v[S];
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+      uint32_t idx;
+      if (!ALIGNED || BITS == 16) idx = (R.lo[t] >> (16 * u)) & 0xffffu;
+      else {
+        idx = (R.lo[t] >> (8 * u)) & 0xffu;
+        if (BITS == 12) idx |= ((R.hi[t] >> (4 * u)) & 0xfu) << 8;
+      }
+      v[t] = CB_LDS ? s_cb[(t << BITS) + idx] : reinterpret_cast<const uint4 *>(a.cb[t])[idx];
+    }
+    uint4 pk = group_to_bf16<S>(v, h2f(R.sc[u]));
+    if (!wok || (!ALIGNED && g >= a.G)) pk = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4 *>(&wt[drow * kWP + 8 * (dg + u)]) = pk;
+  }
+}
+
+// Tile 256 x 128, K step 32, 4 waves stacked along M, each owning 64 token
+// rows x all 128 W columns as 2 x 4 accumulator blocks of
+// v_mfma_f32_32x32x16_bf16 (x fragments are never loaded twice).  Per K step every thread decodes two
+// groups (LDS codebook gathers, fp32 stage sum and scale, bf16) into one of
+// two LDS W tiles, a barrier publishes it, and the waves multiply it with
+// their x fragments.  Global loads (indices, scales, x fragments) run three
+// steps ahead in a ring of four register sets.
+template <int S, int BITS, bool CB_LDS, bool ALIGNED>
 __global__ __launch_bounds__(256) void k_gemm_large(GemmArgs a) {
   __shared__ uint4 s_cb[CB_LDS ? (S << BITS) : 1];
-  __shared__ __attribute__((aligned(16))) uint16_t s_w[kLN * kWP];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[2][kLN * kWP];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -80,63 +243,107 @@ __global__ __launch_bounds__(256) void k_gemm_large(GemmArgs a) {
   if (L >= a.tiles_m * a.tiles_n) return;  // whole workgroup, before any barrier
   const int m0 = (L / a.tiles_n) * kLM;
   const int n0 = (L % a.tiles_n) * kLN;
-  const int wm = wave >> 1, wn = wave & 1;
 
   if (CB_LDS) {
-    for (int i = tid; i < (S << BITS); i += 256)
-      s_cb[i] = reinterpret_cast<const uint4 *>(a.cb[i >> BITS])[i & ((1 << BITS) - 1)];
-    __syncthreads();
+    constexpr int CBN = S << BITS;
+#pragma unroll 4
+    for (int r = 0; r < CBN / 256; ++r) {
+      const int blk = (r * 4 + wave) * 64;
+      lds_direct_16(reinterpret_cast<const uint4 *>(a.cb[blk >> BITS]) + (blk & ((1 << BITS) - 1)) + lane,
+                    s_cb + blk);
+    }
   }
-  const int drow = tid >> 1;      // W-tile row decoded by this thread
-  const int dg = 2 * (tid & 1);   // first of its two groups in the K step
+  const int drow = tid >> 1;     // W-tile row decoded by this thread
+  const int dg = 2 * (tid & 1);  // first of its two groups in a K step
   const int wrow = n0 + drow;
+  const bool wok = wrow < a.n;
+  const int wrow_c = wok ? wrow : a.n - 1;  // loads stay in bounds; result zeroed
+  LaneOffsets o;
+  o.f = (uint32_t)wrow_c * a.G + dg;
+  o.scrow = (uint32_t)wrow_c * a.nblk;
+  o.kh = 8 * (lane >> 5);
+  // A rows of this lane (one per 32-row block).  Rows past m load row m-1:
+  // they only feed output rows past m, which are never stored.
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    int r = m0 + wave * 64 + 32 * i + (lane & 31);
+    r = r < a.m ? r : a.m - 1;
+    o.a[i] = 2u * ((uint32_t)r * a.k + o.kh);
+  }
 
-  f32x16 acc[4][2];
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nks = (a.G + 3) / 4;
-  for (int ks = 0; ks < nks; ++ks) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int g = ks * 4 + dg + u;
-      uint4 pk = make_uint4(0, 0, 0, 0);
-      if (wrow < a.n && g < a.G) pk = decode_group_bf16<S, BITS, CB_LDS>(a, s_cb, wrow, g);
-      *reinterpret_cast<uint4 *>(&s_w[drow * kWP + 8 * (dg + u)]) = pk;
-    }
-    __syncthreads();
+  StepRegs<S> R0, R1, R2, R3;
+  // Unconditional prefetch (past the last step it reloads the last step):
+  // with no branch around the loads the wait counts stay exact.
+  auto load = [&](int ks, StepRegs<S> &R) {
+    gemm_load_step<S, BITS, ALIGNED>(a, ks < nks ? ks : nks - 1, dg, o, R);
+    sched_fence();  // keep the prefetch here, three steps ahead of its use
+  };
+  auto mma = [&](const StepRegs<S> &R, const uint16_t *wt) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const int col = ks * 32 + 16 * kk + 8 * (lane >> 5);
-      bf16x8_t bfr[2];
+      bf16x8_t bfr[4];
 #pragma unroll
-      for (int jn = 0; jn < 2; ++jn)
-        bfr[jn] = *reinterpret_cast<const bf16x8_t *>(&s_w[(wn * 64 + 32 * jn + (lane & 31)) * kWP + 16 * kk + 8 * (lane >> 5)]);
+      for (int jn = 0; jn < 4; ++jn)
+        bfr[jn] = *reinterpret_cast<const bf16x8_t *>(&wt[(32 * jn + (lane & 31)) * kWP + 16 * kk + 8 * (lane >> 5)]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = m0 + wm * 128 + 32 * i + (lane & 31);
-        uint4 av = make_uint4(0, 0, 0, 0);
-        if (row < a.m && col < a.k) av = *reinterpret_cast<const uint4 *>(a.x + (size_t)row * a.k + col);
-        const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, av);
+      for (int i = 0; i < 2; ++i) {
+        const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, R.av[kk][i]);
 #pragma unroll
-        for (int jn = 0; jn < 2; ++jn)
+        for (int jn = 0; jn < 4; ++jn)
           acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[jn], acc[i][jn], 0, 0, 0);
       }
     }
+  };
+  // one K step: decode into W buffer (ks & 1), barrier, multiply.  The
+  // barrier of step ks also orders the reads of buffer (ks & 1) at step ks-2
+  // before its rewrite here.
+  auto step = [&](int ks, const StepRegs<S> &R) {
+    uint16_t *wt = s_w[ks & 1];
+    gemm_decode_store<S, BITS, CB_LDS, ALIGNED>(a, s_cb, R, ks, dg, wok, wt, drow);
     __syncthreads();
+    mma(R, wt);
+  };
+
+  load(0, R0);
+  load(1, R1);
+  load(2, R2);
+  wait_all_memory();  // codebook (LDS-direct) has landed (and the first steps)
+  __syncthreads();
+  // main loop: four steps per iteration, a single exit (a loop with several
+  // exits made the compiler move the accumulators between register files)
+  int ks = 0;
+  for (; ks + 4 <= nks; ks += 4) {
+    load(ks + 3, R3);
+    step(ks, R0);
+    load(ks + 4, R0);
+    step(ks + 1, R1);
+    load(ks + 5, R1);
+    step(ks + 2, R2);
+    load(ks + 6, R2);
+    step(ks + 3, R3);
   }
+  // remainder: sets R0, R1, R2 hold steps ks, ks+1, ks+2
+  const int rem = nks - ks;
+  if (rem > 0) step(ks, R0);
+  if (rem > 1) step(ks + 1, R1);
+  if (rem > 2) step(ks + 2, R2);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int jn = 0; jn < 2; ++jn) {
-      const int col = n0 + wn * 64 + 32 * jn + (lane & 31);
+    for (int jn = 0; jn < 4; ++jn) {
+      const int col = n0 + 32 * jn + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int row = m0 + wave * 64 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (row < a.m && col < a.n) a.y[(size_t)row * a.n + col] = acc[i][jn][r];
       }
     }
@@ -147,8 +354,160 @@ __global__ __launch_bounds__(256) void k_gemm_large(GemmArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kSWaves = 8;
 
+// Registers of one 128-column super step for one lane: index bits of its 4
+// consecutive groups per stage, their scale, and 32 x values of its token.
+template <int S>
+struct SmallRegs {
+  uint32_t lo[S];  // 4 low bytes (8/12-bit) or, 16-bit, 2 indices in lo and 2 in hi
+  uint32_t hi[S];  // 12-bit: 4 nibbles; 16-bit: indices 2 and 3
+  uint32_t sc;     // fp16 bits (all 4 groups share a block: scale_block % 32 == 0)
+  uint4 av[4];     // x[token][128 J + 32 q .. + 32)
+};
+
+template <int S, int BITS>
+__device__ __forceinline__ void small_load(const GemmArgs &a, int J, int q, int wrow_c, int tok_c, SmallRegs<S> &R) {
+  const int g = 16 * J + 4 * q;
+  const size_t f = (size_t)wrow_c * a.G + g;
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    if (BITS == 16) {
+      const uint2 v = *reinterpret_cast<const uint2 *>(a.i16[t] + f);
+      R.lo[t] = v.x;
+      R.hi[t] = v.y;
+    } else {
+      R.lo[t] = *reinterpret_cast<const uint32_t *>(a.lo[t] + f);
+      R.hi[t] = (BITS == 12) ? (uint32_t) * reinterpret_cast<const uint16_t *>(a.hi[t] + (f >> 1)) : 0u;
+    }
+  }
+  R.sc = a.sc[(size_t)wrow_c * a.nblk + scale_blk(a, g)];
+  const uint4 *px = reinterpret_cast<const uint4 *>(a.x + (size_t)tok_c * a.k + 8 * g);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) R.av[v] = px[v];
+}
+
+// 1 <= m <= 16.  Persistent workgroups of 8 waves walk 16-row slabs of W.
+// A 128-column super step J holds 16 groups; lane l (W row and token l%16,
+// slot q = l/16) takes groups 16J + 4q + r and feeds group r to the r-th
+// v_mfma_f32_16x16x32_bf16 of the step in k-slot q (the same permutation of
+// k for A and B, so the contraction is unchanged).  Wave w takes super
+// steps w, w+8, ...; the next one loads while the current one decodes
+// (LDS codebook gathers straight into B fragments) and multiplies.  The
+// eight wave partials are added in LDS in a fixed order.
+// Requires K % 128 == 0 and scale_block % 32 == 0 (else k_gemm_small_gen).
 template <int S, int BITS, bool CB_LDS>
 __global__ __launch_bounds__(kSWaves * 64) void k_gemm_small(GemmArgs a) {
+  __shared__ uint4 s_cb[CB_LDS ? (S << BITS) : 1];
+  __shared__ float s_red[kSWaves][16][17];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  if (CB_LDS) {
+    constexpr int CBN = S << BITS;
+#pragma unroll 4
+    for (int r = 0; r < (CBN + kSWaves * 64 - 1) / (kSWaves * 64); ++r) {
+      const int blk = (r * kSWaves + wave) * 64;
+      if (blk < CBN)
+        lds_direct_16(reinterpret_cast<const uint4 *>(a.cb[blk >> BITS]) + (blk & ((1 << BITS) - 1)) + lane,
+                      s_cb + blk);
+    }
+    wait_all_memory();
+    __syncthreads();
+  }
+  const int j16 = lane & 15;  // W row within the slab = token of the A fragment
+  const int q = lane >> 4;
+  const int tok_c = j16 < a.m ? j16 : a.m - 1;  // tokens past m only feed unstored outputs
+  const int nJ = a.G / 16;
+  const int nslabs = (a.n + 15) / 16;
+
+  auto decode = [&](const SmallRegs<S> &R, int r) -> bf16x8_t {
+    float w[8];
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+      uint32_t idx;
+      if (BITS == 16) idx = (r < 2 ? (R.lo[t] >> (16 * r)) : (R.hi[t] >> (16 * (r - 2)))) & 0xffffu;
+      else {
+        idx = (R.lo[t] >> (8 * r)) & 0xffu;
+        if (BITS == 12) idx |= ((R.hi[t] >> (4 * r)) & 0xfu) << 8;
+      }
+      const uint4 v = CB_LDS ? s_cb[(t << BITS) + idx] : reinterpret_cast<const uint4 *>(a.cb[t])[idx];
+      const uint32_t hv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float c0 = h2f(hv[e] & 0xffffu), c1 = h2f(hv[e] >> 16);
+        w[2 * e] = (t == 0) ? c0 : w[2 * e] + c0;
+        w[2 * e + 1] = (t == 0) ? c1 : w[2 * e + 1] + c1;
+      }
+    }
+    const float sf = h2f(R.sc);
+    uint4 pk;
+    pk.x = pack_bf16(sf * w[0], sf * w[1]);
+    pk.y = pack_bf16(sf * w[2], sf * w[3]);
+    pk.z = pack_bf16(sf * w[4], sf * w[5]);
+    pk.w = pack_bf16(sf * w[6], sf * w[7]);
+    return __builtin_bit_cast(bf16x8_t, pk);
+  };
+
+  for (int slab = blockIdx.x; slab < nslabs; slab += gridDim.x) {
+    const int n0 = slab * 16;
+    const int wrow = n0 + j16;
+    const int wrow_c = wrow < a.n ? wrow : a.n - 1;  // rows past n only feed unstored outputs
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // this wave's super steps: J_i = wave + 8 i; ring of four register sets,
+    // three super steps in flight while one is decoded and multiplied
+    const int nmine = wave < nJ ? (nJ - 1 - wave) / kSWaves + 1 : 0;
+    SmallRegs<S> R0, R1, R2, R3;
+    // unconditional prefetch (past this wave's last super step it reloads
+    // the last one), so no branch surrounds the loads
+    auto load = [&](int i, SmallRegs<S> &R) {
+      small_load<S, BITS>(a, wave + kSWaves * (i < nmine ? i : nmine - 1), q, wrow_c, tok_c, R);
+      sched_fence();  // keep the prefetch here, three super steps ahead of its use
+    };
+    auto run = [&](const SmallRegs<S> &R) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bf16x8_t bfr = decode(R, r);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, R.av[r]), bfr, acc, 0, 0, 0);
+      }
+    };
+    if (nmine > 0) {  // wave-uniform; every wave still reaches both barriers below
+      load(0, R0);
+      load(1, R1);
+      load(2, R2);
+      int i = 0;
+      for (; i + 4 <= nmine; i += 4) {  // single exit (see the large-M kernel)
+        load(i + 3, R3);
+        run(R0);
+        load(i + 4, R0);
+        run(R1);
+        load(i + 5, R1);
+        run(R2);
+        load(i + 6, R2);
+        run(R3);
+      }
+      const int rem = nmine - i;  // sets R0, R1, R2 hold super steps i, i+1, i+2
+      if (rem > 0) run(R0);
+      if (rem > 1) run(R1);
+      if (rem > 2) run(R2);
+    }
+    // lane holds D[token 4*(lane/16)+r][W row lane%16]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_red[wave][4 * (lane >> 4) + r][lane & 15] = acc[r];
+    __syncthreads();
+    if (tid < 256) {
+      const int ti = tid >> 4, wj = tid & 15;
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kSWaves; ++w) sum += s_red[w][ti][wj];
+      if (ti < a.m && n0 + wj < a.n) a.y[(size_t)ti * a.n + n0 + wj] = sum;
+    }
+    __syncthreads();
+  }
+}
+
+// General small-M path (any K % 8 == 0, any scale block): one group per lane
+// per 32-column K step, byte-wise index loads.
+template <int S, int BITS, bool CB_LDS>
+__global__ __launch_bounds__(kSWaves * 64) void k_gemm_small_gen(GemmArgs a) {
   __shared__ uint4 s_cb[CB_LDS ? (S << BITS) : 1];
   __shared__ float s_red[kSWaves][16][17];
   const int tid = threadIdx.x;
@@ -160,8 +519,8 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_small(GemmArgs a) {
     __syncthreads();
   }
   const int nks = (a.G + 3) / 4;
-  const int tok = lane & 15;   // A row (token) and B column (W row) of this lane
-  const int q = lane >> 4;     // group within the K step
+  const int tok = lane & 15;
+  const int q = lane >> 4;
   const int nslabs = (a.n + 15) / 16;
   for (int slab = blockIdx.x; slab < nslabs; slab += gridDim.x) {
     const int n0 = slab * 16;
@@ -177,16 +536,15 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_small(GemmArgs a) {
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
                                                     __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
     }
-    // lane holds D[token 4*(lane/16)+r][W row lane%16]
 #pragma unroll
     for (int r = 0; r < 4; ++r) s_red[wave][4 * (lane >> 4) + r][lane & 15] = acc[r];
     __syncthreads();
     if (tid < 256) {
       const int ti = tid >> 4, wj = tid & 15;
-      float s = 0.f;
+      float sum = 0.f;
 #pragma unroll
-      for (int w = 0; w < kSWaves; ++w) s += s_red[w][ti][wj];
-      if (ti < a.m && n0 + wj < a.n) a.y[(size_t)ti * a.n + n0 + wj] = s;
+      for (int w = 0; w < kSWaves; ++w) sum += s_red[w][ti][wj];
+      if (ti < a.m && n0 + wj < a.n) a.y[(size_t)ti * a.n + n0 + wj] = sum;
     }
     __syncthreads();
   }
@@ -213,6 +571,8 @@ static GemmArgs make_gemm_args(const WView &w, const uint16_t *x, int m, float *
   a.S = w.S;
   a.nblk = w.nblk;
   a.bs = w.bs;
+  const int gb = w.bs / 8;
+  a.gshift = (gb & (gb - 1)) == 0 ? __builtin_ctz((unsigned)gb) : -1;
   return a;
 }
 
@@ -223,13 +583,19 @@ static void launch_gemm_sb(const GemmArgs &a0, hipStream_t s) {
     const int nslabs = (a.n + 15) / 16;
     int nwg = device_cu_count();
     if (nwg > nslabs) nwg = nslabs;
-    hipLaunchKernelGGL((k_gemm_small<S, BITS, CB_LDS>), dim3(nwg), dim3(kSWaves * 64), 0, s, a);
+    if (a.k % 128 == 0 && a.bs % 32 == 0)
+      hipLaunchKernelGGL((k_gemm_small<S, BITS, CB_LDS>), dim3(nwg), dim3(kSWaves * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_gemm_small_gen<S, BITS, CB_LDS>), dim3(nwg), dim3(kSWaves * 64), 0, s, a);
   } else {
     a.tiles_m = (a.m + kLM - 1) / kLM;
     a.tiles_n = (a.n + kLN - 1) / kLN;
     const int total = a.tiles_m * a.tiles_n;
     a.per_xcd = (total + 7) / 8;
-    hipLaunchKernelGGL((k_gemm_large<S, BITS, CB_LDS>), dim3(8 * a.per_xcd), dim3(256), 0, s, a);
+    if (a.k % 32 == 0)
+      hipLaunchKernelGGL((k_gemm_large<S, BITS, CB_LDS, true>), dim3(8 * a.per_xcd), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_gemm_large<S, BITS, CB_LDS, false>), dim3(8 * a.per_xcd), dim3(256), 0, s, a);
   }
 }
 

@@ -88,6 +88,14 @@ __device__ __forceinline__ void lds_direct_16(const void *src, void *lds_wave_ba
 #endif
 }
 
+// Scheduling fence: the compiler may not move instructions across it (keeps
+// prefetch loads where they are issued instead of sinking them to their use).
+__device__ __forceinline__ void sched_fence() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+
 // Wait for every outstanding memory operation of the wave.
 __device__ __forceinline__ void wait_all_memory() {
 #if defined(__HIP_DEVICE_COMPILE__)
