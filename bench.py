@@ -43,6 +43,11 @@ def parse():
     ap.add_argument("--quick", action="store_true", help="headline only (no detail, no cpu baseline)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu baseline")
     ap.add_argument("--only", default="", help="comma list of detail legs to run")
+    ap.add_argument("--traffic-probe", default="", metavar="N,K",
+                    help="launch only the GEMV of shape N x K (llama8b format, rotating copies) "
+                         "and a plain 256 MiB device copy, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("N,K", "FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
+                    help="turn the two counter CSVs of --traffic-probe into a traffic summary")
     return ap.parse_args()
 
 
@@ -283,8 +288,84 @@ def cpu_baseline():
             "seconds": dt, "host_cpus": os.cpu_count()}
 
 
+KERNEL_SOURCES = ["compressed_index_matmul_amd/csrc/k_gemv.hip", "compressed_index_matmul_amd/csrc/vqmm_device.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemv_lds_llama8b_down_4096x14336_traffic.json")
+COPY_BYTES = 256 << 20
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_probe(spec, launches=20):
+    """Launch the batch-1 decode GEMV of one Llama-3-8B-shaped linear
+    `launches` times (weights rotated through >= 512 MiB of copies), then a
+    plain 256 MiB float32 copy (`dst = src * 1`) whose HBM bytes are known."""
+    import torch
+    import vqsynth
+    import compressed_index_matmul_amd as vq
+    n, k = (int(v) for v in spec.split(","))
+    ws, act_ss = vqsynth.workload_weights("llama8b")
+    sw = [w for w in ws if (w.n_out, w.k_in) == (n, k)][0]
+    st, _ = vqsynth.make_x(1, k, "bf16", act_ss.spawn(1)[0])
+    x = torch.from_numpy(st.view(np.int16)).cuda().view(torch.bfloat16)
+    sets = upload_set(vq, [sw], copies_for(compressed_bytes(sw)))
+    y = torch.empty((1, n), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    for i in range(launches):
+        vq.vq_gemv(sets[i % len(sets)][0], x, y=y)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": [n, k], "launches": launches, "copy_bytes": COPY_BYTES}), flush=True)
+
+
+def traffic_summary(spec, fetch_csv, write_csv, out_json):
+    """HBM bytes per GEMV dispatch from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by bytes-moved / counter of the plain copy: the
+    copy reads COPY_BYTES and writes COPY_BYTES."""
+    import csv
+
+    def read(path, counter):
+        gemv, other = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"]) * 1024.0
+            (gemv if "k_gemv_lds" in r["Kernel_Name"] else other).append(v)
+        return gemv, other
+    gf, of = read(fetch_csv, "FETCH_SIZE")
+    gw, ow = read(write_csv, "WRITE_SIZE")
+    # the copy is the dispatch with the largest read (resp. write) besides the GEMV
+    f_scale = COPY_BYTES / max(of)
+    w_scale = COPY_BYTES / max(ow)
+    fetch = float(np.median(gf)) * f_scale
+    write = float(np.median(gw)) * w_scale
+    n, k = (int(v) for v in spec.split(","))
+    out = {"kernel": "k_gemv_lds", "shape": [n, k], "source_hash": kernel_source_hash(),
+           "dispatches": len(gf),
+           "fetch_kib_raw_median": float(np.median(gf)) / 1024.0, "write_kib_raw_median": float(np.median(gw)) / 1024.0,
+           "copy_fetch_kib_raw": max(of) / 1024.0, "copy_write_kib_raw": max(ow) / 1024.0,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+           "traffic_bytes_per_launch": fetch + write}
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs on a "
               "single MI355X and has no multi-GPU path)", file=sys.stderr)
@@ -297,12 +378,24 @@ def main():
     vq.lib()
     torch.cuda.set_device(0)
 
+    if args.traffic_probe:
+        traffic_probe(args.traffic_probe)
+        return
+
     log("headline: llama8b decode, batch 1")
     head = run_decode_leg(vq, "llama8b", args.steps, args.warmup)
     # dominant kernel of the step: the linear with the largest kernel time
     dom = max(head["linears"], key=lambda e: e["kernel_us_mean"])
+    traffic = None
+    try:  # counters taken on this exact kernel source, else null
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        if t.get("source_hash") == kernel_source_hash() and t.get("shape") == dom["shape"]:
+            traffic = t["traffic_bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        traffic = None
     roof = {"bound": "hbm", "achieved": dom["gbs_algorithmic"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": dom["gbs_algorithmic"] / HBM_PEAK_GBS, "traffic": None,
+            "frac": dom["gbs_algorithmic"] / HBM_PEAK_GBS, "traffic": traffic,
             "kernel": "k_gemv_lds (2 stages, 12-bit)", "shape": dom["shape"],
             "kernel_us_mean": dom["kernel_us_mean"], "algorithmic_bytes": dom["algorithmic_bytes"]}
     detail = {"headline_linears": head["linears"], "weight_copies": head["weight_copies"],

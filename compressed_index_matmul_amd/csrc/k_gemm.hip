@@ -4,11 +4,11 @@
 // memory).
 //
 // k_gemm_large -- m > 16.  Tile 256 (tokens) x 128 (W rows), K step 32
-//   (4 groups), 4 waves in a 2 x 2 grid, each owning a 128 x 64 block of
-//   v_mfma_f32_32x32x16_bf16 accumulators.  Per K step every thread decodes
-//   two groups (stage sum and scale in fp32, rounded to bf16) into the LDS W
-//   tile, which all four waves read as B fragments; A fragments (x) are
-//   loaded from global memory straight into registers.  Tiles are ordered so
+//   (4 groups), 4 waves stacked along the tokens, each owning 64 tokens x
+//   128 W rows of v_mfma_f32_32x32x16_bf16 accumulators.  Per K step every
+//   thread decodes two groups (stage sum and scale in fp32, rounded to bf16)
+//   into the LDS W tile, which all four waves read as B fragments; A
+//   fragments (x) are loaded from global memory straight into registers.  Tiles are ordered so
 //   that consecutive tiles of one token panel land on the same XCD (its L2
 //   keeps the x panel).
 //
