@@ -3,20 +3,22 @@
 // codebook vectors, and accumulates against the indices without forming W;
 // split-K-style lane partials reduced inside the wave in a fixed order).
 //
-// k_gemv_lds  -- codebooks that fit in LDS (8/12-bit, S * 2^b * 16 B <= 128 KiB),
-//                K % 32 == 0, scale_block % 32 == 0, K <= 16384.
-//   * persistent grid, one workgroup per CU slot; every workgroup stages the
-//     codebooks into LDS once and walks rows (one row per wave at a time);
-//   * lane l owns the 4-group chunks c = l + 64 j of every row, so its slice of
-//     x stays in registers for the whole launch;
-//   * per chunk and stage the lane loads one dword of the low-byte plane and
-//     one short of the high-nibble plane (coalesced 256 B + 128 B per wave),
-//     the next row's loads are issued before the current row is computed;
-//   * bf16 x is held as fp16 after a per-lane power-of-two rescale (exact for
-//     values within 2^28 of the lane's largest |x|), so a group-stage costs
-//     one 16-byte LDS gather and four v_dot2_f32_f16; fp32 x uses v_fma_mix;
-//   * the lane partial is scaled per chunk, un-rescaled, and summed across
-//     the wave with DPP (fixed order, no atomics).
+// k_gemv_lds  -- codebooks and x that fit in one workgroup's LDS (8/12-bit,
+//                K % 32 == 0, scale_block % 32 == 0; K <= 16384 for bf16 x).
+//   * persistent grid, one workgroup per CU holding a contiguous block of
+//     rows; its waves take every WAVES-th row of the block;
+//   * prologue: x loads, the first rows' index loads (HBM) and the codebooks
+//     (LDS-direct, global_load_lds_dwordx4) are all in flight together; x is
+//     converted once per workgroup into LDS;
+//   * lane l owns the 4-group chunks c = l + 64 j of every row; per chunk and
+//     stage it loads one dword of the low-byte plane and one short of the
+//     high-nibble plane (coalesced 256 B + 128 B per wave); a ring of row
+//     buffers keeps the next rows' loads in flight while a row is computed;
+//   * bf16 x is held as fp16 after a per-chunk power-of-two rescale (exact
+//     for values within 2^28 of the chunk's largest |x|), so a group-stage
+//     costs one 16-byte LDS gather and four v_dot2_f32_f16; fp32 x uses fma;
+//   * the lane partial is scaled per chunk (block scale times the inverse
+//     rescale) and summed across the wave with DPP (fixed order, no atomics).
 //
 // k_gemv_gen  -- everything else (16-bit indices into a 1 MiB codebook, 3-4
 //                12-bit stages, ragged K or scale blocks): codebook rows are
@@ -43,35 +45,40 @@ struct GemvArgs {
 // ---------------------------------------------------------------------------
 // fast path
 // ---------------------------------------------------------------------------
-template <int S, int BITS, int CPL, int WAVES, bool XF16, int RB>
+// LDS bytes of the fast kernel: codebooks, x (fp16: 64 B per 4-group chunk
+// plus a float factor; fp32: 128 B per chunk) for 64 * CPL chunks.
+__host__ __device__ constexpr size_t gemv_lds_bytes(int S, int BITS, int CPL, bool XF16) {
+  return (size_t)(S << BITS) * 16 + (size_t)64 * CPL * (XF16 ? 64 + 4 : 128 + 0) + (XF16 ? 0 : 4);
+}
+constexpr size_t kLdsBytes = 163840;  // 160 KiB per workgroup on gfx950
+
+template <int S, int BITS, int CPL, int WAVES, bool XF16, int D, bool XREG, bool PIPE>
 __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
   constexpr int NT = WAVES * 64;
   constexpr int CBN = S << BITS;                 // codebook rows of all stages
   constexpr int CB_ITERS = (CBN + NT - 1) / NT;  // 1 KiB LDS-direct loads per wave
   constexpr int XV = XF16 ? 4 : 8;               // 16-byte x vectors per chunk
+  constexpr int CMAX = 64 * CPL;                 // chunk capacity
+  constexpr int XCH = (CMAX + NT - 1) / NT;      // x chunks converted per thread
+  static_assert(XF16 || XREG, "fp32 x is always held in registers");
+  // x in LDS is vector-major (s_x[v * CMAX + c]) so that a wave reading the
+  // same vector of 64 consecutive chunks touches consecutive 16-byte slots.
   __shared__ uint4 s_cb[CBN];
+  __shared__ uint4 s_x[CMAX * XV];
+  __shared__ float s_f[XF16 ? CMAX : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int stride = gridDim.x * WAVES;
-  int row = blockIdx.x * WAVES + wave;
+  // Each workgroup owns a contiguous block of rows (equal sizes up to one
+  // row); its waves take every WAVES-th row of the block.
+  const int per_wg = (a.n + gridDim.x - 1) / gridDim.x;
+  const int blk_lo = blockIdx.x * per_wg;
+  const int blk_hi = min(a.n, blk_lo + per_wg);
+  constexpr int stride = WAVES;
+  const int row0 = blk_lo + wave;
   const int last = a.n - 1;
+  const int nrows = row0 < blk_hi ? (blk_hi - 1 - row0) / stride + 1 : 0;  // rows of this wave (uniform)
 
-  // Global loads are issued oldest-first in the order they are needed:
-  // codebooks, then x, then the first row's indices, so waiting for the
-  // codebooks does not wait for anything else.  Chunks past the end of the
-  // row load a valid duplicate and are masked out of the sum; no branch
-  // surrounds a load, so every load stays in flight until its first use.
-  // Codebooks stream straight into LDS (global_load_lds_dwordx4: lane l of a
-  // wave writes 16 bytes at the wave's LDS base + 16 l), no registers used.
-#pragma unroll
-  for (int r = 0; r < CB_ITERS; ++r) {
-    const int blk = (r * WAVES + wave) * 64;  // first codebook row of this wave's 1 KiB
-    if (blk < CBN) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(a.cb[blk >> BITS]) + (blk & ((1 << BITS) - 1)) + lane;
-      lds_direct_16(src, s_cb + blk);
-    }
-  }
   int cc[CPL];
   bool ok[CPL];
 #pragma unroll
@@ -80,138 +87,224 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
     ok[j] = c < a.C;
     cc[j] = ok[j] ? c : a.C - 1;
   }
-  uint4 xr[CPL][XV];
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const uint4 *px = XF16 ? reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.x) + 32 * cc[j])
-                           : reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(a.x) + 32 * cc[j]);
-#pragma unroll
-    for (int v = 0; v < XV; ++v) xr[j][v] = px[v];
-  }
 
-  // Rows of this wave: row0 + k * stride.  They are processed in batches of
-  // RB rows whose index loads are all in flight together; two register sets
-  // alternate so the next batch loads while the current one is computed.
-  // Guards are wave-uniform (a row exists or not for the whole wave).
-  const int row0 = row;
-  uint32_t L[RB][CPL][S], H[RB][CPL][S], SCb[RB][CPL];
-#define VQ_LOAD_BATCH(B_, L_, H_, SC_)                                                     \
-  _Pragma("unroll") for (int i = 0; i < RB; ++i) {                                         \
-    const int rr = row0 + ((B_) * RB + i) * stride;                                        \
-    if (rr < a.n) {                                                                        \
-      const size_t rb = (size_t)rr * a.G;                                                  \
-      _Pragma("unroll") for (int j = 0; j < CPL; ++j) {                                    \
-        _Pragma("unroll") for (int t = 0; t < S; ++t) {                                    \
-          L_[i][j][t] = *reinterpret_cast<const uint32_t *>(a.lo[t] + rb + 4 * cc[j]);     \
-          if (BITS == 12)                                                                  \
-            H_[i][j][t] = *reinterpret_cast<const uint16_t *>(a.hi[t] + (rb >> 1) + 2 * cc[j]); \
-        }                                                                                  \
-        SC_[i][j] = a.sc[(size_t)rr * a.nblk + (32 * cc[j]) / a.bs];                       \
-      }                                                                                    \
-    }                                                                                      \
-  }
-  VQ_LOAD_BATCH(0, L, H, SCb);
+  // Index planes and scales of one row (this lane's chunks).
+  struct RowIdx {
+    uint32_t L[CPL][S];
+    uint32_t H[CPL][S];
+    uint32_t SC[CPL];
+  };
+  auto load_row = [&](int r, RowIdx &R) {
+    const int rr = min(row0 + r * stride, last);  // past the end: a valid duplicate, never stored
+    const size_t rb = (size_t)rr * a.G;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+#pragma unroll
+      for (int t = 0; t < S; ++t) {
+        R.L[j][t] = *reinterpret_cast<const uint32_t *>(a.lo[t] + rb + 4 * cc[j]);
+        if (BITS == 12) R.H[j][t] = *reinterpret_cast<const uint16_t *>(a.hi[t] + (rb >> 1) + 2 * cc[j]);
+      }
+      R.SC[j] = a.sc[(size_t)rr * a.nblk + (32 * cc[j]) / a.bs];
+    }
+  };
 
-  // this lane's slice of x, held for the whole launch
-  half2_t xh[XF16 ? CPL : 1][16];
-  float xf[XF16 ? 1 : CPL][32];
-  int xexp = 0;
-  if (XF16) {
-    float mx = 0.f;
+  // Global loads are issued in the order their latency matters: this
+  // thread's x chunks (L2), the first D rows' indices (HBM), then the
+  // codebooks straight into LDS (global_load_lds_dwordx4: lane l of a wave
+  // writes 16 bytes at the wave's LDS base + 16 l).  Loads return in order,
+  // so converting x waits for the x loads only.  No branch surrounds a load:
+  // out-of-range chunks and rows load a valid duplicate and are discarded.
+  // (waves whose chunks all lie past the end of x load nothing: a
+  // wave-uniform branch)
+  uint4 xin[XCH][XV];
 #pragma unroll
-    for (int j = 0; j < CPL; ++j)
+  for (int i = 0; i < XCH; ++i) {
+    if (wave * 64 + NT * i < a.C) {
+      const int c = min(tid + NT * i, a.C - 1);
+      const uint4 *px = XF16 ? reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.x) + 32 * c)
+                             : reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(a.x) + 32 * c);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const uint32_t w4[4] = {xr[j][v].x, xr[j][v].y, xr[j][v].z, xr[j][v].w};
+      for (int v = 0; v < XV; ++v) xin[i][v] = px[v];
+    }
+  }
+  sched_fence();
+  RowIdx R[D + 1];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float m2 = fmaxf(fabsf(bf2f(w4[e] & 0xffffu)), fabsf(bf2f(w4[e] >> 16)));
-          mx = ok[j] ? fmaxf(mx, m2) : mx;
+  for (int k = 0; k < D; ++k) load_row(k, R[k]);
+  sched_fence();
+#pragma unroll
+  for (int r = 0; r < CB_ITERS; ++r) {
+    const int blk = (r * WAVES + wave) * 64;  // first codebook row of this wave's 1 KiB
+    if (blk < CBN) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(a.cb[blk >> BITS]) + (blk & ((1 << BITS) - 1)) + lane;
+      lds_direct_16(src, s_cb + blk);
+    }
+  }
+  sched_fence();
+
+  // x -> LDS.  bf16 x becomes fp16 after a per-chunk power-of-two rescale
+  // that puts the chunk's largest |x| in [2^14, 2^15): exact for every value
+  // within 2^28 of that maximum.  The chunk's partial dot product is scaled
+  // back by s_f[c].
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) {
+    const int c = tid + NT * i;
+    if (c < a.C) {
+      if (XF16) {
+        float mx = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t w4[4] = {xin[i][v].x, xin[i][v].y, xin[i][v].z, xin[i][v].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            mx = fmaxf(mx, fmaxf(fabsf(bf2f(w4[e] & 0xffffu)), fabsf(bf2f(w4[e] >> 16))));
         }
+        const int xexp = (mx > 0.f && mx <= 3.0e38f) ? 14 - ilogbf(mx) : 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t w4[4] = {xin[i][v].x, xin[i][v].y, xin[i][v].z, xin[i][v].w};
+          uint32_t o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const half2_t h = half2_t{(_Float16)ldexpf(bf2f(w4[e] & 0xffffu), xexp),
+                                      (_Float16)ldexpf(bf2f(w4[e] >> 16), xexp)};
+            o[e] = __builtin_bit_cast(uint32_t, h);
+          }
+          s_x[v * CMAX + c] = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+        s_f[c] = ldexpf(1.f, -xexp);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 8; ++v) s_x[v * CMAX + c] = xin[i][v];
       }
-    // the largest |x| scaled into [2^14, 2^15): fp16 holds every bf16 value
-    // within 2^28 of it exactly
-    if (mx > 0.f) xexp = 14 - ilogbf(mx);
-#pragma unroll
-    for (int j = 0; j < CPL; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const uint32_t w4[4] = {xr[j][v].x, xr[j][v].y, xr[j][v].z, xr[j][v].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          xh[j][4 * v + e] = half2_t{(_Float16)ldexpf(bf2f(w4[e] & 0xffffu), xexp),
-                                     (_Float16)ldexpf(bf2f(w4[e] >> 16), xexp)};
-      }
-  } else {
-#pragma unroll
-    for (int j = 0; j < CPL; ++j)
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        xf[j][4 * v] = __uint_as_float(xr[j][v].x);
-        xf[j][4 * v + 1] = __uint_as_float(xr[j][v].y);
-        xf[j][4 * v + 2] = __uint_as_float(xr[j][v].z);
-        xf[j][4 * v + 3] = __uint_as_float(xr[j][v].w);
-      }
+    }
   }
-  // the LDS-direct codebook loads of this wave have landed; then the barrier
-  // makes every wave's part visible
+  // the LDS-direct codebook loads of this wave have landed; the barrier
+  // makes every wave's codebook part and x visible
   wait_all_memory();
   __syncthreads();
 
-  // One row: gather every codebook row of a chunk first, then its dot
-  // products; scale per chunk; masked chunks add nothing.
-#define VQ_ROW(R_, L_, H_, SC_)                                                              \
-  {                                                                                          \
-    float acc = 0.f;                                                                         \
-    _Pragma("unroll") for (int j = 0; j < CPL; ++j) {                                        \
-      uint4 v[S][4];                                                                         \
-      _Pragma("unroll") for (int t = 0; t < S; ++t)                                          \
-      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                        \
-        uint32_t idx = (L_[j][t] >> (8 * q)) & 0xffu;                                        \
-        if (BITS == 12) idx |= ((H_[j][t] >> (4 * q)) & 0xfu) << 8;                          \
-        v[t][q] = s_cb[(t << BITS) + idx];                                                   \
-      }                                                                                      \
-      float d = 0.f;                                                                         \
-      _Pragma("unroll") for (int t = 0; t < S; ++t)                                          \
-      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                        \
-        if (XF16) {                                                                          \
-          d = __builtin_amdgcn_fdot2(as_h2(v[t][q].x), xh[j][4 * q + 0], d, false);          \
-          d = __builtin_amdgcn_fdot2(as_h2(v[t][q].y), xh[j][4 * q + 1], d, false);          \
-          d = __builtin_amdgcn_fdot2(as_h2(v[t][q].z), xh[j][4 * q + 2], d, false);          \
-          d = __builtin_amdgcn_fdot2(as_h2(v[t][q].w), xh[j][4 * q + 3], d, false);          \
-        } else {                                                                             \
-          const uint32_t hv[4] = {v[t][q].x, v[t][q].y, v[t][q].z, v[t][q].w};               \
-          _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                    \
-            d = fmaf(h2f(hv[e] & 0xffffu), xf[j][8 * q + 2 * e], d);                         \
-            d = fmaf(h2f(hv[e] >> 16), xf[j][8 * q + 2 * e + 1], d);                         \
-          }                                                                                  \
-        }                                                                                    \
-      }                                                                                      \
-      acc = ok[j] ? fmaf(h2f(SC_[j]), d, acc) : acc;                                         \
-    }                                                                                        \
-    if (XF16) acc = ldexpf(acc, -xexp);                                                      \
-    const float tot = wave_sum(acc);                                                         \
-    if (lane == 0) a.y[R_] = tot;                                                            \
-  }
-#define VQ_BATCH(B_, L_, H_, SC_)                                                            \
-  _Pragma("unroll") for (int i = 0; i < RB; ++i) {                                           \
-    const int rr = row0 + ((B_) * RB + i) * stride;                                          \
-    if (rr < a.n) VQ_ROW(rr, L_[i], H_[i], SC_[i]);                                          \
+  // this lane's x chunks: registers for the whole launch (XREG) or LDS reads
+  // per use; the per-chunk factor, zero for chunks past the end of the row
+  half2_t xh[XREG && XF16 ? CPL : 1][16];
+  float xf[XF16 ? 1 : CPL][32];
+  float fm[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    fm[j] = XF16 ? (ok[j] ? s_f[cc[j]] : 0.f) : (ok[j] ? 1.f : 0.f);
+    if (XF16 && XREG) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint4 u = s_x[v * CMAX + cc[j]];
+        xh[j][4 * v + 0] = as_h2(u.x);
+        xh[j][4 * v + 1] = as_h2(u.y);
+        xh[j][4 * v + 2] = as_h2(u.z);
+        xh[j][4 * v + 3] = as_h2(u.w);
+      }
+    }
+    if (!XF16) {
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const uint4 u = s_x[v * CMAX + cc[j]];
+        xf[j][4 * v + 0] = __uint_as_float(u.x);
+        xf[j][4 * v + 1] = __uint_as_float(u.y);
+        xf[j][4 * v + 2] = __uint_as_float(u.z);
+        xf[j][4 * v + 3] = __uint_as_float(u.w);
+      }
+    }
   }
 
-  const int nrows = row0 < a.n ? (a.n - 1 - row0) / stride + 1 : 0;  // rows of this wave
-  const int nbatch = (nrows + RB - 1) / RB;
-  uint32_t L2[RB][CPL][S], H2[RB][CPL][S], SC2[RB][CPL];
-  for (int b = 0; b < nbatch; b += 2) {
-    if (b + 1 < nbatch) VQ_LOAD_BATCH(b + 1, L2, H2, SC2);
-    VQ_BATCH(b, L, H, SCb);
-    if (b + 1 >= nbatch) break;
-    if (b + 2 < nbatch) VQ_LOAD_BATCH(b + 2, L, H, SCb);
-    VQ_BATCH(b + 1, L2, H2, SC2);
+  // One item = one 4-group chunk of a row: S x 4 LDS gathers (in the order
+  // the dot products consume them) and, without XREG, the chunk's 64 B of x.
+  struct Item {
+    uint4 v[S][4];
+    uint4 x[XREG ? 1 : 4];
+  };
+  auto gather = [&](const RowIdx &Rr, int j, Item &it) {
+#pragma unroll
+    for (int t = 0; t < S; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t idx = (Rr.L[j][t] >> (8 * q)) & 0xffu;
+        if (BITS == 12) idx |= ((Rr.H[j][t] >> (4 * q)) & 0xfu) << 8;
+        it.v[t][q] = s_cb[(t << BITS) + idx];
+      }
+    if (!XREG) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) it.x[v] = s_x[v * CMAX + cc[j]];
+    }
+  };
+  auto dot = [&](int j, const Item &it) -> float {
+    float d = 0.f;
+#pragma unroll
+    for (int t = 0; t < S; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (XF16) {
+          const uint4 xq = it.x[XREG ? 0 : q];
+          const half2_t x0 = XREG ? xh[XREG ? j : 0][4 * q + 0] : as_h2(xq.x);
+          const half2_t x1 = XREG ? xh[XREG ? j : 0][4 * q + 1] : as_h2(xq.y);
+          const half2_t x2 = XREG ? xh[XREG ? j : 0][4 * q + 2] : as_h2(xq.z);
+          const half2_t x3 = XREG ? xh[XREG ? j : 0][4 * q + 3] : as_h2(xq.w);
+          d = __builtin_amdgcn_fdot2(as_h2(it.v[t][q].x), x0, d, false);
+          d = __builtin_amdgcn_fdot2(as_h2(it.v[t][q].y), x1, d, false);
+          d = __builtin_amdgcn_fdot2(as_h2(it.v[t][q].z), x2, d, false);
+          d = __builtin_amdgcn_fdot2(as_h2(it.v[t][q].w), x3, d, false);
+        } else {
+          const uint32_t hv[4] = {it.v[t][q].x, it.v[t][q].y, it.v[t][q].z, it.v[t][q].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            d = fmaf(h2f(hv[e] & 0xffffu), xf[XF16 ? 0 : j][8 * q + 2 * e], d);
+            d = fmaf(h2f(hv[e] >> 16), xf[XF16 ? 0 : j][8 * q + 2 * e + 1], d);
+          }
+        }
+      }
+    return d;
+  };
+  // One row: CPL items (with PIPE the gathers of chunk j+1 are issued before
+  // the dot products of chunk j), one fixed-order wave reduction.
+  auto compute_row = [&](int r, const RowIdx &Rr) {
+    float acc = 0.f;
+    if (PIPE) {
+      Item ia, ib;
+      gather(Rr, 0, ia);
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        sched_fence();
+        if (j + 1 < CPL) gather(Rr, j + 1, (j & 1) ? ia : ib);
+        sched_fence();
+        const float d = dot(j, (j & 1) ? ib : ia);
+        const float f = h2f(Rr.SC[j]) * fm[j];
+        acc = j == 0 ? f * d : fmaf(f, d, acc);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        Item it;
+        gather(Rr, j, it);
+        const float d = dot(j, it);
+        const float f = h2f(Rr.SC[j]) * fm[j];
+        acc = j == 0 ? f * d : fmaf(f, d, acc);
+      }
+    }
+    const float tot = wave_sum(acc);
+    if (lane == 0) a.y[row0 + r * stride] = tot;
+  };
+
+  // Ring of D+1 row buffers: row r+D's index loads are issued before row r is
+  // computed, so D rows of HBM loads stay in flight per wave.
+  int r = 0;
+  for (; r + (D + 1) <= nrows; r += D + 1) {
+#pragma unroll
+    for (int k = 0; k <= D; ++k) {
+      load_row(r + k + D, R[(k + D) % (D + 1)]);
+      sched_fence();
+      compute_row(r + k, R[k]);
+    }
   }
-#undef VQ_BATCH
-#undef VQ_ROW
-#undef VQ_LOAD_BATCH
+#pragma unroll
+  for (int k = 0; k < D; ++k)
+    if (r + k < nrows) compute_row(r + k, R[k]);
 }
 
 // ---------------------------------------------------------------------------
@@ -324,41 +417,36 @@ static GemvArgs make_args(const WView &w) {
   return a;
 }
 
-// x lives in registers: up to 8 chunks per lane as fp16 (K <= 16384), up to
-// 4 as fp32 (K <= 8192).
+// x is staged in LDS; the fast path needs the codebooks and x of a whole row
+// in one workgroup's LDS, up to 8 chunks per lane (K <= 16384) for bf16 x and
+// 4 for fp32 x (held in registers).
 bool gemv_fast_eligible(const WView &w, int xt) {
   if (w.bits == 16) return false;
-  if ((size_t)(w.S << w.bits) * 16 > 131072) return false;
   if (w.k % 32 || w.bs % 32) return false;
   const int cpl = (w.G / 4 + 63) / 64;
-  return cpl <= (xt == VQ_BF16 ? 8 : 4);
+  if (cpl > (xt == VQ_BF16 ? 8 : 4)) return false;
+  return gemv_lds_bytes(w.S, w.bits, cpl, xt == VQ_BF16) <= kLdsBytes;
 }
 
-template <int S, int BITS, int CPL, int W, int RB, bool XF16>
-static void launch_fast_w(const GemvArgs &a, int nwg, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemv_lds<S, BITS, CPL, W, XF16, RB>), dim3(nwg), dim3(W * 64), 0, s, a);
+template <int S, int BITS, int CPL, int W, int D, bool XF16, bool XREG, bool PIPE>
+static void launch_fast_w(const GemvArgs &a, int cus, hipStream_t s) {
+  const int g = (a.n + W - 1) / W;
+  hipLaunchKernelGGL((k_gemv_lds<S, BITS, CPL, W, XF16, D, XREG, PIPE>), dim3(g < cus ? g : cus), dim3(W * 64), 0,
+                     s, a);
 }
 
-// Persistent grid of one workgroup per CU slot (two when the codebooks take
-// <= 80 KiB of LDS).  Waves per workgroup and rows in flight per wave (RB) are
-// chosen so that the x slice, two batches of row indices and the gathers fit
-// in the registers a wave gets: 16 waves -> 128 VGPRs, 8 -> 256, 4 -> 512.
+// Persistent grid of one workgroup per CU (the codebooks and x take most of
+// the LDS).  Waves per workgroup, the prefetch depth D (rows of index loads
+// in flight per wave) and in-row gather pipelining trade registers: 16 waves
+// get 128 VGPRs each, 8 get 256.  Rows of 1-2 chunks per lane: 16 waves, x in
+// registers; 3-4 chunks: 8 waves, two rows in flight, pipelined gathers;
+// longer rows: 8 waves, x read from LDS per chunk.
 template <int S, int BITS, int CPL, bool XF16>
 static void launch_fast_c(const GemvArgs &a, int cus, hipStream_t s) {
-  constexpr size_t lds = (size_t)(S << BITS) * 16;
-  const int slots = cus * (lds > 81920 ? 1 : 2);
-  constexpr int xload = CPL * (XF16 ? 1 : 2) * (S > 2 ? 2 : 1);
-  auto grid = [&](int w) { const int g = (a.n + w - 1) / w; return g < slots ? g : slots; };
-  auto rows_per_wave = [&](int w) { const int g = grid(w); return (a.n + g * w - 1) / (g * w); };
-  if constexpr (xload <= 2) {
-    if (rows_per_wave(16) <= 1) launch_fast_w<S, BITS, CPL, 16, 1, XF16>(a, grid(16), s);
-    else launch_fast_w<S, BITS, CPL, 8, 4, XF16>(a, grid(8), s);
-  } else if constexpr (xload <= 4) {
-    if (rows_per_wave(8) <= 1) launch_fast_w<S, BITS, CPL, 8, 1, XF16>(a, grid(8), s);
-    else launch_fast_w<S, BITS, CPL, 8, 2, XF16>(a, grid(8), s);
-  } else {
-    if (rows_per_wave(4) <= 1) launch_fast_w<S, BITS, CPL, 4, 1, XF16>(a, grid(4), s);
-    else launch_fast_w<S, BITS, CPL, 4, 2, XF16>(a, grid(4), s);
+  if constexpr (gemv_lds_bytes(S, BITS, CPL, XF16) <= kLdsBytes) {
+    if constexpr (CPL <= 2) launch_fast_w<S, BITS, CPL, 16, 1, XF16, true, false>(a, cus, s);
+    else if constexpr (CPL <= 4 || !XF16) launch_fast_w<S, BITS, CPL, 8, 2, XF16, true, true>(a, cus, s);
+    else launch_fast_w<S, BITS, CPL, 8, 1, XF16, false, true>(a, cus, s);
   }
 }
 

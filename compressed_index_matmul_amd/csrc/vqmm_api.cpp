@@ -9,9 +9,6 @@
 
 namespace vqmm {
 
-// Launchers that live in other translation units.
-hipError_t launch_gemv_token(const WView &w, const void *x, int xt, float *y, hipStream_t s);
-
 namespace {
 
 constexpr int kMaxDevices = 64;

@@ -32,7 +32,8 @@ int device_cu_count();
 hipError_t launch_unpack_dequant(const WView &w, uint16_t *idx_out, uint16_t *w_out, hipStream_t s);
 hipError_t launch_rht(const void *x, int xt, int batch, int n, const int8_t *signs, int max_block,
                       float *out, hipStream_t s);
-hipError_t launch_gemv(const WView &w, const void *x, int xt, int batch, float *y, hipStream_t s);
+// One token of x (fp32 or bf16, VQ_F32 / VQ_BF16) against W: y[n].
+hipError_t launch_gemv_token(const WView &w, const void *x, int xt, float *y, hipStream_t s);
 hipError_t launch_gemm(const WView &w, const uint16_t *x, int m, float *y, hipStream_t s);
 
 }  // namespace vqmm
