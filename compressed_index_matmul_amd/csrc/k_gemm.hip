@@ -34,6 +34,7 @@ struct GemmArgs {
   int m, n, k, G, S, nblk, bs;
   int gshift;  // log2(scale_block / 8) when a power of two, else -1
   int tiles_m, tiles_n, per_xcd;
+  uint64_t smagic;  // ceil(2^32 / (scale_block / 32)): K step -> scale block by a multiply
 };
 
 // Scale block of group g (8 columns): g / (scale_block / 8).
@@ -201,6 +202,53 @@ __device__ __forceinline__ void gemm_load_step(const GemmArgs &a, int ks, int dg
   }
 }
 
+// Buffer descriptors and per-lane offsets of the aligned large-M kernel
+// (K % 32 == 0, scale_block % 32 == 0): every load of a K step is a scalar
+// descriptor plus a constant lane offset plus a wave-uniform step offset.
+template <int S>
+struct BufSet {
+  buf_t lo[S], hi[S], sc, x;
+  uint32_t vlo, vhi, vsc, va[2];
+};
+
+template <int S, int BITS>
+__device__ __forceinline__ void gemm_bufs(const GemmArgs &a, int wrow_c, int dg, const LaneOffsets &o, BufSet<S> &B) {
+  const uint32_t ng = (uint32_t)a.n * a.G;
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    B.lo[t] = BITS == 16 ? make_buf(a.i16[t], 2 * ng) : make_buf(a.lo[t], ng);
+    B.hi[t] = make_buf(BITS == 12 ? a.hi[t] : a.lo[t], BITS == 12 ? (ng + 1) / 2 : ng);
+  }
+  B.sc = make_buf(a.sc, 2u * a.n * a.nblk);
+  B.x = make_buf(a.x, 2u * a.m * a.k);
+  const uint32_t f = (uint32_t)wrow_c * a.G + dg;
+  B.vlo = (BITS == 16 ? 2 : 1) * f;
+  B.vhi = f >> 1;  // f is even: G % 4 == 0 and dg is 0 or 2
+  B.vsc = 2u * wrow_c * a.nblk;
+  B.va[0] = o.a[0];
+  B.va[1] = o.a[1];
+}
+
+template <int S, int BITS>
+__device__ __forceinline__ void gemm_load_step_buf(const GemmArgs &a, const BufSet<S> &B, int ks, StepRegs<S> &R) {
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    if (BITS == 16) {
+      R.lo[t] = buf_u32(B.lo[t], B.vlo, 8u * ks);
+    } else {
+      R.lo[t] = buf_u16(B.lo[t], B.vlo, 4u * ks);
+      if (BITS == 12) R.hi[t] = buf_u8(B.hi[t], B.vhi, 2u * ks);
+    }
+  }
+  const uint32_t blk = (uint32_t)(((uint64_t)ks * a.smagic) >> 32);  // (32 ks) / scale_block
+  R.sc[0] = buf_u16(B.sc, B.vsc, 2u * blk);
+  R.sc[1] = R.sc[0];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) R.av[kk][i] = buf_u128(B.x, B.va[i], 64u * ks + 32u * kk);
+}
+
 // Decode the thread's two groups of step ks into the LDS W tile.
 template <int S, int BITS, bool CB_LDS, bool ALIGNED>
 __device__ __forceinline__ void gemm_decode_store(const GemmArgs &a, const uint4 *s_cb, const StepRegs<S> &R,
@@ -227,11 +275,13 @@ __device__ __forceinline__ void gemm_decode_store(const GemmArgs &a, const uint4
 
 // Tile 256 x 128, K step 32, 4 waves stacked along M, each owning 64 token
 // rows x all 128 W columns as 2 x 4 accumulator blocks of
-// v_mfma_f32_32x32x16_bf16 (x fragments are never loaded twice).  Per K step every thread decodes two
-// groups (LDS codebook gathers, fp32 stage sum and scale, bf16) into one of
-// two LDS W tiles, a barrier publishes it, and the waves multiply it with
-// their x fragments.  Global loads (indices, scales, x fragments) run three
-// steps ahead in a ring of four register sets.
+// v_mfma_f32_32x32x16_bf16 (x fragments are never loaded twice).  Every
+// thread decodes two groups per K step (LDS codebook gathers, fp32 stage sum
+// and scale, bf16) into one of two LDS W tiles.  Software pipeline, one
+// barrier per step: iteration k reads the B fragments of tile k, issues the
+// codebook gathers of step k+1, then interleaves the 16 MFMAs of step k with
+// the decode of step k+1 into the other tile.  Global loads (indices,
+// scales, x fragments) run four steps ahead in a ring of four register sets.
 template <int S, int BITS, bool CB_LDS, bool ALIGNED>
 __global__ __launch_bounds__(256) void k_gemm_large(GemmArgs a) {
   __shared__ uint4 s_cb[CB_LDS ? (S << BITS) : 1];
@@ -281,61 +331,103 @@ __global__ __launch_bounds__(256) void k_gemm_large(GemmArgs a) {
 
   const int nks = (a.G + 3) / 4;
   StepRegs<S> R0, R1, R2, R3;
+  BufSet<S> B;
+  if (ALIGNED) gemm_bufs<S, BITS>(a, wrow_c, dg, o, B);
   // Unconditional prefetch (past the last step it reloads the last step):
   // with no branch around the loads the wait counts stay exact.
   auto load = [&](int ks, StepRegs<S> &R) {
-    gemm_load_step<S, BITS, ALIGNED>(a, ks < nks ? ks : nks - 1, dg, o, R);
-    sched_fence();  // keep the prefetch here, three steps ahead of its use
+    if (ALIGNED) gemm_load_step_buf<S, BITS>(a, B, ks < nks ? ks : nks - 1, R);
+    else gemm_load_step<S, BITS, ALIGNED>(a, ks < nks ? ks : nks - 1, dg, o, R);
   };
-  auto mma = [&](const StepRegs<S> &R, const uint16_t *wt) {
+  // codebook gathers of the thread's two groups of a step
+  auto gather = [&](const StepRegs<S> &R, uint4 (&v)[2][S]) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8_t bfr[4];
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int t = 0; t < S; ++t) {
+        uint32_t idx;
+        if (!ALIGNED || BITS == 16) idx = (R.lo[t] >> (16 * u)) & 0xffffu;
+        else {
+          idx = (R.lo[t] >> (8 * u)) & 0xffu;
+          if (BITS == 12) idx |= ((R.hi[t] >> (4 * u)) & 0xfu) << 8;
+        }
+        v[u][t] = CB_LDS ? s_cb[(t << BITS) + idx] : reinterpret_cast<const uint4 *>(a.cb[t])[idx];
+      }
+  };
+  // decode group u of step ks (gathered vectors v) and store it in tile wt
+  // (aligned path: W rows past n only feed output columns that are never
+  // stored, so they are decoded from the clamped row and not zeroed)
+  auto decode = [&](int ks, int u, const StepRegs<S> &R, const uint4 (&v)[S], uint16_t *wt) {
+    uint4 pk = group_to_bf16<S>(v, h2f(R.sc[ALIGNED ? 0 : u]));
+    const int g = ks * 4 + dg + u;
+    if (!ALIGNED && (!wok || g >= a.G)) pk = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4 *>(&wt[drow * kWP + 8 * (dg + u)]) = pk;
+  };
+  auto mma4 = [&](const StepRegs<S> &R, const bf16x8_t (&bfr)[2][4], int kk, int i) {
+    const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, R.av[kk][i]);
+#pragma unroll
+    for (int jn = 0; jn < 4; ++jn)
+      acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[kk][jn], acc[i][jn], 0, 0, 0);
+  };
+  // Iteration ks: MFMAs of step ks (A fragments in Rm, B fragments from tile
+  // ks & 1) with the decode of step ks+1 (indices in Rd) into the other
+  // tile, then the loads of step ks+4 into Rm, then the barrier.  The tile
+  // written here was last read in iteration ks-1, before its barrier.
+  auto iter = [&](int ks, StepRegs<S> &Rm, const StepRegs<S> &Rd) {
+    const uint16_t *wr = s_w[ks & 1];
+    uint16_t *ww = s_w[(ks + 1) & 1];
+    bf16x8_t bfr[2][4];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int jn = 0; jn < 4; ++jn)
-        bfr[jn] = *reinterpret_cast<const bf16x8_t *>(&wt[(32 * jn + (lane & 31)) * kWP + 16 * kk + 8 * (lane >> 5)]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, R.av[kk][i]);
-#pragma unroll
-        for (int jn = 0; jn < 4; ++jn)
-          acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[jn], acc[i][jn], 0, 0, 0);
-      }
-    }
-  };
-  // one K step: decode into W buffer (ks & 1), barrier, multiply.  The
-  // barrier of step ks also orders the reads of buffer (ks & 1) at step ks-2
-  // before its rewrite here.
-  auto step = [&](int ks, const StepRegs<S> &R) {
-    uint16_t *wt = s_w[ks & 1];
-    gemm_decode_store<S, BITS, CB_LDS, ALIGNED>(a, s_cb, R, ks, dg, wok, wt, drow);
+        bfr[kk][jn] = *reinterpret_cast<const bf16x8_t *>(&wr[(32 * jn + (lane & 31)) * kWP + 16 * kk + 8 * (lane >> 5)]);
+    uint4 v[2][S];
+    gather(Rd, v);
+    sched_fence();
+    mma4(Rm, bfr, 0, 0);
+    sched_fence();
+    decode(ks + 1, 0, Rd, v[0], ww);
+    sched_fence();
+    mma4(Rm, bfr, 0, 1);
+    sched_fence();
+    decode(ks + 1, 1, Rd, v[1], ww);
+    sched_fence();
+    mma4(Rm, bfr, 1, 0);
+    sched_fence();
+    mma4(Rm, bfr, 1, 1);
+    sched_fence();
+    load(ks + 4, Rm);
     __syncthreads();
-    mma(R, wt);
   };
 
   load(0, R0);
   load(1, R1);
   load(2, R2);
+  load(3, R3);
   wait_all_memory();  // codebook (LDS-direct) has landed (and the first steps)
   __syncthreads();
-  // main loop: four steps per iteration, a single exit (a loop with several
+  {
+    uint4 v[2][S];
+    gather(R0, v);
+    decode(0, 0, R0, v[0], s_w[0]);
+    decode(0, 1, R0, v[1], s_w[0]);
+  }
+  __syncthreads();
+  // main loop: four iterations per trip, a single exit (a loop with several
   // exits made the compiler move the accumulators between register files)
   int ks = 0;
   for (; ks + 4 <= nks; ks += 4) {
-    load(ks + 3, R3);
-    step(ks, R0);
-    load(ks + 4, R0);
-    step(ks + 1, R1);
-    load(ks + 5, R1);
-    step(ks + 2, R2);
-    load(ks + 6, R2);
-    step(ks + 3, R3);
+    iter(ks, R0, R1);
+    iter(ks + 1, R1, R2);
+    iter(ks + 2, R2, R3);
+    iter(ks + 3, R3, R0);
   }
   // remainder: sets R0, R1, R2 hold steps ks, ks+1, ks+2
   const int rem = nks - ks;
-  if (rem > 0) step(ks, R0);
-  if (rem > 1) step(ks + 1, R1);
-  if (rem > 2) step(ks + 2, R2);
+  if (rem > 0) iter(ks, R0, R1);
+  if (rem > 1) iter(ks + 1, R1, R2);
+  if (rem > 2) iter(ks + 2, R2, R3);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -344,6 +436,202 @@ __global__ __launch_bounds__(256) void k_gemm_large(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + wave * 64 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < a.m && col < a.n) a.y[(size_t)row * a.n + col] = acc[i][jn][r];
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// large M, K % 256 == 0
+// ---------------------------------------------------------------------------
+// Index planes of one thread's W row for 4 K steps (16 groups): 16 low bytes
+// and, for 12-bit indices, 16 high nibbles per stage.
+template <int S>
+struct Quad {
+  uint4 lo[S];
+  uint2 hi[S];
+};
+
+// x fragments (4 blocks of 16 tokens) and the thread's scale for one K step.
+struct XStep {
+  uint4 av[4];
+  uint32_t sc;
+};
+
+// Tile 256 (tokens) x 128 (W rows), K step 32, 4 waves stacked along the
+// tokens, each owning 64 x 128 as 4 x 8 blocks of v_mfma_f32_16x16x32_bf16
+// (lane l of an A fragment holds 8 consecutive k of token l % 16, so each x
+// load reads 64 contiguous bytes per token).  Every load is a buffer load:
+// the index planes of 4 K steps at once (16 B + 8 B per stage and thread),
+// x fragments and the scale per step.  Software pipeline as k_gemm_large:
+// iteration k reads the B fragments of LDS tile k & 1, issues the codebook
+// gathers of step k+1, interleaves the 32 MFMAs of step k with the decode of
+// step k+1 into the other tile, loads step k+4, then one barrier.
+template <int S, int BITS>
+__global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
+  __shared__ uint4 s_cb[S << BITS];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[2][kLN * kWP];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int L = (blockIdx.x % 8) * a.per_xcd + blockIdx.x / 8;
+  if (L >= a.tiles_m * a.tiles_n) return;  // whole workgroup, before any barrier
+  const int m0 = (L / a.tiles_n) * kLM;
+  const int n0 = (L % a.tiles_n) * kLN;
+  {
+    constexpr int CBN = S << BITS;
+#pragma unroll 4
+    for (int r = 0; r < CBN / 256; ++r) {
+      const int blk = (r * 4 + wave) * 64;
+      lds_direct_16(reinterpret_cast<const uint4 *>(a.cb[blk >> BITS]) + (blk & ((1 << BITS) - 1)) + lane,
+                    s_cb + blk);
+    }
+  }
+  const int drow = tid >> 1;     // W-tile row decoded by this thread
+  const int dg = 2 * (tid & 1);  // first of its two groups in a K step
+  // W rows past n are decoded from the last row: they only feed output
+  // columns past n, which are never stored
+  const int wrow_c = min(n0 + drow, a.n - 1);
+  const uint32_t ng = (uint32_t)a.n * a.G;
+  buf_t blo[S], bhi[S];
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    blo[t] = make_buf(a.lo[t], ng);
+    bhi[t] = make_buf(BITS == 12 ? a.hi[t] : a.lo[t], BITS == 12 ? (ng + 1) / 2 : ng);
+  }
+  const buf_t bsc = make_buf(a.sc, 2u * a.n * a.nblk);
+  const buf_t bx = make_buf(a.x, 2u * a.m * a.k);
+  const uint32_t vlo = (uint32_t)wrow_c * a.G;  // + 16 per quad
+  const uint32_t vhi = vlo >> 1;                // + 8 per quad (G is even)
+  const uint32_t vsc = 2u * wrow_c * a.nblk;
+  // x byte offsets of this lane's token (one per 16-token block) and k chunk;
+  // tokens past m load token m-1 and feed rows that are never stored
+  uint32_t va[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = min(m0 + wave * 64 + 16 * i + (lane & 15), a.m - 1);
+    va[i] = 2u * ((uint32_t)r * a.k + 8 * (lane >> 4));
+  }
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nks = a.G / 4;  // K steps (a multiple of 8)
+  const int nq = a.G / 16;  // quads
+  // Unconditional loads (past the end they reload the last step or quad):
+  // no branch around a load, so the wait counts stay exact.
+  auto load_quad = [&](int j, Quad<S> &Q) {
+    j = min(j, nq - 1);
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+      Q.lo[t] = buf_u128(blo[t], vlo, 16u * j);
+      if (BITS == 12) Q.hi[t] = buf_u64(bhi[t], vhi, 8u * j);
+    }
+  };
+  auto load_x = [&](int ks, XStep &X) {
+    ks = min(ks, nks - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) X.av[i] = buf_u128(bx, va[i], 64u * ks);
+    const uint32_t blk = (uint32_t)(((uint64_t)ks * a.smagic) >> 32);  // (32 ks) / scale_block
+    X.sc = buf_u16(bsc, vsc, 2u * blk);
+  };
+  // index of group u (0, 1) of the thread's pair in step s (0..3) of a quad
+  auto idx_of = [&](const Quad<S> &Q, int s, int u, int t) -> uint32_t {
+    const uint32_t lw = s == 0 ? Q.lo[t].x : s == 1 ? Q.lo[t].y : s == 2 ? Q.lo[t].z : Q.lo[t].w;
+    uint32_t idx = (lw >> (8 * (dg + u))) & 0xffu;
+    if (BITS == 12) {
+      const uint32_t hw = s < 2 ? Q.hi[t].x : Q.hi[t].y;  // nibbles of groups 8 (s / 2) .. + 7
+      idx |= ((hw >> (4 * (4 * (s & 1) + dg + u))) & 0xfu) << 8;
+    }
+    return idx;
+  };
+  auto gather = [&](const Quad<S> &Q, int s, uint4 (&v)[2][S]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int t = 0; t < S; ++t) v[u][t] = s_cb[(t << BITS) + idx_of(Q, s, u, t)];
+  };
+  auto decode = [&](int u, const uint4 (&v)[S], uint32_t sc, uint16_t *wt) {
+    const uint4 pk = group_to_bf16<S>(v, h2f(sc));
+    *reinterpret_cast<uint4 *>(&wt[drow * kWP + 8 * (dg + u)]) = pk;
+  };
+  auto mma8 = [&](const XStep &X, const bf16x8_t (&bfr)[8], int i) {
+    const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, X.av[i]);
+#pragma unroll
+    for (int jn = 0; jn < 8; ++jn)
+      acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[jn], acc[i][jn], 0, 0, 0);
+  };
+  // Iteration ks: MFMAs of step ks (Xm, tile ks & 1), decode of step ks+1
+  // (quad Qd, step sd within it, scale in Xd) into the other tile, loads of
+  // step ks+4 into Xm (and, when ks % 4 == 3, of quad (ks+5)/4 into Qn),
+  // barrier.  The tile written here was last read in iteration ks-1.
+  auto iter = [&](int ks, XStep &Xm, const XStep &Xd, const Quad<S> &Qd, int sd, Quad<S> &Qn, bool quad_load) {
+    const uint16_t *wr = s_w[ks & 1];
+    uint16_t *ww = s_w[(ks + 1) & 1];
+    bf16x8_t bfr[8];
+#pragma unroll
+    for (int jn = 0; jn < 8; ++jn)
+      bfr[jn] = *reinterpret_cast<const bf16x8_t *>(&wr[(16 * jn + (lane & 15)) * kWP + 8 * (lane >> 4)]);
+    uint4 v[2][S];
+    gather(Qd, sd, v);
+    sched_fence();
+    mma8(Xm, bfr, 0);
+    sched_fence();
+    decode(0, v[0], Xd.sc, ww);
+    sched_fence();
+    mma8(Xm, bfr, 1);
+    sched_fence();
+    decode(1, v[1], Xd.sc, ww);
+    sched_fence();
+    mma8(Xm, bfr, 2);
+    sched_fence();
+    if (quad_load) load_quad((ks + 5) / 4, Qn);
+    sched_fence();
+    mma8(Xm, bfr, 3);
+    sched_fence();
+    load_x(ks + 4, Xm);
+    __syncthreads();
+  };
+
+  Quad<S> Q0, Q1;
+  XStep X0, X1, X2, X3;
+  load_quad(0, Q0);
+  load_quad(1, Q1);
+  load_x(0, X0);
+  load_x(1, X1);
+  load_x(2, X2);
+  load_x(3, X3);
+  wait_all_memory();  // codebook (LDS-direct) has landed (and the first steps)
+  __syncthreads();
+  {
+    uint4 v[2][S];
+    gather(Q0, 0, v);
+    decode(0, v[0], X0.sc, s_w[0]);
+    decode(1, v[1], X0.sc, s_w[0]);
+  }
+  __syncthreads();
+  // eight steps (two quads) per trip; quads alternate between Q0 and Q1
+  for (int ks = 0; ks < nks; ks += 8) {
+    iter(ks + 0, X0, X1, Q0, 1, Q0, false);
+    iter(ks + 1, X1, X2, Q0, 2, Q0, false);
+    iter(ks + 2, X2, X3, Q0, 3, Q0, false);
+    iter(ks + 3, X3, X0, Q1, 0, Q0, true);   // quad (ks+8)/4 -> Q0
+    iter(ks + 4, X0, X1, Q1, 1, Q1, false);
+    iter(ks + 5, X1, X2, Q1, 2, Q1, false);
+    iter(ks + 6, X2, X3, Q1, 3, Q1, false);
+    iter(ks + 7, X3, X0, Q0, 0, Q1, true);   // quad (ks+12)/4 -> Q1
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jn = 0; jn < 8; ++jn) {
+      const int col = n0 + 16 * jn + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wave * 64 + 16 * i + 4 * (lane >> 4) + r;
         if (row < a.m && col < a.n) a.y[(size_t)row * a.n + col] = acc[i][jn][r];
       }
     }
@@ -573,6 +861,8 @@ static GemmArgs make_gemm_args(const WView &w, const uint16_t *x, int m, float *
   a.bs = w.bs;
   const int gb = w.bs / 8;
   a.gshift = (gb & (gb - 1)) == 0 ? __builtin_ctz((unsigned)gb) : -1;
+  const uint64_t spb = w.bs % 32 == 0 ? (uint64_t)(w.bs / 32) : 1;
+  a.smagic = ((uint64_t(1) << 32) + spb - 1) / spb;
   return a;
 }
 
@@ -592,7 +882,17 @@ static void launch_gemm_sb(const GemmArgs &a0, hipStream_t s) {
     a.tiles_n = (a.n + kLN - 1) / kLN;
     const int total = a.tiles_m * a.tiles_n;
     a.per_xcd = (total + 7) / 8;
-    if (a.k % 32 == 0)
+    // buffer paths: K % 32 == 0 and scale blocks of whole K steps (the
+    // scale-block multiply is exact for K < 2^20); the 16x16 tile kernel
+    // also needs K % 256 == 0 and LDS codebooks of 8/12-bit indices
+    const bool buf_ok = a.k % 32 == 0 && a.bs % 32 == 0 && a.k < (1 << 20);
+    if constexpr (CB_LDS && BITS != 16) {
+      if (buf_ok && a.k % 256 == 0) {
+        hipLaunchKernelGGL((k_gemm_tile<S, BITS>), dim3(8 * a.per_xcd), dim3(256), 0, s, a);
+        return;
+      }
+    }
+    if (buf_ok)
       hipLaunchKernelGGL((k_gemm_large<S, BITS, CB_LDS, true>), dim3(8 * a.per_xcd), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL((k_gemm_large<S, BITS, CB_LDS, false>), dim3(8 * a.per_xcd), dim3(256), 0, s, a);

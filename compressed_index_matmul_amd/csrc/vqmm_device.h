@@ -103,6 +103,71 @@ __device__ __forceinline__ void wait_all_memory() {
 #endif
 }
 
+// Raw buffer resources (CDNA buffer descriptors): a loaded element is the
+// base address plus a 32-bit per-lane offset plus a wave-uniform offset kept
+// in a scalar register, so a load needs no per-lane 64-bit address math.
+// The builtins exist only for the GPU target; the host pass sees stubs.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t buf_t;
+#else
+typedef const void *buf_t;
+#endif
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Descriptor for `bytes` bytes at p (raw, no stride; dword 3 = 0x00020000,
+// the plain 32-bit data format used for raw buffers on gfx9).
+__device__ __forceinline__ buf_t make_buf(const void *p, uint32_t bytes) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+#else
+  (void)bytes;
+  return p;
+#endif
+}
+__device__ __forceinline__ uint32_t buf_u8(buf_t r, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+#else
+  (void)r, (void)voff, (void)soff;
+  return 0;
+#endif
+}
+__device__ __forceinline__ uint32_t buf_u16(buf_t r, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+#else
+  (void)r, (void)voff, (void)soff;
+  return 0;
+#endif
+}
+__device__ __forceinline__ uint32_t buf_u32(buf_t r, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+#else
+  (void)r, (void)voff, (void)soff;
+  return 0;
+#endif
+}
+__device__ __forceinline__ uint2 buf_u64(buf_t r, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return make_uint2(v.x, v.y);
+#else
+  (void)r, (void)voff, (void)soff;
+  return make_uint2(0, 0);
+#endif
+}
+__device__ __forceinline__ uint4 buf_u128(buf_t r, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  (void)r, (void)voff, (void)soff;
+  return make_uint4(0, 0, 0, 0);
+#endif
+}
+
 // Index of flat group f of stage planes (any width).
 __device__ __forceinline__ uint32_t load_index(int bits, const uint8_t *lo, const uint8_t *hi,
                                                const uint16_t *i16, size_t f) {

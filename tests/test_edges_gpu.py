@@ -155,6 +155,22 @@ def test_gemm_ragged(vq, m, n, k, st, bits):
     assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"gemm {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("m,n,k,st,bits,bs", [(257, 131, 512, 2, 12, 128), (40, 64, 768, 2, 8, 768),
+                                             (18, 300, 256, 1, 12, 64), (600, 70, 1024, 2, 12, 1024),
+                                             (300, 129, 2048, 2, 12, 32)])
+def test_gemm_tile_ragged(vq, m, n, k, st, bits, bs):
+    """Shapes of the large-M buffer-load kernel (K % 256 == 0): ragged token
+    and W-row tiles, several scale-block sizes (one per K step up to one per
+    row), 8- and 12-bit indices."""
+    import torch
+    sw = vqsynth.random_weight(n, k, st, bits, bs, seed=m * 3 + n + k + bs)
+    xs, x64 = _x(m, k, "bf16", m * 11 + n)
+    y = vq.vq_gemm(device_weight(sw), x_to_device(xs, "bf16"))
+    torch.cuda.synchronize()
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
+    assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"gemm {m}x{n}x{k} bs {bs}")
+
+
 def test_gemv_one_hot_columns(vq):
     """x = e_k through the fp32-decode path recovers dequantized columns to
     fp32 rounding (the oracle's one-hot pin, on the GPU)."""
