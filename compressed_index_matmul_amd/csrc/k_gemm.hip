@@ -463,14 +463,17 @@ struct XStep {
 // (lane l of an A fragment holds 8 consecutive k of token l % 16, so each x
 // load reads 64 contiguous bytes per token).  Every load is a buffer load:
 // the index planes of 4 K steps at once (16 B + 8 B per stage and thread),
-// x fragments and the scale per step.  Software pipeline as k_gemm_large:
-// iteration k reads the B fragments of LDS tile k & 1, issues the codebook
-// gathers of step k+1, interleaves the 32 MFMAs of step k with the decode of
-// step k+1 into the other tile, loads step k+4, then one barrier.
+// x fragments and the scale per step.  Software pipeline over a ring of three
+// LDS W tiles, one barrier per step: iteration k issues the codebook gathers
+// of step k+2 and the B-fragment reads of step k+1 (published by the previous
+// barrier), interleaves the 32 MFMAs of step k (B fragments read one
+// iteration earlier) with the decode of step k+2, loads step k+4, then the
+// barrier.  The tile written in iteration k holds step k-1, whose fragments
+// were read in iteration k-2.
 template <int S, int BITS>
 __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
   __shared__ uint4 s_cb[S << BITS];
-  __shared__ __attribute__((aligned(16))) uint16_t s_w[2][kLN * kWP];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[3][kLN * kWP];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -558,40 +561,43 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
     const uint4 pk = group_to_bf16<S>(v, h2f(sc));
     *reinterpret_cast<uint4 *>(&wt[drow * kWP + 8 * (dg + u)]) = pk;
   };
+  auto read_b = [&](const uint16_t *wr, bf16x8_t (&bfr)[8]) {
+#pragma unroll
+    for (int jn = 0; jn < 8; ++jn)
+      bfr[jn] = *reinterpret_cast<const bf16x8_t *>(&wr[(16 * jn + (lane & 15)) * kWP + 8 * (lane >> 4)]);
+  };
   auto mma8 = [&](const XStep &X, const bf16x8_t (&bfr)[8], int i) {
     const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, X.av[i]);
 #pragma unroll
     for (int jn = 0; jn < 8; ++jn)
       acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[jn], acc[i][jn], 0, 0, 0);
   };
-  // Iteration ks: MFMAs of step ks (Xm, tile ks & 1), decode of step ks+1
-  // (quad Qd, step sd within it, scale in Xd) into the other tile, loads of
-  // step ks+4 into Xm (and, when ks % 4 == 3, of quad (ks+5)/4 into Qn),
-  // barrier.  The tile written here was last read in iteration ks-1.
-  auto iter = [&](int ks, XStep &Xm, const XStep &Xd, const Quad<S> &Qd, int sd, Quad<S> &Qn, bool quad_load) {
-    const uint16_t *wr = s_w[ks & 1];
-    uint16_t *ww = s_w[(ks + 1) & 1];
-    bf16x8_t bfr[8];
-#pragma unroll
-    for (int jn = 0; jn < 8; ++jn)
-      bfr[jn] = *reinterpret_cast<const bf16x8_t *>(&wr[(16 * jn + (lane & 15)) * kWP + 8 * (lane >> 4)]);
+  // Iteration ks: B fragments of step ks+1 into Bn (tile (ks+1) % 3), MFMAs
+  // of step ks (Xm, Bc), decode of step ks+2 (quad Qd, step sd, scale in Xd)
+  // into tile (ks+2) % 3, loads of step ks+4 into Xm (and, when ks % 4 == 2,
+  // of quad (ks+6)/4 into Qn), barrier.
+  auto iter = [&](int ks, XStep &Xm, const XStep &Xd, const bf16x8_t (&Bc)[8], bf16x8_t (&Bn)[8],
+                  const Quad<S> &Qd, int sd, Quad<S> &Qn, bool quad_load) {
+    uint16_t *ww = s_w[(ks + 2) % 3];
     uint4 v[2][S];
     gather(Qd, sd, v);
+    read_b(s_w[(ks + 1) % 3], Bn);
     sched_fence();
-    mma8(Xm, bfr, 0);
-    sched_fence();
+    // 32 MFMAs with the decode's vector work between them: one MFMA, then
+    // two VALU instructions, so the matrix core and the VALU run together
+    mma8(Xm, Bc, 0);
     decode(0, v[0], Xd.sc, ww);
-    sched_fence();
-    mma8(Xm, bfr, 1);
-    sched_fence();
+    mma8(Xm, Bc, 1);
     decode(1, v[1], Xd.sc, ww);
+    mma8(Xm, Bc, 2);
+    mma8(Xm, Bc, 3);
+#pragma unroll
+    for (int g = 0; g < 32; ++g) {
+      sched_group<0x008, 1>();
+      sched_group<0x002, 2>();
+    }
     sched_fence();
-    mma8(Xm, bfr, 2);
-    sched_fence();
-    if (quad_load) load_quad((ks + 5) / 4, Qn);
-    sched_fence();
-    mma8(Xm, bfr, 3);
-    sched_fence();
+    if (quad_load) load_quad((ks + 6) / 4, Qn);
     load_x(ks + 4, Xm);
     __syncthreads();
   };
@@ -611,18 +617,25 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
     gather(Q0, 0, v);
     decode(0, v[0], X0.sc, s_w[0]);
     decode(1, v[1], X0.sc, s_w[0]);
+    gather(Q0, 1, v);
+    decode(0, v[0], X1.sc, s_w[1]);
+    decode(1, v[1], X1.sc, s_w[1]);
   }
   __syncthreads();
-  // eight steps (two quads) per trip; quads alternate between Q0 and Q1
+  bf16x8_t B0[8], B1[8];
+  read_b(s_w[0], B0);
+  // eight steps (two quads) per trip; the three W tiles rotate with ks % 3
+  // (compile-time inside the trip only when 3 divides the trip length, so the
+  // tile index is computed at run time); quads alternate between Q0 and Q1
   for (int ks = 0; ks < nks; ks += 8) {
-    iter(ks + 0, X0, X1, Q0, 1, Q0, false);
-    iter(ks + 1, X1, X2, Q0, 2, Q0, false);
-    iter(ks + 2, X2, X3, Q0, 3, Q0, false);
-    iter(ks + 3, X3, X0, Q1, 0, Q0, true);   // quad (ks+8)/4 -> Q0
-    iter(ks + 4, X0, X1, Q1, 1, Q1, false);
-    iter(ks + 5, X1, X2, Q1, 2, Q1, false);
-    iter(ks + 6, X2, X3, Q1, 3, Q1, false);
-    iter(ks + 7, X3, X0, Q0, 0, Q1, true);   // quad (ks+12)/4 -> Q1
+    iter(ks + 0, X0, X2, B0, B1, Q0, 2, Q1, false);
+    iter(ks + 1, X1, X3, B1, B0, Q0, 3, Q1, false);
+    iter(ks + 2, X2, X0, B0, B1, Q1, 0, Q0, true);   // quad (ks+8)/4 -> Q0
+    iter(ks + 3, X3, X1, B1, B0, Q1, 1, Q0, false);
+    iter(ks + 4, X0, X2, B0, B1, Q1, 2, Q0, false);
+    iter(ks + 5, X1, X3, B1, B0, Q1, 3, Q0, false);
+    iter(ks + 6, X2, X0, B0, B1, Q0, 0, Q1, true);   // quad (ks+12)/4 -> Q1
+    iter(ks + 7, X3, X1, B1, B0, Q0, 1, Q1, false);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -792,6 +805,172 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_small(GemmArgs a) {
   }
 }
 
+// 1 <= m <= 16, K % 128 == 0, scale_block % 32 == 0, LDS codebooks.
+// A unit is 32 W rows (two blocks of 16) over a K range; lane l decodes, per
+// 32-column K step, group l / 16 of row l % 16 of each block straight into a
+// B fragment of v_mfma_f32_16x16x32_bf16, and loads 8 x values of token l % 16
+// (the A fragment, shared by both blocks).  A workgroup's eight waves take
+// its units times KP K parts (KP = 8 / units per workgroup); the KP partial
+// tiles of a unit are added in LDS in a fixed order at the end.  Index planes
+// come four K steps at a time (16 + 8 bytes per stage and block), x and the
+// scales two steps ahead, all as buffer loads.
+constexpr int kFewBlocks = 2;  // 16-row blocks per unit
+
+template <int S>
+struct FewQuad {
+  uint4 lo[kFewBlocks][S];
+  uint2 hi[kFewBlocks][S];
+};
+struct FewStep {
+  uint4 av;                // A fragment
+  uint32_t sc[kFewBlocks];  // scale of the lane's row in each block
+};
+
+template <int S, int BITS>
+__global__ __launch_bounds__(kSWaves * 64) void k_gemm_few(GemmArgs a, int units_per_wg, int kp) {
+  __shared__ uint4 s_cb[S << BITS];
+  __shared__ float s_red[kSWaves][kFewBlocks][16][17];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  {
+    constexpr int CBN = S << BITS;
+#pragma unroll 4
+    for (int r = 0; r < (CBN + kSWaves * 64 - 1) / (kSWaves * 64); ++r) {
+      const int blk = (r * kSWaves + wave) * 64;
+      if (blk < CBN)
+        lds_direct_16(reinterpret_cast<const uint4 *>(a.cb[blk >> BITS]) + (blk & ((1 << BITS) - 1)) + lane,
+                      s_cb + blk);
+    }
+  }
+  const int units = (a.n + 16 * kFewBlocks - 1) / (16 * kFewBlocks);
+  const int nks = a.G / 4;
+  const int steps = nks / kp;        // K steps per part (a multiple of 4)
+  const int ui = wave / kp;          // unit slot of this wave in the workgroup
+  const int part = wave % kp;
+  const int unit = blockIdx.x * units_per_wg + ui;
+  const bool active = ui < units_per_wg && unit < units;  // wave-uniform
+  const int r16 = lane & 15;
+  const int q = lane >> 4;           // k chunk of the lane within a K step
+  const int tok = min(r16, a.m - 1); // tokens past m only feed unstored outputs
+  const int ks0 = part * steps;
+
+  const uint32_t ng = (uint32_t)a.n * a.G;
+  buf_t blo[S], bhi[S];
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    blo[t] = make_buf(a.lo[t], ng);
+    bhi[t] = make_buf(BITS == 12 ? a.hi[t] : a.lo[t], BITS == 12 ? (ng + 1) / 2 : ng);
+  }
+  const buf_t bsc = make_buf(a.sc, 2u * a.n * a.nblk);
+  const buf_t bx = make_buf(a.x, 2u * a.m * a.k);
+  uint32_t vlo[kFewBlocks], vsc[kFewBlocks];
+#pragma unroll
+  for (int b = 0; b < kFewBlocks; ++b) {
+    const int row = min((active ? unit : 0) * 16 * kFewBlocks + 16 * b + r16, a.n - 1);
+    vlo[b] = (uint32_t)row * a.G;
+    vsc[b] = 2u * row * a.nblk;
+  }
+  const uint32_t vx = 2u * ((uint32_t)tok * a.k + 8 * q);
+
+  f32x4 acc[kFewBlocks];
+#pragma unroll
+  for (int b = 0; b < kFewBlocks; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // loads of step / quad index i of this part, clamped to its last one
+  auto load_quad = [&](int j, FewQuad<S> &Q) {
+    j = ks0 / 4 + min(j, steps / 4 - 1);
+#pragma unroll
+    for (int b = 0; b < kFewBlocks; ++b)
+#pragma unroll
+      for (int t = 0; t < S; ++t) {
+        Q.lo[b][t] = buf_u128(blo[t], vlo[b], 16u * j);
+        if (BITS == 12) Q.hi[b][t] = buf_u64(bhi[t], vlo[b] >> 1, 8u * j);
+      }
+  };
+  auto load_step = [&](int i, FewStep &X) {
+    const int ks = ks0 + min(i, steps - 1);
+    X.av = buf_u128(bx, vx, 64u * ks);
+    const uint32_t blk = (uint32_t)(((uint64_t)ks * a.smagic) >> 32);  // (32 ks) / scale_block
+#pragma unroll
+    for (int b = 0; b < kFewBlocks; ++b) X.sc[b] = buf_u16(bsc, vsc[b], 2u * blk);
+  };
+  // decode the lane's group of block b in step s (0..3) of quad Q, multiply
+  auto step = [&](const FewQuad<S> &Q, int s, const FewStep &X) {
+    uint4 v[kFewBlocks][S];
+#pragma unroll
+    for (int b = 0; b < kFewBlocks; ++b)
+#pragma unroll
+      for (int t = 0; t < S; ++t) {
+        const uint4 lw4 = Q.lo[b][t];
+        const uint32_t lw = s == 0 ? lw4.x : s == 1 ? lw4.y : s == 2 ? lw4.z : lw4.w;
+        uint32_t idx = (lw >> (8 * q)) & 0xffu;
+        if (BITS == 12) {
+          const uint32_t hw = s < 2 ? Q.hi[b][t].x : Q.hi[b][t].y;
+          idx |= ((hw >> (4 * (4 * (s & 1) + q))) & 0xfu) << 8;
+        }
+        v[b][t] = s_cb[(t << BITS) + idx];
+      }
+    const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, X.av);
+#pragma unroll
+    for (int b = 0; b < kFewBlocks; ++b) {
+      const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, group_to_bf16<S>(v[b], h2f(X.sc[b])));
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr, acc[b], 0, 0, 0);
+    }
+  };
+
+  FewQuad<S> Q0, Q1;
+  FewStep X0, X1, X2, X3;
+  load_quad(0, Q0);
+  load_quad(1, Q1);
+  load_step(0, X0);
+  load_step(1, X1);
+  load_step(2, X2);
+  wait_all_memory();  // codebook (LDS-direct) has landed
+  __syncthreads();
+  if (active) {  // wave-uniform; every wave reaches the barriers below
+    // eight steps per trip (two quads); steps ahead: 3 (x, scales), 4-8 (quads)
+    for (int i = 0; i < steps; i += 8) {
+      load_step(i + 3, X3);
+      step(Q0, 0, X0);
+      load_step(i + 4, X0);
+      step(Q0, 1, X1);
+      load_step(i + 5, X1);
+      step(Q0, 2, X2);
+      load_step(i + 6, X2);
+      step(Q0, 3, X3);
+      load_quad(i / 4 + 2, Q0);
+      load_step(i + 7, X3);
+      step(Q1, 0, X0);
+      load_step(i + 8, X0);
+      step(Q1, 1, X1);
+      load_step(i + 9, X1);
+      step(Q1, 2, X2);
+      load_step(i + 10, X2);
+      step(Q1, 3, X3);
+      load_quad(i / 4 + 3, Q1);
+    }
+  }
+  // lane holds D[token 4 (lane / 16) + r][row lane % 16] of each block
+#pragma unroll
+  for (int b = 0; b < kFewBlocks; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_red[wave][b][4 * (lane >> 4) + r][lane & 15] = acc[b][r];
+  __syncthreads();
+  if (active && part == 0) {
+#pragma unroll
+    for (int b = 0; b < kFewBlocks; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ti = 4 * (lane >> 4) + r;
+        float sum = 0.f;
+        for (int h = 0; h < kp; ++h) sum += s_red[wave + h][b][ti][lane & 15];
+        const int col = unit * 16 * kFewBlocks + 16 * b + (lane & 15);
+        if (ti < a.m && col < a.n) a.y[(size_t)ti * a.n + col] = sum;
+      }
+  }
+}
+
 // General small-M path (any K % 8 == 0, any scale block): one group per lane
 // per 32-column K step, byte-wise index loads.
 template <int S, int BITS, bool CB_LDS>
@@ -873,6 +1052,24 @@ static void launch_gemm_sb(const GemmArgs &a0, hipStream_t s) {
     const int nslabs = (a.n + 15) / 16;
     int nwg = device_cu_count();
     if (nwg > nslabs) nwg = nslabs;
+    if constexpr (CB_LDS && BITS != 16) {
+      // the unit kernel: K in whole quads per part (K % 256 == 0 keeps at
+      // least two quads per part for the eight-step trips)
+      if (a.k % 256 == 0 && a.bs % 32 == 0 && a.k < (1 << 20)) {
+        const int units = (a.n + 16 * kFewBlocks - 1) / (16 * kFewBlocks);
+        const int cus = device_cu_count();
+        // with fewer units than CUs the slab kernel below spreads better
+        const int grid = units < cus ? 0 : cus;
+        const int upw = grid > 0 ? (units + grid - 1) / grid : 1;
+        const int nks = a.k / 32;
+        int kp = 1;
+        while (kp * 2 * upw <= kSWaves && nks % (kp * 2 * 8) == 0) kp *= 2;
+        if (grid > 0 && upw * kp <= kSWaves) {
+          hipLaunchKernelGGL((k_gemm_few<S, BITS>), dim3(grid), dim3(kSWaves * 64), 0, s, a, upw, kp);
+          return;
+        }
+      }
+    }
     if (a.k % 128 == 0 && a.bs % 32 == 0)
       hipLaunchKernelGGL((k_gemm_small<S, BITS, CB_LDS>), dim3(nwg), dim3(kSWaves * 64), 0, s, a);
     else

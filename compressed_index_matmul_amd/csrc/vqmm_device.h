@@ -96,6 +96,16 @@ __device__ __forceinline__ void sched_fence() {
 #endif
 }
 
+// Scheduling-group hint: the next `n` instructions of the region that match
+// `mask` (0x002 VALU, 0x008 MFMA, 0x100 LDS read, 0x200 LDS write, 0x020
+// global read) form one group, groups in program order of these calls.
+template <int MASK, int N>
+__device__ __forceinline__ void sched_group() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
+#endif
+}
+
 // Wait for every outstanding memory operation of the wave.
 __device__ __forceinline__ void wait_all_memory() {
 #if defined(__HIP_DEVICE_COMPILE__)

@@ -171,6 +171,21 @@ def test_gemm_tile_ragged(vq, m, n, k, st, bits, bs):
     assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"gemm {m}x{n}x{k} bs {bs}")
 
 
+@pytest.mark.parametrize("m,n,k,st,bits,bs", [(5, 8200, 512, 2, 12, 128), (16, 8192, 1024, 1, 8, 1024),
+                                             (1, 9000, 256, 2, 12, 32), (11, 12000, 768, 2, 12, 64)])
+def test_gemm_few_tokens_wide(vq, m, n, k, st, bits, bs):
+    """Few tokens against wide weights (at least one 32-row unit per CU): the
+    unit kernel with its K split across waves and the fixed-order partial
+    sums, ragged W rows, 1-16 tokens, several scale blocks."""
+    import torch
+    sw = vqsynth.random_weight(n, k, st, bits, bs, seed=m * 5 + n + k)
+    xs, x64 = _x(m, k, "bf16", m * 13 + n)
+    y = vq.vq_gemm(device_weight(sw), x_to_device(xs, "bf16"))
+    torch.cuda.synchronize()
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
+    assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"gemm {m}x{n}x{k} bs {bs}")
+
+
 def test_gemv_one_hot_columns(vq):
     """x = e_k through the fp32-decode path recovers dequantized columns to
     fp32 rounding (the oracle's one-hot pin, on the GPU)."""
