@@ -651,6 +651,209 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// large M, wide N (N >= 8192), K % 256 == 0
+// ---------------------------------------------------------------------------
+constexpr int kWN = 256;  // W rows per tile of the wide kernel
+
+// MFMA with the accumulator tied to its registers (the compiler then keeps
+// every accumulator in place across the unrolled K loop instead of moving it
+// between register sets).  Accumulators are reused 64 MFMAs later at the
+// soonest; mfma_drain() separates the last MFMAs from the epilogue reads.
+__device__ __forceinline__ void mfma_tied(f32x4 &acc, const bf16x8_t &a, const bf16x8_t &b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+#else
+  (void)acc, (void)a, (void)b;
+#endif
+}
+
+// Tile 256 (tokens) x 256 (W rows), K step 32, 4 waves stacked along the
+// tokens, each owning 64 x 256 as 4 x 16 blocks of v_mfma_f32_16x16x32_bf16:
+// twice the W rows of k_gemm_tile per x fragment, so half the x traffic per
+// MFMA.  Thread t decodes W row t (all four groups of a K step) into an LDS
+// tile of 64-byte rows whose four 16-byte chunks are XOR-swizzled by row
+// (conflict-free fragment reads without padding: two tiles and the
+// codebooks fill the 160 KiB).  Pipeline: iteration k reads the B fragments
+// of tile k & 1 in two halves, issues the gathers of step k+1, interleaves
+// the 64 MFMAs of step k with the decode of step k+1 into the other tile,
+// loads step k+4, one barrier.
+template <int S, int BITS>
+__global__ __launch_bounds__(256) void k_gemm_wide(GemmArgs a) {
+  __shared__ uint4 s_cb[S << BITS];
+  __shared__ __attribute__((aligned(16))) uint4 s_w[2][kWN * 4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int L = (blockIdx.x % 8) * a.per_xcd + blockIdx.x / 8;
+  if (L >= a.tiles_m * a.tiles_n) return;  // whole workgroup, before any barrier
+  const int m0 = (L / a.tiles_n) * kLM;
+  const int n0 = (L % a.tiles_n) * kWN;
+  {
+    constexpr int CBN = S << BITS;
+#pragma unroll 4
+    for (int r = 0; r < CBN / 256; ++r) {
+      const int blk = (r * 4 + wave) * 64;
+      lds_direct_16(reinterpret_cast<const uint4 *>(a.cb[blk >> BITS]) + (blk & ((1 << BITS) - 1)) + lane,
+                    s_cb + blk);
+    }
+  }
+  // W row of this thread (rows past n decode the last row: they only feed
+  // output columns past n, which are never stored)
+  const int wrow_c = min(n0 + tid, a.n - 1);
+  const uint32_t ng = (uint32_t)a.n * a.G;
+  buf_t blo[S], bhi[S];
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    blo[t] = make_buf(a.lo[t], ng);
+    bhi[t] = make_buf(BITS == 12 ? a.hi[t] : a.lo[t], BITS == 12 ? (ng + 1) / 2 : ng);
+  }
+  const buf_t bsc = make_buf(a.sc, 2u * a.n * a.nblk);
+  const buf_t bx = make_buf(a.x, 2u * a.m * a.k);
+  const uint32_t vlo = (uint32_t)wrow_c * a.G;
+  const uint32_t vhi = vlo >> 1;
+  const uint32_t vsc = 2u * wrow_c * a.nblk;
+  uint32_t va[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = min(m0 + wave * 64 + 16 * i + (lane & 15), a.m - 1);
+    va[i] = 2u * ((uint32_t)r * a.k + 8 * (lane >> 4));
+  }
+  // swizzled chunk position of chunk c of tile row r
+  auto wpos = [](int r, int c) { return 4 * r + (c ^ ((r >> 2) & 3)); };
+
+  f32x4 acc[4][16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nks = a.G / 4;
+  const int nq = a.G / 16;
+  auto load_quad = [&](int j, Quad<S> &Q) {
+    j = min(j, nq - 1);
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+      Q.lo[t] = buf_u128(blo[t], vlo, 16u * j);
+      if (BITS == 12) Q.hi[t] = buf_u64(bhi[t], vhi, 8u * j);
+    }
+  };
+  auto load_x = [&](int ks, XStep &X) {
+    ks = min(ks, nks - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) X.av[i] = buf_u128(bx, va[i], 64u * ks);
+    const uint32_t blk = (uint32_t)(((uint64_t)ks * a.smagic) >> 32);
+    X.sc = buf_u16(bsc, vsc, 2u * blk);
+  };
+  // the four groups of the thread's row in step s of quad Q
+  auto gather = [&](const Quad<S> &Q, int s, uint4 (&v)[4][S]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int t = 0; t < S; ++t) {
+        const uint32_t lw = s == 0 ? Q.lo[t].x : s == 1 ? Q.lo[t].y : s == 2 ? Q.lo[t].z : Q.lo[t].w;
+        uint32_t idx = (lw >> (8 * g)) & 0xffu;
+        if (BITS == 12) {
+          const uint32_t hw = s < 2 ? Q.hi[t].x : Q.hi[t].y;
+          idx |= ((hw >> (4 * (4 * (s & 1) + g))) & 0xfu) << 8;
+        }
+        v[g][t] = s_cb[(t << BITS) + idx];
+      }
+  };
+  auto decode = [&](int g, const uint4 (&v)[S], uint32_t sc, uint4 *wt) {
+    wt[wpos(tid, g)] = group_to_bf16<S>(v, h2f(sc));
+  };
+  auto read_b = [&](const uint4 *wr, int half, bf16x8_t (&bfr)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      bfr[j] = __builtin_bit_cast(bf16x8_t, wr[wpos(16 * (8 * half + j) + (lane & 15), lane >> 4)]);
+  };
+  auto mma = [&](const XStep &X, const bf16x8_t (&bfr)[8], int half, int i) {
+    const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, X.av[i]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mfma_tied(acc[i][8 * half + j], afr, bfr[j]);
+  };
+  auto iter = [&](int ks, XStep &Xm, const XStep &Xd, const Quad<S> &Qd, int sd, Quad<S> &Qn, bool quad_load) {
+    const uint4 *wr = s_w[ks & 1];
+    uint4 *ww = s_w[(ks + 1) & 1];
+    bf16x8_t bfr[8];
+    uint4 v[4][S];
+    read_b(wr, 0, bfr);
+    gather(Qd, sd, v);
+    sched_fence();
+    mma(Xm, bfr, 0, 0);
+    decode(0, v[0], Xd.sc, ww);
+    mma(Xm, bfr, 0, 1);
+    decode(1, v[1], Xd.sc, ww);
+    mma(Xm, bfr, 0, 2);
+    mma(Xm, bfr, 0, 3);
+    sched_fence();
+    read_b(wr, 1, bfr);
+    sched_fence();
+    mma(Xm, bfr, 1, 0);
+    decode(2, v[2], Xd.sc, ww);
+    mma(Xm, bfr, 1, 1);
+    decode(3, v[3], Xd.sc, ww);
+    mma(Xm, bfr, 1, 2);
+    mma(Xm, bfr, 1, 3);
+    sched_fence();
+    if (quad_load) load_quad((ks + 5) / 4, Qn);
+    load_x(ks + 4, Xm);
+    __syncthreads();
+  };
+
+  Quad<S> Q0, Q1;
+  XStep X0, X1, X2, X3;
+  load_quad(0, Q0);
+  load_quad(1, Q1);
+  load_x(0, X0);
+  load_x(1, X1);
+  load_x(2, X2);
+  load_x(3, X3);
+  wait_all_memory();  // codebook (LDS-direct) has landed (and the first steps)
+  __syncthreads();
+  {
+    uint4 v[4][S];
+    gather(Q0, 0, v);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) decode(g, v[g], X0.sc, s_w[0]);
+  }
+  __syncthreads();
+  for (int ks = 0; ks < nks; ks += 8) {
+    iter(ks + 0, X0, X1, Q0, 1, Q0, false);
+    iter(ks + 1, X1, X2, Q0, 2, Q0, false);
+    iter(ks + 2, X2, X3, Q0, 3, Q0, false);
+    iter(ks + 3, X3, X0, Q1, 0, Q0, true);   // quad (ks+8)/4 -> Q0
+    iter(ks + 4, X0, X1, Q1, 1, Q1, false);
+    iter(ks + 5, X1, X2, Q1, 2, Q1, false);
+    iter(ks + 6, X2, X3, Q1, 3, Q1, false);
+    iter(ks + 7, X3, X0, Q0, 0, Q1, true);   // quad (ks+12)/4 -> Q1
+  }
+  // the last MFMAs have written their accumulators before they are read
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
+                   "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+    asm volatile("s_nop 0"
+                 : "+a"(acc[i][8]), "+a"(acc[i][9]), "+a"(acc[i][10]), "+a"(acc[i][11]), "+a"(acc[i][12]),
+                   "+a"(acc[i][13]), "+a"(acc[i][14]), "+a"(acc[i][15]));
+  }
+#endif
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jn = 0; jn < 16; ++jn) {
+      const int col = n0 + 16 * jn + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wave * 64 + 16 * i + 4 * (lane >> 4) + r;
+        if (row < a.m && col < a.n) a.y[(size_t)row * a.n + col] = acc[i][jn][r];
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // small M
 // ---------------------------------------------------------------------------
 constexpr int kSWaves = 8;
@@ -1083,6 +1286,17 @@ static void launch_gemm_sb(const GemmArgs &a0, hipStream_t s) {
     // scale-block multiply is exact for K < 2^20); the 16x16 tile kernel
     // also needs K % 256 == 0 and LDS codebooks of 8/12-bit indices
     const bool buf_ok = a.k % 32 == 0 && a.bs % 32 == 0 && a.k < (1 << 20);
+    if constexpr (CB_LDS && BITS != 16 && (S << BITS) * 16 + 2 * kWN * 64 <= 163840) {
+      // wide N: 256 x 256 tiles once there is at least one per CU
+      const int wide_tiles = a.tiles_m * ((a.n + kWN - 1) / kWN);
+      if (buf_ok && a.k % 256 == 0 && wide_tiles >= device_cu_count()) {
+        GemmArgs w = a;
+        w.tiles_n = (a.n + kWN - 1) / kWN;
+        w.per_xcd = (w.tiles_m * w.tiles_n + 7) / 8;
+        hipLaunchKernelGGL((k_gemm_wide<S, BITS>), dim3(8 * w.per_xcd), dim3(256), 0, s, w);
+        return;
+      }
+    }
     if constexpr (CB_LDS && BITS != 16) {
       if (buf_ok && a.k % 256 == 0) {
         hipLaunchKernelGGL((k_gemm_tile<S, BITS>), dim3(8 * a.per_xcd), dim3(256), 0, s, a);

@@ -157,7 +157,8 @@ def test_gemm_ragged(vq, m, n, k, st, bits):
 
 @pytest.mark.parametrize("m,n,k,st,bits,bs", [(257, 131, 512, 2, 12, 128), (40, 64, 768, 2, 8, 768),
                                              (18, 300, 256, 1, 12, 64), (600, 70, 1024, 2, 12, 1024),
-                                             (300, 129, 2048, 2, 12, 32)])
+                                             (300, 129, 2048, 2, 12, 32), (1300, 11000, 256, 2, 12, 128),
+                                             (1100, 15000, 512, 1, 8, 64)])
 def test_gemm_tile_ragged(vq, m, n, k, st, bits, bs):
     """Shapes of the large-M buffer-load kernel (K % 256 == 0): ragged token
     and W-row tiles, several scale-block sizes (one per K step up to one per
