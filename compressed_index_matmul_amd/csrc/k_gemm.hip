@@ -772,33 +772,40 @@ __global__ __launch_bounds__(256) void k_gemm_wide(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) mfma_tied(acc[i][8 * half + j], afr, bfr[j]);
   };
-  auto iter = [&](int ks, XStep &Xm, const XStep &Xd, const Quad<S> &Qd, int sd, Quad<S> &Qn, bool quad_load) {
+  // Iteration ks, two phases around one barrier.  A: the MFMAs of the first
+  // half of step ks (fragments in BA) overlap the gathers and decode of step
+  // ks+1 into tile (ks+1) & 1 and the reads of the second half of step ks
+  // (tile ks & 1) into BB.  Barrier: tile ks+1 is complete, and every read of
+  // tile ks & 1 has finished (it is rewritten in iteration ks+1).  B: the
+  // MFMAs of the second half (BB) overlap the reads of the first half of step
+  // ks+1 into BA; then the loads of step ks+4.
+  auto iter = [&](int ks, XStep &Xm, const XStep &Xd, const Quad<S> &Qd, int sd, Quad<S> &Qn, bool quad_load,
+                  bf16x8_t (&BA)[8], bf16x8_t (&BB)[8]) {
     const uint4 *wr = s_w[ks & 1];
     uint4 *ww = s_w[(ks + 1) & 1];
-    bf16x8_t bfr[8];
     uint4 v[4][S];
-    read_b(wr, 0, bfr);
     gather(Qd, sd, v);
+    read_b(wr, 1, BB);
     sched_fence();
-    mma(Xm, bfr, 0, 0);
+    mma(Xm, BA, 0, 0);
     decode(0, v[0], Xd.sc, ww);
-    mma(Xm, bfr, 0, 1);
+    mma(Xm, BA, 0, 1);
     decode(1, v[1], Xd.sc, ww);
-    mma(Xm, bfr, 0, 2);
-    mma(Xm, bfr, 0, 3);
-    sched_fence();
-    read_b(wr, 1, bfr);
-    sched_fence();
-    mma(Xm, bfr, 1, 0);
+    mma(Xm, BA, 0, 2);
     decode(2, v[2], Xd.sc, ww);
-    mma(Xm, bfr, 1, 1);
+    mma(Xm, BA, 0, 3);
     decode(3, v[3], Xd.sc, ww);
-    mma(Xm, bfr, 1, 2);
-    mma(Xm, bfr, 1, 3);
+    sched_fence();
+    __syncthreads();
+    read_b(ww, 0, BA);
+    sched_fence();
+    mma(Xm, BB, 1, 0);
+    mma(Xm, BB, 1, 1);
+    mma(Xm, BB, 1, 2);
+    mma(Xm, BB, 1, 3);
     sched_fence();
     if (quad_load) load_quad((ks + 5) / 4, Qn);
     load_x(ks + 4, Xm);
-    __syncthreads();
   };
 
   Quad<S> Q0, Q1;
@@ -818,15 +825,17 @@ __global__ __launch_bounds__(256) void k_gemm_wide(GemmArgs a) {
     for (int g = 0; g < 4; ++g) decode(g, v[g], X0.sc, s_w[0]);
   }
   __syncthreads();
+  bf16x8_t BA[8], BB[8];
+  read_b(s_w[0], 0, BA);
   for (int ks = 0; ks < nks; ks += 8) {
-    iter(ks + 0, X0, X1, Q0, 1, Q0, false);
-    iter(ks + 1, X1, X2, Q0, 2, Q0, false);
-    iter(ks + 2, X2, X3, Q0, 3, Q0, false);
-    iter(ks + 3, X3, X0, Q1, 0, Q0, true);   // quad (ks+8)/4 -> Q0
-    iter(ks + 4, X0, X1, Q1, 1, Q1, false);
-    iter(ks + 5, X1, X2, Q1, 2, Q1, false);
-    iter(ks + 6, X2, X3, Q1, 3, Q1, false);
-    iter(ks + 7, X3, X0, Q0, 0, Q1, true);   // quad (ks+12)/4 -> Q1
+    iter(ks + 0, X0, X1, Q0, 1, Q0, false, BA, BB);
+    iter(ks + 1, X1, X2, Q0, 2, Q0, false, BA, BB);
+    iter(ks + 2, X2, X3, Q0, 3, Q0, false, BA, BB);
+    iter(ks + 3, X3, X0, Q1, 0, Q0, true, BA, BB);   // quad (ks+8)/4 -> Q0
+    iter(ks + 4, X0, X1, Q1, 1, Q1, false, BA, BB);
+    iter(ks + 5, X1, X2, Q1, 2, Q1, false, BA, BB);
+    iter(ks + 6, X2, X3, Q1, 3, Q1, false, BA, BB);
+    iter(ks + 7, X3, X0, Q0, 0, Q1, true, BA, BB);   // quad (ks+12)/4 -> Q1
   }
   // the last MFMAs have written their accumulators before they are read
 #if defined(__HIP_DEVICE_COMPILE__)
