@@ -51,6 +51,92 @@ __device__ __forceinline__ void rht_block(const RhtArgs &a, int b, int &off, int
   len = 0;  // unreachable for b < nblocks
 }
 
+// Blocks of nb = r * kRhtThreads elements (r = 8, 16 or 32, at most RM) with
+// every block of every row 16-byte aligned in x, signs and out: each thread
+// loads its r contiguous inputs and signs with vector loads, runs log2(r)
+// stages in registers, and the remaining stages run two at a time (radix 4)
+// through LDS.  r is uniform over the workgroup.
+template <int RM, bool BF16>
+__global__ __launch_bounds__(kRhtThreads) void k_rht_vec(RhtArgs a) {
+  __shared__ float buf[kRhtMaxBlock];
+  const int blk = blockIdx.x % a.nblocks;
+  const int row = blockIdx.x / a.nblocks;
+  int off, nb;
+  rht_block(a, blk, off, nb);
+  const int r = nb / kRhtThreads;  // 8, 16 or 32 (the launcher checks)
+  const int tid = threadIdx.x;
+  const int64_t base = (int64_t)row * a.n + off;
+  const int i0 = tid * r;
+  float v[RM];
+#pragma unroll
+  for (int c = 0; c < RM / 8; ++c) {
+    if (8 * c < r) {  // workgroup-uniform
+      const uint2 su = *reinterpret_cast<const uint2 *>(a.signs + off + i0 + 8 * c);
+      float xs[8];
+      if (BF16) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.x) + base + i0 + 8 * c);
+        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xs[2 * e] = bf2f(w4[e] & 0xffffu);
+          xs[2 * e + 1] = bf2f(w4[e] >> 16);
+        }
+      } else {
+        const float4 *px = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.x) + base + i0 + 8 * c);
+        const float4 u0 = px[0], u1 = px[1];
+        xs[0] = u0.x; xs[1] = u0.y; xs[2] = u0.z; xs[3] = u0.w;
+        xs[4] = u1.x; xs[5] = u1.y; xs[6] = u1.z; xs[7] = u1.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[8 * c + e] = xs[e] * (float)(int8_t)((e < 4 ? su.x : su.y) >> (8 * (e & 3)));
+    }
+  }
+#pragma unroll
+  for (int h = 1; h < RM; h <<= 1)
+    if (h < r) {
+#pragma unroll
+      for (int q = 0; q < RM; ++q)
+        if ((q & h) == 0 && q + h < RM) {
+          const float p = v[q], m = v[q + h];
+          v[q] = p + m;
+          v[q + h] = p - m;
+        }
+    }
+#pragma unroll
+  for (int q = 0; q < RM; ++q)
+    if (q < r) buf[i0 + q] = v[q];
+  // stages h = r, 2r, ...: two per pass on groups {i, i+h, i+2h, i+3h}
+  int h = r;
+  for (; 4 * h <= nb; h *= 4) {
+    __syncthreads();
+    for (int p = tid; p < nb / 4; p += kRhtThreads) {
+      const int i = (p / h) * 4 * h + (p % h);
+      const float x0 = buf[i], x1 = buf[i + h], x2 = buf[i + 2 * h], x3 = buf[i + 3 * h];
+      const float s0 = x0 + x1, d0 = x0 - x1, s1 = x2 + x3, d1 = x2 - x3;
+      buf[i] = s0 + s1;
+      buf[i + h] = d0 + d1;
+      buf[i + 2 * h] = s0 - s1;
+      buf[i + 3 * h] = d0 - d1;
+    }
+  }
+  if (h < nb) {  // one stage left
+    __syncthreads();
+    for (int p = tid; p < nb / 2; p += kRhtThreads) {
+      const int i = (p / h) * 2 * h + (p % h);
+      const float x0 = buf[i], x1 = buf[i + h];
+      buf[i] = x0 + x1;
+      buf[i + h] = x0 - x1;
+    }
+  }
+  __syncthreads();
+  const float sc = (float)(1.0 / __builtin_sqrt((double)nb));
+  float4 *po = reinterpret_cast<float4 *>(a.out + base);
+  for (int i = tid; i < nb / 4; i += kRhtThreads) {
+    const float4 u = reinterpret_cast<const float4 *>(buf)[i];
+    po[i] = make_float4(u.x * sc, u.y * sc, u.z * sc, u.w * sc);
+  }
+}
+
 template <int R>
 __global__ __launch_bounds__(kRhtThreads) void k_rht(RhtArgs a) {
   __shared__ float buf[kRhtMaxBlock];
@@ -125,6 +211,25 @@ hipError_t launch_rht(const void *x, int xt, int batch, int n, const int8_t *sig
   // Elements per thread for the register stages: the largest block spread
   // over the workgroup (at least 1, at most 32 for a 16384 block).
   int r = maxlen / kRhtThreads;
+  // vector path: every block is at least 8 * 512 elements long (so every
+  // block offset is a multiple of 4096), and x, signs, out and the row pitch
+  // keep 16-byte alignment
+  const int xb = xt == VQ_F32 ? 4 : 2;
+  const bool big_blocks = (a.nfull == 0 || max_block >= 8 * kRhtThreads) && a.rest % (8 * kRhtThreads) == 0;
+  const bool aligned = ((uintptr_t)x % 16 == 0) && ((uintptr_t)signs % 16 == 0) && ((uintptr_t)out % 16 == 0) &&
+                       ((int64_t)n * xb % 16 == 0);
+  if (big_blocks && aligned && r >= 8) {
+    if (xt == VQ_BF16) {
+      if (r <= 8) hipLaunchKernelGGL((k_rht_vec<8, true>), grid, dim3(kRhtThreads), 0, s, a);
+      else if (r <= 16) hipLaunchKernelGGL((k_rht_vec<16, true>), grid, dim3(kRhtThreads), 0, s, a);
+      else hipLaunchKernelGGL((k_rht_vec<32, true>), grid, dim3(kRhtThreads), 0, s, a);
+    } else {
+      if (r <= 8) hipLaunchKernelGGL((k_rht_vec<8, false>), grid, dim3(kRhtThreads), 0, s, a);
+      else if (r <= 16) hipLaunchKernelGGL((k_rht_vec<16, false>), grid, dim3(kRhtThreads), 0, s, a);
+      else hipLaunchKernelGGL((k_rht_vec<32, false>), grid, dim3(kRhtThreads), 0, s, a);
+    }
+    return hipGetLastError();
+  }
   if (r <= 1)
     hipLaunchKernelGGL(k_rht<1>, grid, dim3(kRhtThreads), 0, s, a);
   else if (r == 2)
