@@ -95,7 +95,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
     uint32_t SC[CPL];
   };
   auto load_row = [&](int r, RowIdx &R) {
-    const int rr = min(row0 + r * stride, last);  // past the end: a valid duplicate, never stored
+    // past the wave's last row: that row again (an L2 hit, never stored)
+    const int rr = min(row0 + min(r, nrows - 1) * stride, last);
     const size_t rb = (size_t)rr * a.G;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
