@@ -125,8 +125,8 @@ int vq_unpack_dequant(const vq_weight *w, uint16_t *idx_out, uint16_t *w_out, vo
  *   batch : 1..16
  *   y     : float [batch][n_out]
  * One token, or fp32 tokens: exact fp16 codebook products accumulated in fp32
- * (bf16 x is held in fp16 after a per-lane power-of-two rescale, exact for
- * every value within 2^28 of the largest |x| the lane holds), so every output
+ * (bf16 x is held in fp16 after a power-of-two rescale per 32 columns, exact
+ * for every value within 2^28 of the largest |x| of its 32), so every output
  * satisfies |y - y_exact| <= 2e-3 * sum_k |w x| + 1e-6.
  * 2..16 bf16 tokens: run on bf16 matrix cores as vq_gemm does, with the same
  * error behaviour.
