@@ -68,7 +68,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
   __shared__ float s_f[XF16 ? CMAX : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: row math stays scalar
   // Each workgroup owns a contiguous block of rows (equal sizes up to one
   // row); its waves take every WAVES-th row of the block.
   const int per_wg = (a.n + gridDim.x - 1) / gridDim.x;
@@ -79,14 +79,31 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
   const int last = a.n - 1;
   const int nrows = row0 < blk_hi ? (blk_hi - 1 - row0) / stride + 1 : 0;  // rows of this wave (uniform)
 
+  // This lane's chunks and their byte offsets within a row of each plane
+  // (low bytes: 4 per chunk; high nibbles: 2 per chunk; scales: the chunk's
+  // scale block).  Chunks past the end of the row reuse the last chunk.
   int cc[CPL];
   bool ok[CPL];
+  uint32_t vlo[CPL], vsc[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int c = lane + 64 * j;
     ok[j] = c < a.C;
     cc[j] = ok[j] ? c : a.C - 1;
+    vlo[j] = 4u * cc[j];
+    vsc[j] = 2u * (uint32_t)((32 * cc[j]) / a.bs);
   }
+  // Buffer descriptors: a load is descriptor + lane offset + a wave-uniform
+  // row offset held in a scalar register, so no per-lane 64-bit address
+  // arithmetic.  Every plane is below 2^31 bytes (n_out * k_in < 2^31).
+  const uint32_t plane = (uint32_t)a.n * (uint32_t)a.G;
+  buf_t blo[S], bhi[S];
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    blo[t] = make_buf(a.lo[t], plane);
+    bhi[t] = make_buf(BITS == 12 ? a.hi[t] : a.lo[t], (plane + 1) / 2);
+  }
+  const buf_t bsc = make_buf(a.sc, 2u * (uint32_t)a.n * (uint32_t)a.nblk);
 
   // Index planes and scales of one row (this lane's chunks).
   struct RowIdx {
@@ -96,43 +113,27 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
   };
   auto load_row = [&](int r, RowIdx &R) {
     // past the wave's last row: that row again (an L2 hit, never stored)
-    const int rr = min(row0 + min(r, nrows - 1) * stride, last);
-    const size_t rb = (size_t)rr * a.G;
+    const uint32_t rr = (uint32_t)min(row0 + min(r, nrows - 1) * stride, last);
+    const uint32_t rb = rr * (uint32_t)a.G;  // G is a multiple of 4 here
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
 #pragma unroll
       for (int t = 0; t < S; ++t) {
-        R.L[j][t] = *reinterpret_cast<const uint32_t *>(a.lo[t] + rb + 4 * cc[j]);
-        if (BITS == 12) R.H[j][t] = *reinterpret_cast<const uint16_t *>(a.hi[t] + (rb >> 1) + 2 * cc[j]);
+        R.L[j][t] = buf_u32(blo[t], vlo[j], rb);
+        if (BITS == 12) R.H[j][t] = buf_u16(bhi[t], vlo[j] >> 1, rb >> 1);
       }
-      R.SC[j] = a.sc[(size_t)rr * a.nblk + (32 * cc[j]) / a.bs];
+      R.SC[j] = buf_u16(bsc, vsc[j], 2u * rr * (uint32_t)a.nblk);
     }
   };
 
-  // Global loads are issued in the order their latency matters: this
-  // thread's x chunks (L2), the first D rows' indices (HBM), then the
-  // codebooks straight into LDS (global_load_lds_dwordx4: lane l of a wave
-  // writes 16 bytes at the wave's LDS base + 16 l).  Loads return in order,
-  // so converting x waits for the x loads only.  No branch surrounds a load:
+  // Global loads are issued in the order they are needed: the codebooks
+  // straight into LDS (global_load_lds_dwordx4: lane l of a wave writes 16
+  // bytes at the wave's LDS base + 16 l), this thread's x chunks, then the
+  // first D rows' index planes from HBM.  Loads complete in issue order, so
+  // once at most the index loads are outstanding the codebooks and x have
+  // landed; the HBM latency of the index loads then overlaps the x
+  // conversion and the barrier.  No branch surrounds an index load:
   // out-of-range chunks and rows load a valid duplicate and are discarded.
-  // (waves whose chunks all lie past the end of x load nothing: a
-  // wave-uniform branch)
-  uint4 xin[XCH][XV];
-#pragma unroll
-  for (int i = 0; i < XCH; ++i) {
-    if (wave * 64 + NT * i < a.C) {
-      const int c = min(tid + NT * i, a.C - 1);
-      const uint4 *px = XF16 ? reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.x) + 32 * c)
-                             : reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(a.x) + 32 * c);
-#pragma unroll
-      for (int v = 0; v < XV; ++v) xin[i][v] = px[v];
-    }
-  }
-  sched_fence();
-  RowIdx R[D + 1];
-#pragma unroll
-  for (int k = 0; k < D; ++k) load_row(k, R[k]);
-  sched_fence();
 #pragma unroll
   for (int r = 0; r < CB_ITERS; ++r) {
     const int blk = (r * WAVES + wave) * 64;  // first codebook row of this wave's 1 KiB
@@ -142,6 +143,25 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
     }
   }
   sched_fence();
+  // (waves whose x chunks all lie past the end of x load none: a
+  // wave-uniform branch)
+  uint4 xin[XCH][XV];
+  const buf_t bx = make_buf(a.x, (uint32_t)a.k * (XF16 ? 2u : 4u));
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) {
+    if (wave * 64 + NT * i < a.C) {
+      const uint32_t c = (uint32_t)min(tid + NT * i, a.C - 1);
+#pragma unroll
+      for (int v = 0; v < XV; ++v) xin[i][v] = buf_u128(bx, c * (16u * XV) + 16u * v, 0);
+    }
+  }
+  sched_fence();
+  RowIdx R[D + 1];
+#pragma unroll
+  for (int k = 0; k < D; ++k) load_row(k, R[k]);
+  sched_fence();
+  constexpr int kIdxLoads = D * CPL * (S * (BITS == 12 ? 2 : 1) + 1);
+  wait_vmem<(kIdxLoads < 63 ? kIdxLoads : 63)>();
 
   // x -> LDS.  bf16 x becomes fp16 after a per-chunk power-of-two rescale
   // that puts the chunk's largest |x| in [2^14, 2^15): exact for every value
@@ -180,9 +200,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
       }
     }
   }
-  // the LDS-direct codebook loads of this wave have landed; the barrier
-  // makes every wave's codebook part and x visible
-  wait_all_memory();
+  // this wave's codebook part landed before its x; the barrier makes every
+  // wave's codebook part and x visible
   __syncthreads();
 
   // this lane's x chunks: registers for the whole launch (XREG) or LDS reads

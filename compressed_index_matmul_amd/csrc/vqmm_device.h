@@ -106,6 +106,18 @@ __device__ __forceinline__ void sched_group() {
 #endif
 }
 
+// Wait until at most N vector-memory loads of this wave are outstanding
+// (loads complete in issue order).  gfx9 s_waitcnt immediate: vmcnt bits
+// [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]; the other two counters
+// are left at their maxima (no wait).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N <= 63, "vmcnt holds 0..63");
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+#endif
+}
+
 // Wait for every outstanding memory operation of the wave.
 __device__ __forceinline__ void wait_all_memory() {
 #if defined(__HIP_DEVICE_COMPILE__)
