@@ -744,68 +744,83 @@ __global__ __launch_bounds__(256) void k_gemm_wide(GemmArgs a) {
     const uint32_t blk = (uint32_t)(((uint64_t)ks * a.smagic) >> 32);
     X.sc = buf_u16(bsc, vsc, 2u * blk);
   };
+  // group g of the thread's row in step s of quad Q (one codebook vector per
+  // stage)
+  auto gather1 = [&](const Quad<S> &Q, int s, int g, uint4 (&vg)[S]) {
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+      const uint32_t lw = s == 0 ? Q.lo[t].x : s == 1 ? Q.lo[t].y : s == 2 ? Q.lo[t].z : Q.lo[t].w;
+      uint32_t idx = (lw >> (8 * g)) & 0xffu;
+      if (BITS == 12) {
+        const uint32_t hw = s < 2 ? Q.hi[t].x : Q.hi[t].y;
+        idx |= ((hw >> (4 * (4 * (s & 1) + g))) & 0xfu) << 8;
+      }
+      vg[t] = s_cb[(t << BITS) + idx];
+    }
+  };
   // the four groups of the thread's row in step s of quad Q
   auto gather = [&](const Quad<S> &Q, int s, uint4 (&v)[4][S]) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int t = 0; t < S; ++t) {
-        const uint32_t lw = s == 0 ? Q.lo[t].x : s == 1 ? Q.lo[t].y : s == 2 ? Q.lo[t].z : Q.lo[t].w;
-        uint32_t idx = (lw >> (8 * g)) & 0xffu;
-        if (BITS == 12) {
-          const uint32_t hw = s < 2 ? Q.hi[t].x : Q.hi[t].y;
-          idx |= ((hw >> (4 * (4 * (s & 1) + g))) & 0xfu) << 8;
-        }
-        v[g][t] = s_cb[(t << BITS) + idx];
-      }
+    for (int g = 0; g < 4; ++g) gather1(Q, s, g, v[g]);
   };
   auto decode = [&](int g, const uint4 (&v)[S], uint32_t sc, uint4 *wt) {
     wt[wpos(tid, g)] = group_to_bf16<S>(v, h2f(sc));
   };
+  auto read_b2 = [&](const uint4 *wr, int half, int j0, bf16x8_t (&bfr)[8]) {
+#pragma unroll
+    for (int j = j0; j < j0 + 2; ++j)
+      bfr[j] = __builtin_bit_cast(bf16x8_t, wr[wpos(16 * (8 * half + j) + (lane & 15), lane >> 4)]);
+  };
   auto read_b = [&](const uint4 *wr, int half, bf16x8_t (&bfr)[8]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      bfr[j] = __builtin_bit_cast(bf16x8_t, wr[wpos(16 * (8 * half + j) + (lane & 15), lane >> 4)]);
+    for (int j = 0; j < 8; j += 2) read_b2(wr, half, j, bfr);
   };
   auto mma = [&](const XStep &X, const bf16x8_t (&bfr)[8], int half, int i) {
     const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, X.av[i]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) mfma_tied(acc[i][8 * half + j], afr, bfr[j]);
   };
-  // Iteration ks, two phases around one barrier.  A: the MFMAs of the first
-  // half of step ks (fragments in BA) overlap the gathers and decode of step
-  // ks+1 into tile (ks+1) & 1 and the reads of the second half of step ks
-  // (tile ks & 1) into BB.  Barrier: tile ks+1 is complete, and every read of
-  // tile ks & 1 has finished (it is rewritten in iteration ks+1).  B: the
-  // MFMAs of the second half (BB) overlap the reads of the first half of step
-  // ks+1 into BA; then the loads of step ks+4.
-  auto iter = [&](int ks, XStep &Xm, const XStep &Xd, const Quad<S> &Qd, int sd, Quad<S> &Qn, bool quad_load,
-                  bf16x8_t (&BA)[8], bf16x8_t (&BB)[8]) {
+  // Iteration ks, two phases around one barrier.  A: the reads of the second
+  // half of step ks (tile ks & 1) into BB are issued, then the MFMAs of the
+  // first half (fragments in BA) alternate with the decode of step ks+1
+  // (codebook vectors gathered one iteration earlier, in v) into tile
+  // (ks+1) & 1; the global loads of step ks+4 (and of a quad of index steps)
+  // go out after the first MFMA group (x of step ks+3 into the registers
+  // step ks-1 used; an index quad into the quad register set whose last
+  // step was gathered in the previous iteration).  Barrier: tile ks+1 is complete, and
+  // every read of tile ks & 1 has finished (it is rewritten in iteration
+  // ks+1).  B: four rounds of four LDS reads (two B fragments of the first
+  // half of step ks+1 into BA, the gathers of one group of step ks+2 into v)
+  // each followed by eight MFMAs of the second half (BB), so a wave never has
+  // more LDS reads in flight than the 15 the counter tracks and the MFMAs
+  // start at once.
+  auto iter = [&](int ks, const XStep &Xm, const XStep &Xd, XStep &Xl, const Quad<S> &Qg, int sg, Quad<S> &Qn,
+                  bool quad_load, bf16x8_t (&BA)[8], bf16x8_t (&BB)[8], uint4 (&v)[4][S]) {
     const uint4 *wr = s_w[ks & 1];
     uint4 *ww = s_w[(ks + 1) & 1];
-    uint4 v[4][S];
-    gather(Qd, sd, v);
     read_b(wr, 1, BB);
     sched_fence();
-    mma(Xm, BA, 0, 0);
-    decode(0, v[0], Xd.sc, ww);
-    mma(Xm, BA, 0, 1);
-    decode(1, v[1], Xd.sc, ww);
-    mma(Xm, BA, 0, 2);
-    decode(2, v[2], Xd.sc, ww);
-    mma(Xm, BA, 0, 3);
-    decode(3, v[3], Xd.sc, ww);
-    sched_fence();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mma(Xm, BA, 0, i);
+      sched_fence();
+      decode(i, v[i], Xd.sc, ww);
+      sched_fence();
+      if (i == 0) {
+        if (quad_load) load_quad((ks + 6) / 4, Qn);
+        load_x(ks + 3, Xl);
+        sched_fence();
+      }
+    }
     __syncthreads();
-    read_b(ww, 0, BA);
-    sched_fence();
-    mma(Xm, BB, 1, 0);
-    mma(Xm, BB, 1, 1);
-    mma(Xm, BB, 1, 2);
-    mma(Xm, BB, 1, 3);
-    sched_fence();
-    if (quad_load) load_quad((ks + 5) / 4, Qn);
-    load_x(ks + 4, Xm);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      read_b2(ww, 0, 2 * i, BA);
+      gather1(Qg, sg, i, v[i]);
+      sched_fence();
+      mma(Xm, BB, 1, i);
+      sched_fence();
+    }
   };
 
   Quad<S> Q0, Q1;
@@ -815,36 +830,49 @@ __global__ __launch_bounds__(256) void k_gemm_wide(GemmArgs a) {
   load_x(0, X0);
   load_x(1, X1);
   load_x(2, X2);
-  load_x(3, X3);
   wait_all_memory();  // codebook (LDS-direct) has landed (and the first steps)
   __syncthreads();
-  {
-    uint4 v[4][S];
-    gather(Q0, 0, v);
+  uint4 v[4][S];
+  gather(Q0, 0, v);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) decode(g, v[g], X0.sc, s_w[0]);
-  }
+  for (int g = 0; g < 4; ++g) decode(g, v[g], X0.sc, s_w[0]);
+  gather(Q0, 1, v);
   __syncthreads();
   bf16x8_t BA[8], BB[8];
   read_b(s_w[0], 0, BA);
+  // eight steps (two quads) per trip: iteration ks gathers step ks+2, so quad
+  // Q0 (steps ks..ks+3) is last gathered in iteration ks+1 and refilled in
+  // iteration ks+2 with steps ks+8..ks+11 (first gathered in iteration
+  // ks+6); Q1 likewise in iterations ks+5 / ks+6 / ks+10
   for (int ks = 0; ks < nks; ks += 8) {
-    iter(ks + 0, X0, X1, Q0, 1, Q0, false, BA, BB);
-    iter(ks + 1, X1, X2, Q0, 2, Q0, false, BA, BB);
-    iter(ks + 2, X2, X3, Q0, 3, Q0, false, BA, BB);
-    iter(ks + 3, X3, X0, Q1, 0, Q0, true, BA, BB);   // quad (ks+8)/4 -> Q0
-    iter(ks + 4, X0, X1, Q1, 1, Q1, false, BA, BB);
-    iter(ks + 5, X1, X2, Q1, 2, Q1, false, BA, BB);
-    iter(ks + 6, X2, X3, Q1, 3, Q1, false, BA, BB);
-    iter(ks + 7, X3, X0, Q0, 0, Q1, true, BA, BB);   // quad (ks+12)/4 -> Q1
+    iter(ks + 0, X0, X1, X3, Q0, 2, Q0, false, BA, BB, v);
+    iter(ks + 1, X1, X2, X0, Q0, 3, Q0, false, BA, BB, v);
+    iter(ks + 2, X2, X3, X1, Q1, 0, Q0, true, BA, BB, v);   // quad (ks+8)/4 -> Q0
+    iter(ks + 3, X3, X0, X2, Q1, 1, Q1, false, BA, BB, v);
+    iter(ks + 4, X0, X1, X3, Q1, 2, Q1, false, BA, BB, v);
+    iter(ks + 5, X1, X2, X0, Q1, 3, Q1, false, BA, BB, v);
+    iter(ks + 6, X2, X3, X1, Q0, 0, Q1, true, BA, BB, v);   // quad (ks+12)/4 -> Q1
+    iter(ks + 7, X3, X0, X2, Q0, 1, Q1, false, BA, BB, v);
+    // The hardware does not interlock a read of an accumulator after the
+    // MFMA that writes it, and the compiler cannot see into the MFMA asm: at
+    // the loop exit it may copy accumulators (register-allocation moves)
+    // right after the last MFMAs.  32 wait cycles at the end of every trip
+    // (inside the loop, so before any such copy) cover the MFMA latency.
+    sched_fence();
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+#endif
+    sched_fence();
   }
-  // the last MFMAs have written their accumulators before they are read
+  // the same wait before the epilogue reads, tied to every block of eight
+  // accumulators
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
                  : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
                    "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
-    asm volatile("s_nop 0"
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
                  : "+a"(acc[i][8]), "+a"(acc[i][9]), "+a"(acc[i][10]), "+a"(acc[i][11]), "+a"(acc[i][12]),
                    "+a"(acc[i][13]), "+a"(acc[i][14]), "+a"(acc[i][15]));
   }
