@@ -288,7 +288,7 @@ __global__ __launch_bounds__(256) void k_gemm_large(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_w[2][kLN * kWP];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int L = (blockIdx.x % 8) * a.per_xcd + blockIdx.x / 8;
   if (L >= a.tiles_m * a.tiles_n) return;  // whole workgroup, before any barrier
   const int m0 = (L / a.tiles_n) * kLM;
@@ -476,7 +476,7 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_w[3][kLN * kWP];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int L = (blockIdx.x % 8) * a.per_xcd + blockIdx.x / 8;
   if (L >= a.tiles_m * a.tiles_n) return;  // whole workgroup, before any barrier
   const int m0 = (L / a.tiles_n) * kLM;
@@ -683,7 +683,7 @@ __global__ __launch_bounds__(256) void k_gemm_wide(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint4 s_w[2][kWN * 4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int L = (blockIdx.x % 8) * a.per_xcd + blockIdx.x / 8;
   if (L >= a.tiles_m * a.tiles_n) return;  // whole workgroup, before any barrier
   const int m0 = (L / a.tiles_n) * kLM;
@@ -941,7 +941,7 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_small(GemmArgs a) {
   __shared__ float s_red[kSWaves][16][17];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   if (CB_LDS) {
     constexpr int CBN = S << BITS;
 #pragma unroll 4
@@ -1045,34 +1045,34 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_small(GemmArgs a) {
   }
 }
 
-// 1 <= m <= 16, K % 128 == 0, scale_block % 32 == 0, LDS codebooks.
-// A unit is 32 W rows (two blocks of 16) over a K range; lane l decodes, per
-// 32-column K step, group l / 16 of row l % 16 of each block straight into a
-// B fragment of v_mfma_f32_16x16x32_bf16, and loads 8 x values of token l % 16
-// (the A fragment, shared by both blocks).  A workgroup's eight waves take
-// its units times KP K parts (KP = 8 / units per workgroup); the KP partial
-// tiles of a unit are added in LDS in a fixed order at the end.  Index planes
-// come four K steps at a time (16 + 8 bytes per stage and block), x and the
-// scales two steps ahead, all as buffer loads.
-constexpr int kFewBlocks = 2;  // 16-row blocks per unit
-
-template <int S>
+// 1 <= m <= 64 tokens, K % 256 == 0, scale_block % 128 == 0, LDS codebooks
+// of 8/12-bit indices.  A unit is NB blocks of 16 W rows over a K range;
+// lane l decodes, per 32-column K step, group l / 16 of row l % 16 of each
+// block straight into a B fragment of v_mfma_f32_16x16x32_bf16 (no LDS round
+// trip) and multiplies it with the A fragments of TB blocks of 16 tokens
+// (lane l loads 8 x values of token l % 16 of each block).  A workgroup's
+// eight waves take its units times KP K parts; the KP partial tiles of a
+// unit are added in LDS in a fixed order at the end.  Index planes and the
+// scale (one per 128 columns at most) come four K steps at a time, x three
+// steps ahead, all as buffer loads with wave-uniform offsets.
+template <int S, int NB>
 struct FewQuad {
-  uint4 lo[kFewBlocks][S];
-  uint2 hi[kFewBlocks][S];
+  uint4 lo[NB][S];
+  uint2 hi[NB][S];
+  uint32_t sc[NB];  // fp16 scale of the lane's row in each block
 };
+template <int TB>
 struct FewStep {
-  uint4 av;                // A fragment
-  uint32_t sc[kFewBlocks];  // scale of the lane's row in each block
+  uint4 av[TB];  // A fragments of the token blocks
 };
 
-template <int S, int BITS>
+template <int S, int BITS, int NB, int TB>
 __global__ __launch_bounds__(kSWaves * 64) void k_gemm_few(GemmArgs a, int units_per_wg, int kp) {
   __shared__ uint4 s_cb[S << BITS];
-  __shared__ float s_red[kSWaves][kFewBlocks][16][17];
+  __shared__ float s_red[kSWaves][NB][16][17];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   {
     constexpr int CBN = S << BITS;
 #pragma unroll 4
@@ -1083,16 +1083,15 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_few(GemmArgs a, int units
                       s_cb + blk);
     }
   }
-  const int units = (a.n + 16 * kFewBlocks - 1) / (16 * kFewBlocks);
+  const int units = (a.n + 16 * NB - 1) / (16 * NB);
   const int nks = a.G / 4;
-  const int steps = nks / kp;        // K steps per part (a multiple of 4)
+  const int steps = nks / kp;        // K steps per part (a multiple of 8)
   const int ui = wave / kp;          // unit slot of this wave in the workgroup
   const int part = wave % kp;
   const int unit = blockIdx.x * units_per_wg + ui;
   const bool active = ui < units_per_wg && unit < units;  // wave-uniform
   const int r16 = lane & 15;
   const int q = lane >> 4;           // k chunk of the lane within a K step
-  const int tok = min(r16, a.m - 1); // tokens past m only feed unstored outputs
   const int ks0 = part * steps;
 
   const uint32_t ng = (uint32_t)a.n * a.G;
@@ -1104,42 +1103,51 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_few(GemmArgs a, int units
   }
   const buf_t bsc = make_buf(a.sc, 2u * a.n * a.nblk);
   const buf_t bx = make_buf(a.x, 2u * a.m * a.k);
-  uint32_t vlo[kFewBlocks], vsc[kFewBlocks];
+  uint32_t vlo[NB], vsc[NB];
 #pragma unroll
-  for (int b = 0; b < kFewBlocks; ++b) {
-    const int row = min((active ? unit : 0) * 16 * kFewBlocks + 16 * b + r16, a.n - 1);
+  for (int b = 0; b < NB; ++b) {
+    const int row = min((active ? unit : 0) * 16 * NB + 16 * b + r16, a.n - 1);
     vlo[b] = (uint32_t)row * a.G;
     vsc[b] = 2u * row * a.nblk;
   }
-  const uint32_t vx = 2u * ((uint32_t)tok * a.k + 8 * q);
-
-  f32x4 acc[kFewBlocks];
+  uint32_t vx[TB];
 #pragma unroll
-  for (int b = 0; b < kFewBlocks; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int tb = 0; tb < TB; ++tb) {
+    const int tok = min(16 * tb + r16, a.m - 1);  // tokens past m only feed unstored outputs
+    vx[tb] = 2u * ((uint32_t)tok * a.k + 8 * q);
+  }
 
-  // loads of step / quad index i of this part, clamped to its last one
-  auto load_quad = [&](int j, FewQuad<S> &Q) {
+  f32x4 acc[TB][NB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[tb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // loads of quad / step index i of this part, clamped to its last one
+  auto load_quad = [&](int j, FewQuad<S, NB> &Q) {
     j = ks0 / 4 + min(j, steps / 4 - 1);
+    const uint32_t blk = (uint32_t)(((uint64_t)(4 * j) * a.smagic) >> 32);  // (128 j) / scale_block
 #pragma unroll
-    for (int b = 0; b < kFewBlocks; ++b)
+    for (int b = 0; b < NB; ++b) {
 #pragma unroll
       for (int t = 0; t < S; ++t) {
         Q.lo[b][t] = buf_u128(blo[t], vlo[b], 16u * j);
         if (BITS == 12) Q.hi[b][t] = buf_u64(bhi[t], vlo[b] >> 1, 8u * j);
       }
+      Q.sc[b] = buf_u16(bsc, vsc[b], 2u * blk);
+    }
   };
-  auto load_step = [&](int i, FewStep &X) {
+  auto load_step = [&](int i, FewStep<TB> &X) {
     const int ks = ks0 + min(i, steps - 1);
-    X.av = buf_u128(bx, vx, 64u * ks);
-    const uint32_t blk = (uint32_t)(((uint64_t)ks * a.smagic) >> 32);  // (32 ks) / scale_block
 #pragma unroll
-    for (int b = 0; b < kFewBlocks; ++b) X.sc[b] = buf_u16(bsc, vsc[b], 2u * blk);
+    for (int tb = 0; tb < TB; ++tb) X.av[tb] = buf_u128(bx, vx[tb], 64u * ks);
   };
-  // decode the lane's group of block b in step s (0..3) of quad Q, multiply
-  auto step = [&](const FewQuad<S> &Q, int s, const FewStep &X) {
-    uint4 v[kFewBlocks][S];
+  // decode the lane's group of each block in step s (0..3) of quad Q and
+  // multiply with every token block
+  auto step = [&](const FewQuad<S, NB> &Q, int s, const FewStep<TB> &X) {
+    uint4 v[NB][S];
 #pragma unroll
-    for (int b = 0; b < kFewBlocks; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int t = 0; t < S; ++t) {
         const uint4 lw4 = Q.lo[b][t];
@@ -1151,16 +1159,18 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_few(GemmArgs a, int units
         }
         v[b][t] = s_cb[(t << BITS) + idx];
       }
-    const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, X.av);
 #pragma unroll
-    for (int b = 0; b < kFewBlocks; ++b) {
-      const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, group_to_bf16<S>(v[b], h2f(X.sc[b])));
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr, acc[b], 0, 0, 0);
+    for (int b = 0; b < NB; ++b) {
+      const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, group_to_bf16<S>(v[b], h2f(Q.sc[b])));
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+        acc[tb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, X.av[tb]), bfr,
+                                                              acc[tb][b], 0, 0, 0);
     }
   };
 
-  FewQuad<S> Q0, Q1;
-  FewStep X0, X1, X2, X3;
+  FewQuad<S, NB> Q0, Q1;
+  FewStep<TB> X0, X1, X2, X3;
   load_quad(0, Q0);
   load_quad(1, Q1);
   load_step(0, X0);
@@ -1169,7 +1179,7 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_few(GemmArgs a, int units
   wait_all_memory();  // codebook (LDS-direct) has landed
   __syncthreads();
   if (active) {  // wave-uniform; every wave reaches the barriers below
-    // eight steps per trip (two quads); steps ahead: 3 (x, scales), 4-8 (quads)
+    // eight steps per trip (two quads); steps ahead: 3 (x), 4-8 (quads)
     for (int i = 0; i < steps; i += 8) {
       load_step(i + 3, X3);
       step(Q0, 0, X0);
@@ -1191,23 +1201,28 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_few(GemmArgs a, int units
       load_quad(i / 4 + 3, Q1);
     }
   }
-  // lane holds D[token 4 (lane / 16) + r][row lane % 16] of each block
+  // per token block: lane holds D[token 4 (lane / 16) + r][row lane % 16] of
+  // each W block; part 0 of each unit adds the KP parts in order
 #pragma unroll
-  for (int b = 0; b < kFewBlocks; ++b)
+  for (int tb = 0; tb < TB; ++tb) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s_red[wave][b][4 * (lane >> 4) + r][lane & 15] = acc[b][r];
-  __syncthreads();
-  if (active && part == 0) {
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int b = 0; b < kFewBlocks; ++b)
+      for (int r = 0; r < 4; ++r) s_red[wave][b][4 * (lane >> 4) + r][lane & 15] = acc[tb][b][r];
+    __syncthreads();
+    if (active && part == 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ti = 4 * (lane >> 4) + r;
-        float sum = 0.f;
-        for (int h = 0; h < kp; ++h) sum += s_red[wave + h][b][ti][lane & 15];
-        const int col = unit * 16 * kFewBlocks + 16 * b + (lane & 15);
-        if (ti < a.m && col < a.n) a.y[(size_t)ti * a.n + col] = sum;
-      }
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ti = 16 * tb + 4 * (lane >> 4) + r;
+          float sum = 0.f;
+          for (int h = 0; h < kp; ++h) sum += s_red[wave + h][b][4 * (lane >> 4) + r][lane & 15];
+          const int col = unit * 16 * NB + 16 * b + (lane & 15);
+          if (ti < a.m && col < a.n) a.y[(size_t)ti * a.n + col] = sum;
+        }
+    }
+    __syncthreads();
   }
 }
 
@@ -1219,7 +1234,7 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_small_gen(GemmArgs a) {
   __shared__ float s_red[kSWaves][16][17];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   if (CB_LDS) {
     for (int i = tid; i < (S << BITS); i += kSWaves * 64)
       s_cb[i] = reinterpret_cast<const uint4 *>(a.cb[i >> BITS])[i & ((1 << BITS) - 1)];
@@ -1285,31 +1300,48 @@ static GemmArgs make_gemm_args(const WView &w, const uint16_t *x, int m, float *
   return a;
 }
 
+// The few-token unit kernel with NB row blocks per unit and TB token blocks;
+// false when the shape leaves it fewer units than half the CUs (the slab
+// and tile kernels spread such shapes better).
+template <int S, int BITS, int NB>
+static bool launch_few_nb(const GemmArgs &a, hipStream_t s) {
+  const int cus = device_cu_count();
+  const int units = (a.n + 16 * NB - 1) / (16 * NB);
+  if (2 * units < cus) return false;
+  const int grid = units < cus ? units : cus;
+  const int upw = (units + grid - 1) / grid;
+  const int nks = a.k / 32;
+  // K parts per unit: as many as the eight waves allow, each a whole number
+  // of eight-step trips
+  int kp = 1;
+  while (kp * 2 * upw <= kSWaves && nks % (kp * 2 * 8) == 0) kp *= 2;
+  if (upw * kp > kSWaves) return false;
+  switch ((a.m + 15) / 16) {
+    case 1: hipLaunchKernelGGL((k_gemm_few<S, BITS, NB, 1>), dim3(grid), dim3(kSWaves * 64), 0, s, a, upw, kp); break;
+    case 2: hipLaunchKernelGGL((k_gemm_few<S, BITS, NB, 2>), dim3(grid), dim3(kSWaves * 64), 0, s, a, upw, kp); break;
+    case 3: hipLaunchKernelGGL((k_gemm_few<S, BITS, NB, 3>), dim3(grid), dim3(kSWaves * 64), 0, s, a, upw, kp); break;
+    default: hipLaunchKernelGGL((k_gemm_few<S, BITS, NB, 4>), dim3(grid), dim3(kSWaves * 64), 0, s, a, upw, kp); break;
+  }
+  return true;
+}
+
 template <int S, int BITS, bool CB_LDS>
 static void launch_gemm_sb(const GemmArgs &a0, hipStream_t s) {
   GemmArgs a = a0;
+  if constexpr (CB_LDS && BITS != 16) {
+    // 1..64 tokens: the unit kernel (whole eight-step trips per K part, one
+    // scale per 128 columns at most); two row blocks per unit for one token
+    // block once there are enough units for every CU (more token blocks with
+    // two row blocks would not fit the 256 registers of two waves per SIMD)
+    if (a.m <= 64 && a.k % 256 == 0 && a.bs % 128 == 0 && a.k < (1 << 20)) {
+      const bool two = a.m <= 16 && (a.n + 31) / 32 >= device_cu_count();
+      if (two ? launch_few_nb<S, BITS, 2>(a, s) : launch_few_nb<S, BITS, 1>(a, s)) return;
+    }
+  }
   if (a.m <= 16) {
     const int nslabs = (a.n + 15) / 16;
     int nwg = device_cu_count();
     if (nwg > nslabs) nwg = nslabs;
-    if constexpr (CB_LDS && BITS != 16) {
-      // the unit kernel: K in whole quads per part (K % 256 == 0 keeps at
-      // least two quads per part for the eight-step trips)
-      if (a.k % 256 == 0 && a.bs % 32 == 0 && a.k < (1 << 20)) {
-        const int units = (a.n + 16 * kFewBlocks - 1) / (16 * kFewBlocks);
-        const int cus = device_cu_count();
-        // with fewer units than CUs the slab kernel below spreads better
-        const int grid = units < cus ? 0 : cus;
-        const int upw = grid > 0 ? (units + grid - 1) / grid : 1;
-        const int nks = a.k / 32;
-        int kp = 1;
-        while (kp * 2 * upw <= kSWaves && nks % (kp * 2 * 8) == 0) kp *= 2;
-        if (grid > 0 && upw * kp <= kSWaves) {
-          hipLaunchKernelGGL((k_gemm_few<S, BITS>), dim3(grid), dim3(kSWaves * 64), 0, s, a, upw, kp);
-          return;
-        }
-      }
-    }
     if (a.k % 128 == 0 && a.bs % 32 == 0)
       hipLaunchKernelGGL((k_gemm_small<S, BITS, CB_LDS>), dim3(nwg), dim3(kSWaves * 64), 0, s, a);
     else

@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kGenWaves * 64) void k_gemv_gen(GemvArgs a, int xt)
   __shared__ float s_x[X_LDS ? kGenMaxXLds : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   if (X_LDS) {
     for (int i = tid; i < a.k; i += kGenWaves * 64) {
       s_x[i] = (xt == VQ_F32) ? reinterpret_cast<const float *>(a.x)[i]

@@ -172,6 +172,23 @@ def test_gemm_tile_ragged(vq, m, n, k, st, bits, bs):
     assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"gemm {m}x{n}x{k} bs {bs}")
 
 
+@pytest.mark.parametrize("m,n,k,st,bits,bs", [(17, 4096, 512, 2, 12, 128), (40, 8200, 1024, 1, 8, 1024),
+                                             (64, 4100, 256, 2, 12, 256), (33, 2500, 768, 2, 12, 384),
+                                             (16, 4096, 512, 1, 12, 128), (2, 2049, 512, 2, 12, 512)])
+def test_gemm_token_blocks(vq, m, n, k, st, bits, bs):
+    """Up to 64 tokens on the unit kernel: one to four 16-token blocks, one
+    16-row block per unit (every CU busy from 128 units), ragged W rows and
+    tokens, K parts of one to several trips, scale blocks of 128 columns up
+    to a whole row."""
+    import torch
+    sw = vqsynth.random_weight(n, k, st, bits, bs, seed=m * 17 + n + k)
+    xs, x64 = _x(m, k, "bf16", m * 19 + n)
+    y = vq.vq_gemm(device_weight(sw), x_to_device(xs, "bf16"))
+    torch.cuda.synchronize()
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
+    assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"gemm {m}x{n}x{k} bs {bs}")
+
+
 @pytest.mark.parametrize("m,n,k,st,bits,bs", [(5, 8200, 512, 2, 12, 128), (16, 8192, 1024, 1, 8, 1024),
                                              (1, 9000, 256, 2, 12, 32), (11, 12000, 768, 2, 12, 64)])
 def test_gemm_few_tokens_wide(vq, m, n, k, st, bits, bs):
