@@ -152,6 +152,8 @@ def run_decode_leg(vq, workload, steps, warmup, batch=1, rht=False):
             if rht:
                 out.append(lambda j=j: vq.rht_apply(xs[j], signs[j], cfg["rht"], out=xr[j]))
                 out.append(lambda j=j, w=w: vq.vq_gemv(w, xr[j], y=ys[j]))
+            elif batch > 16:  # more tokens than vq_gemv takes: the same product through vq_gemm
+                out.append(lambda j=j, w=w: vq.vq_gemm(w, xs[j], y=ys[j]))
             else:
                 out.append(lambda j=j, w=w: vq.vq_gemv(w, xs[j], y=ys[j]))
         return out
@@ -404,6 +406,9 @@ def main():
     if only or not args.quick:
         legs = [("mlp70b_rht_gemv_b1", lambda: run_decode_leg(vq, "mlp70b", max(5, args.steps // 5), 3, rht=True)),
                 ("llama8b_gemv_b16", lambda: run_decode_leg(vq, "llama8b", args.steps, args.warmup, batch=16)),
+                ("llama8b_tokens_2_to_64", lambda: {
+                    f"m{m}": run_decode_leg(vq, "llama8b", max(5, args.steps // 4), 2, batch=m)
+                    for m in (2, 8, 32, 64)}),
                 ("prefill_gemm_m2048", lambda: run_gemm_leg(vq, max(5, args.steps // 5), 3)),
                 ("smollm_gemv_b1", lambda: run_decode_leg(vq, "smollm", args.steps, args.warmup)),
                 ("tiny_gemv_b1", lambda: run_decode_leg(vq, "tiny", args.steps, args.warmup)),
