@@ -637,6 +637,20 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
     iter(ks + 6, X2, X0, B0, B1, Q0, 0, Q1, true);   // quad (ks+12)/4 -> Q1
     iter(ks + 7, X3, X1, B1, B0, Q0, 1, Q1, false);
   }
+  // tiles wholly inside y: descriptor stores as in the wide kernel
+  if (m0 + kLM <= a.m && n0 + kLN <= a.n && (uint64_t)kLM * a.n * 4 < (1u << 31)) {
+    const buf_t by = make_buf(a.y + (size_t)m0 * a.n + n0, (uint32_t)kLM * (uint32_t)a.n * 4u);
+    const uint32_t vb = (((uint32_t)wave * 64 + 4 * (lane >> 4)) * (uint32_t)a.n + (lane & 15)) * 4u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t so = (uint32_t)(16 * i + r) * (uint32_t)a.n * 4u;
+#pragma unroll
+        for (int jn = 0; jn < 8; ++jn) buf_store_f32(acc[i][jn][r], by, vb + 64u * jn, so);
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -877,6 +891,23 @@ __global__ __launch_bounds__(256) void k_gemm_wide(GemmArgs a) {
                    "+a"(acc[i][13]), "+a"(acc[i][14]), "+a"(acc[i][15]));
   }
 #endif
+  // Tiles lying wholly inside y (every row < m, every column < n) store
+  // through a descriptor based at the tile's first element without per-store
+  // tests: the lane's offset is fixed, rows step by a scalar offset, columns
+  // by an immediate.  Edge tiles take the tested stores below.
+  if (m0 + kLM <= a.m && n0 + kWN <= a.n && (uint64_t)kLM * a.n * 4 < (1u << 31)) {
+    const buf_t by = make_buf(a.y + (size_t)m0 * a.n + n0, (uint32_t)kLM * (uint32_t)a.n * 4u);
+    const uint32_t vb = (((uint32_t)wave * 64 + 4 * (lane >> 4)) * (uint32_t)a.n + (lane & 15)) * 4u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t so = (uint32_t)(16 * i + r) * (uint32_t)a.n * 4u;
+#pragma unroll
+        for (int jn = 0; jn < 16; ++jn) buf_store_f32(acc[i][jn][r], by, vb + 64u * jn, so);
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll

@@ -190,6 +190,18 @@ __device__ __forceinline__ uint4 buf_u128(buf_t r, uint32_t voff, uint32_t soff)
 #endif
 }
 
+// Store one float at descriptor + lane offset + wave-uniform offset (a
+// vector-memory store).  The hardware range check of raw buffers does not
+// include the scalar offset, so callers keep every store inside the buffer
+// themselves.
+__device__ __forceinline__ void buf_store_f32(float v, buf_t r, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
+#else
+  (void)v, (void)r, (void)voff, (void)soff;
+#endif
+}
+
 // Index of flat group f of stage planes (any width).
 __device__ __forceinline__ uint32_t load_index(int bits, const uint8_t *lo, const uint8_t *hi,
                                                const uint16_t *i16, size_t f) {
