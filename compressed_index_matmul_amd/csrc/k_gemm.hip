@@ -597,8 +597,8 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
       sched_group<0x002, 2>();
     }
     sched_fence();
+    load_x(ks + 4, Xm);  // before the index quad: see k_gemm_wide
     if (quad_load) load_quad((ks + 6) / 4, Qn);
-    load_x(ks + 4, Xm);
     __syncthreads();
   };
 
@@ -821,8 +821,11 @@ __global__ __launch_bounds__(256) void k_gemm_wide(GemmArgs a) {
       decode(i, v[i], Xd.sc, ww);
       sched_fence();
       if (i == 0) {
-        if (quad_load) load_quad((ks + 6) / 4, Qn);
+        // x first: loads complete in issue order, so the next x load waited
+        // on after an index quad (from HBM) is then issued an iteration
+        // later and the quad gets four iterations instead of three
         load_x(ks + 3, Xl);
+        if (quad_load) load_quad((ks + 6) / 4, Qn);
         sched_fence();
       }
     }
