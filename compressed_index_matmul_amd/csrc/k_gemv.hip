@@ -47,12 +47,12 @@ struct GemvArgs {
 // ---------------------------------------------------------------------------
 // LDS bytes of the fast kernel: codebooks, x (fp16: 64 B per 4-group chunk
 // plus a float factor; fp32: 128 B per chunk) for 64 * CPL chunks.
-__host__ __device__ constexpr size_t gemv_lds_bytes(int S, int BITS, int CPL, bool XF16) {
-  return (size_t)(S << BITS) * 16 + (size_t)64 * CPL * (XF16 ? 64 + 4 : 128 + 0) + (XF16 ? 0 : 4);
+__host__ __device__ constexpr size_t gemv_lds_bytes(int S, int BITS, int CPL, bool XF16, int T = 1) {
+  return (size_t)(S << BITS) * 16 + (size_t)T * (64 * CPL * (XF16 ? 64 + 4 : 128 + 0) + (XF16 ? 0 : 4));
 }
 constexpr size_t kLdsBytes = 163840;  // 160 KiB per workgroup on gfx950
 
-template <int S, int BITS, int CPL, int WAVES, bool XF16, int D, bool XREG, bool PIPE>
+template <int S, int BITS, int CPL, int WAVES, bool XF16, int D, bool XREG, bool PIPE, int T = 1>
 __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
   constexpr int NT = WAVES * 64;
   constexpr int CBN = S << BITS;                 // codebook rows of all stages
@@ -61,11 +61,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
   constexpr int CMAX = 64 * CPL;                 // chunk capacity
   constexpr int XCH = (CMAX + NT - 1) / NT;      // x chunks converted per thread
   static_assert(XF16 || XREG, "fp32 x is always held in registers");
+  static_assert(T == 1 || (XF16 && XREG), "several tokens: bf16 x held in registers");
   // x in LDS is vector-major (s_x[v * CMAX + c]) so that a wave reading the
   // same vector of 64 consecutive chunks touches consecutive 16-byte slots.
   __shared__ uint4 s_cb[CBN];
-  __shared__ uint4 s_x[CMAX * XV];
-  __shared__ float s_f[XF16 ? CMAX : 1];
+  __shared__ uint4 s_x[T][CMAX * XV];  // T tokens (x is [T][k])
+  __shared__ float s_f[T][XF16 ? CMAX : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: row math stays scalar
@@ -145,16 +146,19 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
   sched_fence();
   // (waves whose x chunks all lie past the end of x load none: a
   // wave-uniform branch)
-  uint4 xin[XCH][XV];
-  const buf_t bx = make_buf(a.x, (uint32_t)a.k * (XF16 ? 2u : 4u));
+  uint4 xin[T][XCH][XV];
+  const uint32_t xrow = (uint32_t)a.k * (XF16 ? 2u : 4u);  // bytes per token
+  const buf_t bx = make_buf(a.x, xrow * T);
 #pragma unroll
-  for (int i = 0; i < XCH; ++i) {
-    if (wave * 64 + NT * i < a.C) {
-      const uint32_t c = (uint32_t)min(tid + NT * i, a.C - 1);
+  for (int tt = 0; tt < T; ++tt)
 #pragma unroll
-      for (int v = 0; v < XV; ++v) xin[i][v] = buf_u128(bx, c * (16u * XV) + 16u * v, 0);
+    for (int i = 0; i < XCH; ++i) {
+      if (wave * 64 + NT * i < a.C) {
+        const uint32_t c = (uint32_t)min(tid + NT * i, a.C - 1);
+#pragma unroll
+        for (int v = 0; v < XV; ++v) xin[tt][i][v] = buf_u128(bx, c * (16u * XV) + 16u * v, xrow * tt);
+      }
     }
-  }
   sched_fence();
   RowIdx R[D + 1];
 #pragma unroll
@@ -168,6 +172,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
   // within 2^28 of that maximum.  The chunk's partial dot product is scaled
   // back by s_f[c].
 #pragma unroll
+  for (int tt = 0; tt < T; ++tt)
+#pragma unroll
   for (int i = 0; i < XCH; ++i) {
     const int c = tid + NT * i;
     if (c < a.C) {
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
         float mx = 0.f;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const uint32_t w4[4] = {xin[i][v].x, xin[i][v].y, xin[i][v].z, xin[i][v].w};
+          const uint32_t w4[4] = {xin[tt][i][v].x, xin[tt][i][v].y, xin[tt][i][v].z, xin[tt][i][v].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             mx = fmaxf(mx, fmaxf(fabsf(bf2f(w4[e] & 0xffffu)), fabsf(bf2f(w4[e] >> 16))));
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
         const int xexp = (mx > 0.f && mx <= 3.0e38f) ? 14 - ilogbf(mx) : 0;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const uint32_t w4[4] = {xin[i][v].x, xin[i][v].y, xin[i][v].z, xin[i][v].w};
+          const uint32_t w4[4] = {xin[tt][i][v].x, xin[tt][i][v].y, xin[tt][i][v].z, xin[tt][i][v].w};
           uint32_t o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -191,12 +197,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
                                       (_Float16)ldexpf(bf2f(w4[e] >> 16), xexp)};
             o[e] = __builtin_bit_cast(uint32_t, h);
           }
-          s_x[v * CMAX + c] = make_uint4(o[0], o[1], o[2], o[3]);
+          s_x[tt][v * CMAX + c] = make_uint4(o[0], o[1], o[2], o[3]);
         }
-        s_f[c] = ldexpf(1.f, -xexp);
+        s_f[tt][c] = ldexpf(1.f, -xexp);
       } else {
 #pragma unroll
-        for (int v = 0; v < 8; ++v) s_x[v * CMAX + c] = xin[i][v];
+        for (int v = 0; v < 8; ++v) s_x[tt][v * CMAX + c] = xin[tt][i][v];
       }
     }
   }
@@ -206,26 +212,29 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
 
   // this lane's x chunks: registers for the whole launch (XREG) or LDS reads
   // per use; the per-chunk factor, zero for chunks past the end of the row
-  half2_t xh[XREG && XF16 ? CPL : 1][16];
+  half2_t xh[T][XREG && XF16 ? CPL : 1][16];
   float xf[XF16 ? 1 : CPL][32];
-  float fm[CPL];
+  float fm[T][CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
-    fm[j] = XF16 ? (ok[j] ? s_f[cc[j]] : 0.f) : (ok[j] ? 1.f : 0.f);
-    if (XF16 && XREG) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const uint4 u = s_x[v * CMAX + cc[j]];
-        xh[j][4 * v + 0] = as_h2(u.x);
-        xh[j][4 * v + 1] = as_h2(u.y);
-        xh[j][4 * v + 2] = as_h2(u.z);
-        xh[j][4 * v + 3] = as_h2(u.w);
+    for (int tt = 0; tt < T; ++tt) {
+      fm[tt][j] = XF16 ? (ok[j] ? s_f[tt][cc[j]] : 0.f) : (ok[j] ? 1.f : 0.f);
+      if (XF16 && XREG) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint4 u = s_x[tt][v * CMAX + cc[j]];
+          xh[tt][j][4 * v + 0] = as_h2(u.x);
+          xh[tt][j][4 * v + 1] = as_h2(u.y);
+          xh[tt][j][4 * v + 2] = as_h2(u.z);
+          xh[tt][j][4 * v + 3] = as_h2(u.w);
+        }
       }
     }
     if (!XF16) {
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
-        const uint4 u = s_x[v * CMAX + cc[j]];
+        const uint4 u = s_x[0][v * CMAX + cc[j]];
         xf[j][4 * v + 0] = __uint_as_float(u.x);
         xf[j][4 * v + 1] = __uint_as_float(u.y);
         xf[j][4 * v + 2] = __uint_as_float(u.z);
@@ -251,40 +260,54 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
       }
     if (!XREG) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) it.x[v] = s_x[v * CMAX + cc[j]];
+      for (int v = 0; v < 4; ++v) it.x[v] = s_x[0][v * CMAX + cc[j]];
     }
   };
-  auto dot = [&](int j, const Item &it) -> float {
-    float d = 0.f;
+  // dot products of chunk j's gathered vectors with x of every token
+  auto dot = [&](int j, const Item &it, float (&d)[T]) {
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt) d[tt] = 0.f;
 #pragma unroll
     for (int t = 0; t < S; ++t)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (XF16) {
-          const uint4 xq = it.x[XREG ? 0 : q];
-          const half2_t x0 = XREG ? xh[XREG ? j : 0][4 * q + 0] : as_h2(xq.x);
-          const half2_t x1 = XREG ? xh[XREG ? j : 0][4 * q + 1] : as_h2(xq.y);
-          const half2_t x2 = XREG ? xh[XREG ? j : 0][4 * q + 2] : as_h2(xq.z);
-          const half2_t x3 = XREG ? xh[XREG ? j : 0][4 * q + 3] : as_h2(xq.w);
-          d = __builtin_amdgcn_fdot2(as_h2(it.v[t][q].x), x0, d, false);
-          d = __builtin_amdgcn_fdot2(as_h2(it.v[t][q].y), x1, d, false);
-          d = __builtin_amdgcn_fdot2(as_h2(it.v[t][q].z), x2, d, false);
-          d = __builtin_amdgcn_fdot2(as_h2(it.v[t][q].w), x3, d, false);
+#pragma unroll
+          for (int tt = 0; tt < T; ++tt) {
+            const uint4 xq = it.x[XREG ? 0 : q];
+            const half2_t x0 = XREG ? xh[tt][XREG ? j : 0][4 * q + 0] : as_h2(xq.x);
+            const half2_t x1 = XREG ? xh[tt][XREG ? j : 0][4 * q + 1] : as_h2(xq.y);
+            const half2_t x2 = XREG ? xh[tt][XREG ? j : 0][4 * q + 2] : as_h2(xq.z);
+            const half2_t x3 = XREG ? xh[tt][XREG ? j : 0][4 * q + 3] : as_h2(xq.w);
+            d[tt] = __builtin_amdgcn_fdot2(as_h2(it.v[t][q].x), x0, d[tt], false);
+            d[tt] = __builtin_amdgcn_fdot2(as_h2(it.v[t][q].y), x1, d[tt], false);
+            d[tt] = __builtin_amdgcn_fdot2(as_h2(it.v[t][q].z), x2, d[tt], false);
+            d[tt] = __builtin_amdgcn_fdot2(as_h2(it.v[t][q].w), x3, d[tt], false);
+          }
         } else {
           const uint32_t hv[4] = {it.v[t][q].x, it.v[t][q].y, it.v[t][q].z, it.v[t][q].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            d = fmaf(h2f(hv[e] & 0xffffu), xf[XF16 ? 0 : j][8 * q + 2 * e], d);
-            d = fmaf(h2f(hv[e] >> 16), xf[XF16 ? 0 : j][8 * q + 2 * e + 1], d);
+            d[0] = fmaf(h2f(hv[e] & 0xffffu), xf[XF16 ? 0 : j][8 * q + 2 * e], d[0]);
+            d[0] = fmaf(h2f(hv[e] >> 16), xf[XF16 ? 0 : j][8 * q + 2 * e + 1], d[0]);
           }
         }
       }
-    return d;
   };
   // One row: CPL items (with PIPE the gathers of chunk j+1 are issued before
   // the dot products of chunk j), one fixed-order wave reduction.
   auto compute_row = [&](int r, const RowIdx &Rr) {
-    float acc = 0.f;
+    float acc[T];
+    auto add = [&](int j, const Item &it) {
+      float d[T];
+      dot(j, it, d);
+      const float sc = h2f(Rr.SC[j]);
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt) {
+        const float f = sc * fm[tt][j];
+        acc[tt] = j == 0 ? f * d[tt] : fmaf(f, d[tt], acc[tt]);
+      }
+    };
     if (PIPE) {
       Item ia, ib;
       gather(Rr, 0, ia);
@@ -293,22 +316,21 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
         sched_fence();
         if (j + 1 < CPL) gather(Rr, j + 1, (j & 1) ? ia : ib);
         sched_fence();
-        const float d = dot(j, (j & 1) ? ib : ia);
-        const float f = h2f(Rr.SC[j]) * fm[j];
-        acc = j == 0 ? f * d : fmaf(f, d, acc);
+        add(j, (j & 1) ? ib : ia);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         Item it;
         gather(Rr, j, it);
-        const float d = dot(j, it);
-        const float f = h2f(Rr.SC[j]) * fm[j];
-        acc = j == 0 ? f * d : fmaf(f, d, acc);
+        add(j, it);
       }
     }
-    const float tot = wave_sum(acc);
-    if (lane == 0) a.y[row0 + r * stride] = tot;
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt) {
+      const float tot = wave_sum(acc[tt]);
+      if (lane == 0) a.y[(size_t)tt * a.n + row0 + r * stride] = tot;
+    }
   };
 
   // Ring of D+1 row buffers: row r+D's index loads are issued before row r is
@@ -509,6 +531,64 @@ static void launch_gen_bits(const WView &w, const GemvArgs &a, int xt, int cus, 
   else if (g4) hipLaunchKernelGGL((k_gemv_gen<BITS, 4, false>), dim3(nwg), dim3(kGenWaves * 64), 0, s, a, xt);
   else if (xl) hipLaunchKernelGGL((k_gemv_gen<BITS, 1, true>), dim3(nwg), dim3(kGenWaves * 64), 0, s, a, xt);
   else hipLaunchKernelGGL((k_gemv_gen<BITS, 1, false>), dim3(nwg), dim3(kGenWaves * 64), 0, s, a, xt);
+}
+
+// 2..4 bf16 tokens in one launch of the LDS kernel: every gathered codebook
+// vector is multiplied with the x of all tokens (held in registers), so the
+// gathers, the LDS-bound part, are shared.  Rows of up to 3 chunks per lane
+// (K <= 6144), at most 6 chunks x tokens, codebooks and all tokens' x in the
+// LDS; other shapes take the matrix-core path.
+template <int S, int BITS, int CPL, int T>
+static bool launch_tokens_c(const GemvArgs &a, int cus, hipStream_t s) {
+  // chunks x tokens <= 6 keeps x in registers without spills at 256 VGPRs
+  if constexpr (CPL * T <= 6 && gemv_lds_bytes(S, BITS, CPL, true, T) <= kLdsBytes) {
+    const int g = (a.n + 7) / 8;
+    hipLaunchKernelGGL((k_gemv_lds<S, BITS, CPL, 8, true, 1, true, false, T>), dim3(g < cus ? g : cus), dim3(512), 0,
+                       s, a);
+    return true;
+  }
+  return false;
+}
+
+template <int S, int BITS, int T>
+static bool launch_tokens_t(const GemvArgs &a, int cus, hipStream_t s) {
+  switch ((a.C + 63) / 64) {
+    case 1: return launch_tokens_c<S, BITS, 1, T>(a, cus, s);
+    case 2: return launch_tokens_c<S, BITS, 2, T>(a, cus, s);
+    case 3: return launch_tokens_c<S, BITS, 3, T>(a, cus, s);
+    default: return false;
+  }
+}
+
+template <int S, int BITS>
+static bool launch_tokens_s(const GemvArgs &a, int batch, int cus, hipStream_t s) {
+  switch (batch) {
+    case 2: return launch_tokens_t<S, BITS, 2>(a, cus, s);
+    case 3: return launch_tokens_t<S, BITS, 3>(a, cus, s);
+    case 4: return launch_tokens_t<S, BITS, 4>(a, cus, s);
+    default: return false;
+  }
+}
+
+bool launch_gemv_tokens(const WView &w, const void *x, int batch, float *y, hipStream_t s, hipError_t *err) {
+  if (batch < 2 || batch > 4 || w.bits == 16 || w.k % 32 || w.bs % 32) return false;
+  if ((w.G / 4 + 63) / 64 > 3) return false;
+  GemvArgs a = make_args(w);
+  a.x = x;
+  a.y = y;
+  const int cus = device_cu_count();
+  bool done = false;
+  if (w.bits == 12) {
+    done = w.S == 1 ? launch_tokens_s<1, 12>(a, batch, cus, s) : w.S == 2 ? launch_tokens_s<2, 12>(a, batch, cus, s) : false;
+  } else {
+    switch (w.S) {
+      case 1: done = launch_tokens_s<1, 8>(a, batch, cus, s); break;
+      case 2: done = launch_tokens_s<2, 8>(a, batch, cus, s); break;
+      default: done = false; break;
+    }
+  }
+  if (done) *err = hipGetLastError();
+  return done;
 }
 
 hipError_t launch_gemv_token(const WView &w, const void *x, int xt, float *y, hipStream_t s) {

@@ -131,6 +131,8 @@ int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, f
   if (!aligned16(x) || !aligned16(y)) return VQ_ERR_ALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (batch > 1 && x_dtype == VQ_BF16) {
+    hipError_t e = hipSuccess;
+    if (launch_gemv_tokens(v, x, batch, y, s, &e)) return map_hip(e);
     return map_hip(launch_gemm(v, reinterpret_cast<const uint16_t *>(x), batch, y, s));
   }
   const size_t esz = x_dtype == VQ_F32 ? 4 : 2;

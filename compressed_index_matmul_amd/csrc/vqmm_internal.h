@@ -34,6 +34,9 @@ hipError_t launch_rht(const void *x, int xt, int batch, int n, const int8_t *sig
                       float *out, hipStream_t s);
 // One token of x (fp32 or bf16, VQ_F32 / VQ_BF16) against W: y[n].
 hipError_t launch_gemv_token(const WView &w, const void *x, int xt, float *y, hipStream_t s);
+// 2..4 bf16 tokens in one launch of the LDS decode kernel when the shape
+// allows it (false: not taken, nothing launched; *err set when taken).
+bool launch_gemv_tokens(const WView &w, const void *x, int batch, float *y, hipStream_t s, hipError_t *err);
 hipError_t launch_gemm(const WView &w, const uint16_t *x, int m, float *y, hipStream_t s);
 
 }  // namespace vqmm

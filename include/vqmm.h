@@ -128,8 +128,10 @@ int vq_unpack_dequant(const vq_weight *w, uint16_t *idx_out, uint16_t *w_out, vo
  * (bf16 x is held in fp16 after a power-of-two rescale per 32 columns, exact
  * for every value within 2^28 of the largest |x| of its 32), so every output
  * satisfies |y - y_exact| <= 2e-3 * sum_k |w x| + 1e-6.
- * 2..16 bf16 tokens: run on bf16 matrix cores as vq_gemm does, with the same
- * error behaviour.
+ * 2..4 bf16 tokens whose rows are short enough (k_in <= 6144, and the
+ * codebooks plus every token's x fit on chip) use the same exact fp16
+ * products, one launch for all tokens.  Other 2..16 bf16 tokens run on bf16
+ * matrix cores as vq_gemm does, with the same error behaviour.
  */
 int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, float *y,
             void *stream);

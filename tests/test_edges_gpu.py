@@ -78,6 +78,44 @@ def test_gemv_ragged(vq, shape, dtype, batch):
         assert_within(got, y_ref, bound, f"{shape} {dtype} B={batch}")
 
 
+@pytest.mark.parametrize("n,k,st,bits,bs,batch", [(300, 1024, 2, 12, 128, 2), (1000, 4096, 2, 12, 128, 3),
+                                                   (777, 6144, 1, 12, 64, 2), (513, 2080, 2, 8, 32, 4),
+                                                   (256, 4096, 2, 12, 4096, 4)])
+def test_gemv_tokens_lds(vq, n, k, st, bits, bs, batch):
+    """2-4 bf16 tokens on the LDS decode kernel (every gathered codebook
+    vector multiplied with each token's x): one to three chunks per lane,
+    a ragged last chunk set, ragged rows, 8- and 12-bit; the last shape does
+    not fit the LDS with four tokens and takes the matrix-core path."""
+    import torch
+    sw = vqsynth.random_weight(n, k, st, bits, bs, seed=n + k + batch)
+    xs, x64 = _x(batch, k, "bf16", 31 + n + batch)
+    y = vq.vq_gemv(device_weight(sw), x_to_device(xs, "bf16"))
+    torch.cuda.synchronize()
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
+    assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"{n}x{k} B={batch}")
+    if (k // 32 + 63) // 64 * batch <= 6 and not (st == 2 and bits == 12 and batch == 4 and k > 2048):
+        assert_within(y.cpu().numpy(), y_ref, bound, f"{n}x{k} B={batch} (exact fp16 products)")
+
+
+def test_gemv_tokens_lds_one_hot(vq):
+    """Each of three tokens is a different unit vector: the outputs are three
+    dequantized columns, exact up to fp32 rounding (fp16 products path)."""
+    import torch
+    n, k = 300, 1024
+    sw = vqsynth.random_weight(n, k, 2, 12, 128, seed=5)
+    cols = [0, 517, k - 1]
+    x64 = np.zeros((3, k))
+    for t, c in enumerate(cols):
+        x64[t, c] = 1.0
+    xs = (x64.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)  # 1.0 is exact in bf16
+    y = vq.vq_gemv(device_weight(sw), x_to_device(xs, "bf16"))
+    torch.cuda.synchronize()
+    w64 = oracle_w64(sw)
+    y_ref, bound = oracle.matmul_ref(w64, x64)
+    assert np.array_equal(y_ref, w64[:, cols].T)
+    assert_within(y.cpu().numpy(), y_ref, bound, "one-hot tokens")
+
+
 @pytest.mark.parametrize("batch", [2, 5, 16])
 def test_gemv_small_batch_mfma(vq, batch):
     import torch
