@@ -1080,30 +1080,39 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_small(GemmArgs a) {
 }
 
 // 1 <= m <= 64 tokens, K % 256 == 0, scale_block % 128 == 0, LDS codebooks
-// of 8/12-bit indices.  A unit is NB blocks of 16 W rows over a K range;
-// lane l decodes, per 32-column K step, group l / 16 of row l % 16 of each
-// block straight into a B fragment of v_mfma_f32_16x16x32_bf16 (no LDS round
-// trip) and multiplies it with the A fragments of TB blocks of 16 tokens
-// (lane l loads 8 x values of token l % 16 of each block).  A workgroup's
-// eight waves take its units times KP K parts; the KP partial tiles of a
-// unit are added in LDS in a fixed order at the end.  Index planes and the
-// scale (one per 128 columns at most) come four K steps at a time, x three
-// steps ahead, all as buffer loads with wave-uniform offsets.
-template <int S, int NB>
+// of 8/12-bit indices.  A unit is 16 W rows over a K range; lane l decodes,
+// per 32-column K step, group l / 16 of row l % 16 straight into a B fragment
+// of v_mfma_f32_16x16x32_bf16 (no LDS round trip) and multiplies it with the
+// A fragments of TB blocks of 16 tokens (lane l loads 8 x values of token
+// l % 16 of each block).  A workgroup's eight waves take its units times KP K
+// parts; the KP partial tiles of a unit are added in LDS in a fixed order at
+// the end.
+// Index bytes: the four lanes of a row need the same 16 bytes per four
+// steps, so instead of four identical loads each wave stages its rows' bytes
+// for eight steps (two quads of low bytes, one 16-byte run of high nibbles
+// per stage) into a two-slot LDS ring with LDS-direct loads, one unique
+// 16-byte piece per lane, a trip ahead, and reads them back (a broadcast LDS
+// read per row).  x is loaded three steps ahead; the scale (one per 128
+// columns at most) once per quad, a trip ahead.
+template <int S, int BITS>
 struct FewQuad {
-  uint4 lo[NB][S];
-  uint2 hi[NB][S];
-  uint32_t sc[NB];  // fp16 scale of the lane's row in each block
+  uint4 lo[S];
+  uint2 hi[S];
+  uint32_t sc;  // fp16 scale of the lane's row
 };
 template <int TB>
 struct FewStep {
   uint4 av[TB];  // A fragments of the token blocks
 };
 
-template <int S, int BITS, int NB, int TB>
+template <int S, int BITS, int TB>
 __global__ __launch_bounds__(kSWaves * 64) void k_gemm_few(GemmArgs a, int units_per_wg, int kp) {
+  constexpr int HI = BITS == 12 ? 1 : 0;
+  constexpr int SLOT = (2 + HI) * S * 16;  // uint4 per wave and slot: 2 lo quads (+ hi pair) x S stages x 16 rows
+  constexpr int RED = (kSWaves * 16 * 17 * 4 + 15) / 16;  // uint4 of the final reduction (aliases the ring)
+  constexpr int STAGE = kSWaves * 2 * SLOT > RED ? kSWaves * 2 * SLOT : RED;
   __shared__ uint4 s_cb[S << BITS];
-  __shared__ float s_red[kSWaves][NB][16][17];
+  __shared__ uint4 s_stage[STAGE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
@@ -1117,9 +1126,10 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_few(GemmArgs a, int units
                       s_cb + blk);
     }
   }
-  const int units = (a.n + 16 * NB - 1) / (16 * NB);
+  const int units = (a.n + 15) / 16;
   const int nks = a.G / 4;
   const int steps = nks / kp;        // K steps per part (a multiple of 8)
+  const int trips = steps / 8;
   const int ui = wave / kp;          // unit slot of this wave in the workgroup
   const int part = wave % kp;
   const int unit = blockIdx.x * units_per_wg + ui;
@@ -1127,48 +1137,65 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_few(GemmArgs a, int units
   const int r16 = lane & 15;
   const int q = lane >> 4;           // k chunk of the lane within a K step
   const int ks0 = part * steps;
+  const int row = min((active ? unit : 0) * 16 + r16, a.n - 1);
 
-  const uint32_t ng = (uint32_t)a.n * a.G;
-  buf_t blo[S], bhi[S];
-#pragma unroll
-  for (int t = 0; t < S; ++t) {
-    blo[t] = make_buf(a.lo[t], ng);
-    bhi[t] = make_buf(BITS == 12 ? a.hi[t] : a.lo[t], BITS == 12 ? (ng + 1) / 2 : ng);
-  }
   const buf_t bsc = make_buf(a.sc, 2u * a.n * a.nblk);
   const buf_t bx = make_buf(a.x, 2u * a.m * a.k);
-  uint32_t vlo[NB], vsc[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int row = min((active ? unit : 0) * 16 * NB + 16 * b + r16, a.n - 1);
-    vlo[b] = (uint32_t)row * a.G;
-    vsc[b] = 2u * row * a.nblk;
-  }
+  const uint32_t vsc = 2u * row * a.nblk;
   uint32_t vx[TB];
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
     const int tok = min(16 * tb + r16, a.m - 1);  // tokens past m only feed unstored outputs
     vx[tb] = 2u * ((uint32_t)tok * a.k + 8 * q);
   }
+  // staging source of this lane: row r16, stage q (lanes q < S take part)
+  const int sq = q < S ? q : 0;
+  const uint8_t *src_lo = a.lo[0], *src_hi = BITS == 12 ? a.hi[0] : a.lo[0];
+#pragma unroll
+  for (int t = 1; t < S; ++t)
+    if (sq == t) {
+      src_lo = a.lo[t];
+      if (BITS == 12) src_hi = a.hi[t];
+    }
+  src_lo += (size_t)row * a.G;
+  if (BITS == 12) src_hi += ((size_t)row * a.G) >> 1;
 
-  f32x4 acc[TB][NB];
+  f32x4 acc[TB];
 #pragma unroll
-  for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[tb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // loads of quad / step index i of this part, clamped to its last one
-  auto load_quad = [&](int j, FewQuad<S, NB> &Q) {
-    j = ks0 / 4 + min(j, steps / 4 - 1);
-    const uint32_t blk = (uint32_t)(((uint64_t)(4 * j) * a.smagic) >> 32);  // (128 j) / scale_block
+  // stage the index bytes of trip i (quads 2i, 2i+1 of this part, clamped)
+  // into slot i & 1 of this wave's ring
+  auto stage = [&](int i) {
+    uint4 *base = s_stage + (wave * 2 + (i & 1)) * SLOT;
+    const int j0 = ks0 / 4 + min(2 * i, steps / 4 - 2);  // first quad (trips hold two)
+    if (q < S) {
+      lds_direct_16(src_lo + 16 * j0, base);
+      lds_direct_16(src_lo + 16 * (j0 + 1), base + S * 16);
+      if (BITS == 12) lds_direct_16(src_hi + 8 * j0, base + 2 * S * 16);
+    }
+  };
+  constexpr int kStageLoads = 2 + HI;
+  auto load_sc = [&](int i, uint32_t (&sc)[2]) {
+    const int j0 = ks0 / 4 + min(2 * i, steps / 4 - 2);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t blk = (uint32_t)(((uint64_t)(4 * (j0 + h)) * a.smagic) >> 32);  // (128 j) / scale_block
+      sc[h] = buf_u16(bsc, vsc, 2u * blk);
+    }
+  };
+  // the staged bytes of trip i: this lane's row, every stage
+  auto read_trip = [&](int i, FewQuad<S, BITS> &Q0, FewQuad<S, BITS> &Q1) {
+    const uint4 *base = s_stage + (wave * 2 + (i & 1)) * SLOT;
 #pragma unroll
-      for (int t = 0; t < S; ++t) {
-        Q.lo[b][t] = buf_u128(blo[t], vlo[b], 16u * j);
-        if (BITS == 12) Q.hi[b][t] = buf_u64(bhi[t], vlo[b] >> 1, 8u * j);
+    for (int t = 0; t < S; ++t) {
+      Q0.lo[t] = base[t * 16 + r16];
+      Q1.lo[t] = base[S * 16 + t * 16 + r16];
+      if (BITS == 12) {
+        const uint4 h = base[2 * S * 16 + t * 16 + r16];
+        Q0.hi[t] = make_uint2(h.x, h.y);
+        Q1.hi[t] = make_uint2(h.z, h.w);
       }
-      Q.sc[b] = buf_u16(bsc, vsc[b], 2u * blk);
     }
   };
   auto load_step = [&](int i, FewStep<TB> &X) {
@@ -1176,85 +1203,103 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_few(GemmArgs a, int units
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) X.av[tb] = buf_u128(bx, vx[tb], 64u * ks);
   };
-  // decode the lane's group of each block in step s (0..3) of quad Q and
-  // multiply with every token block
-  auto step = [&](const FewQuad<S, NB> &Q, int s, const FewStep<TB> &X) {
-    uint4 v[NB][S];
+  // decode the lane's group in step s (0..3) of quad Q and multiply with
+  // every token block
+  auto step = [&](const FewQuad<S, BITS> &Q, int s, const FewStep<TB> &X) {
+    uint4 v[S];
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int t = 0; t < S; ++t) {
-        const uint4 lw4 = Q.lo[b][t];
-        const uint32_t lw = s == 0 ? lw4.x : s == 1 ? lw4.y : s == 2 ? lw4.z : lw4.w;
-        uint32_t idx = (lw >> (8 * q)) & 0xffu;
-        if (BITS == 12) {
-          const uint32_t hw = s < 2 ? Q.hi[b][t].x : Q.hi[b][t].y;
-          idx |= ((hw >> (4 * (4 * (s & 1) + q))) & 0xfu) << 8;
-        }
-        v[b][t] = s_cb[(t << BITS) + idx];
+    for (int t = 0; t < S; ++t) {
+      const uint4 lw4 = Q.lo[t];
+      const uint32_t lw = s == 0 ? lw4.x : s == 1 ? lw4.y : s == 2 ? lw4.z : lw4.w;
+      uint32_t idx = (lw >> (8 * q)) & 0xffu;
+      if (BITS == 12) {
+        const uint32_t hw = s < 2 ? Q.hi[t].x : Q.hi[t].y;
+        idx |= ((hw >> (4 * (4 * (s & 1) + q))) & 0xfu) << 8;
       }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, group_to_bf16<S>(v[b], h2f(Q.sc[b])));
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
-        acc[tb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, X.av[tb]), bfr,
-                                                              acc[tb][b], 0, 0, 0);
+      v[t] = s_cb[(t << BITS) + idx];
     }
+    const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, group_to_bf16<S>(v, h2f(Q.sc)));
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+      acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, X.av[tb]), bfr, acc[tb], 0, 0, 0);
   };
 
-  FewQuad<S, NB> Q0, Q1;
+  FewQuad<S, BITS> Q0, Q1;
   FewStep<TB> X0, X1, X2, X3;
-  load_quad(0, Q0);
-  load_quad(1, Q1);
-  load_step(0, X0);
-  load_step(1, X1);
-  load_step(2, X2);
-  wait_all_memory();  // codebook (LDS-direct) has landed
+  uint32_t nsc[2];
+  if (active) {
+    stage(0);
+    load_sc(0, nsc);
+    load_step(0, X0);
+    load_step(1, X1);
+    load_step(2, X2);
+  }
+  wait_all_memory();  // codebook (LDS-direct) and trip 0 have landed
   __syncthreads();
-  if (active) {  // wave-uniform; every wave reaches the barriers below
-    // eight steps per trip (two quads); steps ahead: 3 (x), 4-8 (quads)
-    for (int i = 0; i < steps; i += 8) {
-      load_step(i + 3, X3);
+  if (active) {  // wave-uniform
+    // one trip (two quads, eight steps) per iteration: trip i+1 is staged
+    // and its scales loaded first.  Loads complete in issue order, and the
+    // loads issued after trip i's staging are trip i's two scale loads, the
+    // 8 TB x loads of iteration i-1 and the staging and scales of trip i+1:
+    // waiting until at most that many are outstanding means trip i landed
+    for (int i = 0; i < trips; ++i) {
+      Q0.sc = nsc[0];
+      Q1.sc = nsc[1];
+      if (i + 1 < trips) {
+        stage(i + 1);
+        load_sc(i + 1, nsc);
+      }
+      sched_fence();
+      // (the last trip stages nothing more, so fewer loads follow its own)
+      constexpr int kAfter = 2 + 8 * TB + kStageLoads + 2;
+      constexpr int kAfterLast = 2 + 8 * TB;
+      if (i + 1 < trips) {
+        if (i > 0) wait_vmem<(kAfter < 63 ? kAfter : 63)>();
+      } else if (i > 0) {
+        wait_vmem<(kAfterLast < 63 ? kAfterLast : 63)>();
+      }
+      read_trip(i, Q0, Q1);
+      sched_fence();
+      const int k = 8 * i;
+      load_step(k + 3, X3);
       step(Q0, 0, X0);
-      load_step(i + 4, X0);
+      load_step(k + 4, X0);
       step(Q0, 1, X1);
-      load_step(i + 5, X1);
+      load_step(k + 5, X1);
       step(Q0, 2, X2);
-      load_step(i + 6, X2);
+      load_step(k + 6, X2);
       step(Q0, 3, X3);
-      load_quad(i / 4 + 2, Q0);
-      load_step(i + 7, X3);
+      load_step(k + 7, X3);
       step(Q1, 0, X0);
-      load_step(i + 8, X0);
+      load_step(k + 8, X0);
       step(Q1, 1, X1);
-      load_step(i + 9, X1);
+      load_step(k + 9, X1);
       step(Q1, 2, X2);
-      load_step(i + 10, X2);
+      load_step(k + 10, X2);
       step(Q1, 3, X3);
-      load_quad(i / 4 + 3, Q1);
     }
   }
-  // per token block: lane holds D[token 4 (lane / 16) + r][row lane % 16] of
-  // each W block; part 0 of each unit adds the KP parts in order
+  // every staged load has landed and every wave has left its ring before the
+  // ring holds the reduction
+  wait_all_memory();
+  __syncthreads();
+  float (*s_red)[16][17] = reinterpret_cast<float (*)[16][17]>(s_stage);
+  // per token block: lane holds D[token 4 (lane / 16) + r][row lane % 16];
+  // part 0 of each unit adds the KP parts in order
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s_red[wave][b][4 * (lane >> 4) + r][lane & 15] = acc[tb][b][r];
+    for (int r = 0; r < 4; ++r) s_red[wave][4 * (lane >> 4) + r][lane & 15] = acc[tb][r];
     __syncthreads();
     if (active && part == 0) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int ti = 16 * tb + 4 * (lane >> 4) + r;
-          float sum = 0.f;
-          for (int h = 0; h < kp; ++h) sum += s_red[wave + h][b][4 * (lane >> 4) + r][lane & 15];
-          const int col = unit * 16 * NB + 16 * b + (lane & 15);
-          if (ti < a.m && col < a.n) a.y[(size_t)ti * a.n + col] = sum;
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int ti = 16 * tb + 4 * (lane >> 4) + r;
+        float sum = 0.f;
+        for (int h = 0; h < kp; ++h) sum += s_red[wave + h][4 * (lane >> 4) + r][lane & 15];
+        const int col = unit * 16 + (lane & 15);
+        if (ti < a.m && col < a.n) a.y[(size_t)ti * a.n + col] = sum;
+      }
     }
     __syncthreads();
   }
@@ -1334,13 +1379,13 @@ static GemmArgs make_gemm_args(const WView &w, const uint16_t *x, int m, float *
   return a;
 }
 
-// The few-token unit kernel with NB row blocks per unit and TB token blocks;
-// false when the shape leaves it fewer units than half the CUs (the slab
-// and tile kernels spread such shapes better).
-template <int S, int BITS, int NB>
-static bool launch_few_nb(const GemmArgs &a, hipStream_t s) {
+// The few-token unit kernel with TB token blocks; false when the shape
+// leaves it fewer units than half the CUs (the slab and tile kernels spread
+// such shapes better).
+template <int S, int BITS>
+static bool launch_few(const GemmArgs &a, hipStream_t s) {
   const int cus = device_cu_count();
-  const int units = (a.n + 16 * NB - 1) / (16 * NB);
+  const int units = (a.n + 15) / 16;
   if (2 * units < cus) return false;
   const int grid = units < cus ? units : cus;
   const int upw = (units + grid - 1) / grid;
@@ -1351,10 +1396,10 @@ static bool launch_few_nb(const GemmArgs &a, hipStream_t s) {
   while (kp * 2 * upw <= kSWaves && nks % (kp * 2 * 8) == 0) kp *= 2;
   if (upw * kp > kSWaves) return false;
   switch ((a.m + 15) / 16) {
-    case 1: hipLaunchKernelGGL((k_gemm_few<S, BITS, NB, 1>), dim3(grid), dim3(kSWaves * 64), 0, s, a, upw, kp); break;
-    case 2: hipLaunchKernelGGL((k_gemm_few<S, BITS, NB, 2>), dim3(grid), dim3(kSWaves * 64), 0, s, a, upw, kp); break;
-    case 3: hipLaunchKernelGGL((k_gemm_few<S, BITS, NB, 3>), dim3(grid), dim3(kSWaves * 64), 0, s, a, upw, kp); break;
-    default: hipLaunchKernelGGL((k_gemm_few<S, BITS, NB, 4>), dim3(grid), dim3(kSWaves * 64), 0, s, a, upw, kp); break;
+    case 1: hipLaunchKernelGGL((k_gemm_few<S, BITS, 1>), dim3(grid), dim3(kSWaves * 64), 0, s, a, upw, kp); break;
+    case 2: hipLaunchKernelGGL((k_gemm_few<S, BITS, 2>), dim3(grid), dim3(kSWaves * 64), 0, s, a, upw, kp); break;
+    case 3: hipLaunchKernelGGL((k_gemm_few<S, BITS, 3>), dim3(grid), dim3(kSWaves * 64), 0, s, a, upw, kp); break;
+    default: hipLaunchKernelGGL((k_gemm_few<S, BITS, 4>), dim3(grid), dim3(kSWaves * 64), 0, s, a, upw, kp); break;
   }
   return true;
 }
@@ -1364,12 +1409,9 @@ static void launch_gemm_sb(const GemmArgs &a0, hipStream_t s) {
   GemmArgs a = a0;
   if constexpr (CB_LDS && BITS != 16) {
     // 1..64 tokens: the unit kernel (whole eight-step trips per K part, one
-    // scale per 128 columns at most); two row blocks per unit for one token
-    // block once there are enough units for every CU (more token blocks with
-    // two row blocks would not fit the 256 registers of two waves per SIMD)
+    // scale per 128 columns at most)
     if (a.m <= 64 && a.k % 256 == 0 && a.bs % 128 == 0 && a.k < (1 << 20)) {
-      const bool two = a.m <= 16 && (a.n + 31) / 32 >= device_cu_count();
-      if (two ? launch_few_nb<S, BITS, 2>(a, s) : launch_few_nb<S, BITS, 1>(a, s)) return;
+      if (launch_few<S, BITS>(a, s)) return;
     }
   }
   if (a.m <= 16) {
