@@ -573,14 +573,13 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
       acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[jn], acc[i][jn], 0, 0, 0);
   };
   // Iteration ks: B fragments of step ks+1 into Bn (tile (ks+1) % 3), MFMAs
-  // of step ks (Xm, Bc), decode of step ks+2 (quad Qd, step sd, scale in Xd)
-  // into tile (ks+2) % 3, loads of step ks+4 into Xm (and, when ks % 4 == 2,
-  // of quad (ks+6)/4 into Qn), barrier.
+  // of step ks (Xm, Bc), decode of step ks+2 (codebook vectors in v, gathered
+  // one iteration earlier; scale in Xd) into tile (ks+2) % 3, gathers of step
+  // ks+3 (quad Qg, step sg) into v, loads of step ks+4 into Xm (and, when
+  // ks % 4 == 2, of quad (ks+6)/4 into Qn), barrier.
   auto iter = [&](int ks, XStep &Xm, const XStep &Xd, const bf16x8_t (&Bc)[8], bf16x8_t (&Bn)[8],
-                  const Quad<S> &Qd, int sd, Quad<S> &Qn, bool quad_load) {
+                  const Quad<S> &Qg, int sg, Quad<S> &Qn, bool quad_load, uint4 (&v)[2][S]) {
     uint16_t *ww = s_w[(ks + 2) % 3];
-    uint4 v[2][S];
-    gather(Qd, sd, v);
     read_b(s_w[(ks + 1) % 3], Bn);
     sched_fence();
     // 32 MFMAs with the decode's vector work between them: one MFMA, then
@@ -589,6 +588,7 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
     decode(0, v[0], Xd.sc, ww);
     mma8(Xm, Bc, 1);
     decode(1, v[1], Xd.sc, ww);
+    gather(Qg, sg, v);
     mma8(Xm, Bc, 2);
     mma8(Xm, Bc, 3);
 #pragma unroll
@@ -612,15 +612,14 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
   load_x(3, X3);
   wait_all_memory();  // codebook (LDS-direct) has landed (and the first steps)
   __syncthreads();
-  {
-    uint4 v[2][S];
-    gather(Q0, 0, v);
-    decode(0, v[0], X0.sc, s_w[0]);
-    decode(1, v[1], X0.sc, s_w[0]);
-    gather(Q0, 1, v);
-    decode(0, v[0], X1.sc, s_w[1]);
-    decode(1, v[1], X1.sc, s_w[1]);
-  }
+  uint4 v[2][S];
+  gather(Q0, 0, v);
+  decode(0, v[0], X0.sc, s_w[0]);
+  decode(1, v[1], X0.sc, s_w[0]);
+  gather(Q0, 1, v);
+  decode(0, v[0], X1.sc, s_w[1]);
+  decode(1, v[1], X1.sc, s_w[1]);
+  gather(Q0, 2, v);  // step 2, decoded in iteration 0
   __syncthreads();
   bf16x8_t B0[8], B1[8];
   read_b(s_w[0], B0);
@@ -628,14 +627,17 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
   // (compile-time inside the trip only when 3 divides the trip length, so the
   // tile index is computed at run time); quads alternate between Q0 and Q1
   for (int ks = 0; ks < nks; ks += 8) {
-    iter(ks + 0, X0, X2, B0, B1, Q0, 2, Q1, false);
-    iter(ks + 1, X1, X3, B1, B0, Q0, 3, Q1, false);
-    iter(ks + 2, X2, X0, B0, B1, Q1, 0, Q0, true);   // quad (ks+8)/4 -> Q0
-    iter(ks + 3, X3, X1, B1, B0, Q1, 1, Q0, false);
-    iter(ks + 4, X0, X2, B0, B1, Q1, 2, Q0, false);
-    iter(ks + 5, X1, X3, B1, B0, Q1, 3, Q0, false);
-    iter(ks + 6, X2, X0, B0, B1, Q0, 0, Q1, true);   // quad (ks+12)/4 -> Q1
-    iter(ks + 7, X3, X1, B1, B0, Q0, 1, Q1, false);
+    // iteration ks+i gathers step ks+i+3: Q0 is last read in iteration ks
+    // and refilled in ks+2 (first read in ks+5); Q1 is last read in ks+4
+    // and refilled in ks+6 (first read in ks+9)
+    iter(ks + 0, X0, X2, B0, B1, Q0, 3, Q1, false, v);
+    iter(ks + 1, X1, X3, B1, B0, Q1, 0, Q1, false, v);
+    iter(ks + 2, X2, X0, B0, B1, Q1, 1, Q0, true, v);   // quad (ks+8)/4 -> Q0
+    iter(ks + 3, X3, X1, B1, B0, Q1, 2, Q0, false, v);
+    iter(ks + 4, X0, X2, B0, B1, Q1, 3, Q0, false, v);
+    iter(ks + 5, X1, X3, B1, B0, Q0, 0, Q1, false, v);
+    iter(ks + 6, X2, X0, B0, B1, Q0, 1, Q1, true, v);   // quad (ks+12)/4 -> Q1
+    iter(ks + 7, X3, X1, B1, B0, Q0, 2, Q1, false, v);
   }
   // tiles wholly inside y: descriptor stores as in the wide kernel
   if (m0 + kLM <= a.m && n0 + kLN <= a.n && (uint64_t)kLM * a.n * 4 < (1u << 31)) {
