@@ -14,7 +14,11 @@ from the two source pages:
   Hadamard transform = random sign flips followed by a fast Walsh-Hadamard
   transform; block-diagonal for large layers) and "Bit widths" (non-power-of-2
   sizes use a block-diagonal FHT built from power-of-2 blocks; 16-bit indices
-  into a 65,536-entry codebook).
+  into a 65,536-entry codebook; higher rates stack 8- or 16-bit residual
+  stages on a 16-bit primary), and the two-stage call of "Inference kernels",
+  which passes an inverse residual scale.
+* orka README, quick start: the ``rvq-12-4`` quant mode (a 12-bit primary
+  stage and a 4-bit residual stage, about 2 bits per weight).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
 leg may import this package.  It shares no code with the HIP library and
@@ -30,7 +34,7 @@ reading taken is stated in the docstring.
 from __future__ import annotations
 
 import math
-from typing import Sequence
+from typing import Optional, Sequence, Union
 
 import numpy as np
 
@@ -76,13 +80,19 @@ def unpack_indices(bits: int, n_groups: int, lo=None, hi=None, idx16=None) -> np
       the high nibble when ``f`` is odd;
     * an 8-bit index is the ``lo`` plane alone;
     * a 16-bit index (GLQ "How it works": one 16-bit index per 8 weights into
-      a 65,536-entry codebook) is a little-endian uint16 array ``idx16``.
+      a 65,536-entry codebook) is a little-endian uint16 array ``idx16``;
+    * a 4-bit index (the residual stage of orka's ``rvq-12-4`` mode) is one
+      nibble plane ``hi``, packed exactly like the 12-bit high plane, so a
+      12-bit index is an 8-bit ``lo`` plane plus a 4-bit plane shifted up by 8.
 
     Groups are numbered row-major: group ``g`` of output row ``r`` is
     ``f = r * (K // 8) + g``.
     """
     out = np.empty(n_groups, dtype=np.int64)
-    if bits == 8:
+    if bits == 4:
+        hib = np.asarray(hi, dtype=np.uint8)[np.arange(n_groups) // 2].astype(np.int64)
+        out[:] = np.where(np.arange(n_groups) % 2 == 0, hib & 0xF, (hib >> 4) & 0xF)
+    elif bits == 8:
         out[:] = np.asarray(lo, dtype=np.uint8)[:n_groups].astype(np.int64)
     elif bits == 12:
         lo = np.asarray(lo, dtype=np.uint8)
@@ -105,9 +115,10 @@ def unpack_indices(bits: int, n_groups: int, lo=None, hi=None, idx16=None) -> np
 def pack_indices(idx: Sequence[int], bits: int):
     """Inverse of :func:`unpack_indices` (used to build structured test inputs).
 
-    Returns ``(lo, hi)`` for 8/12-bit (``hi`` is None for 8-bit) or
-    ``(idx16, None)`` for 16-bit.  For an odd number of 12-bit groups the
-    unused high nibble of the last ``hi`` byte is zero.
+    Returns ``(lo, hi)`` for 8/12-bit (``hi`` is None for 8-bit),
+    ``(None, hi)`` for 4-bit, or ``(idx16, None)`` for 16-bit.  For an odd
+    number of 4/12-bit groups the unused high nibble of the last ``hi`` byte
+    is zero.
     """
     idx = np.asarray(idx, dtype=np.int64)
     if idx.size and (idx.min() < 0 or idx.max() >= (1 << bits)):
@@ -116,14 +127,15 @@ def pack_indices(idx: Sequence[int], bits: int):
         return idx.astype(np.uint8), None
     if bits == 16:
         return idx.astype(np.uint16), None
-    if bits != 12:
+    if bits not in (4, 12):
         raise ValueError(f"unsupported index width {bits}")
     n = idx.size
-    lo = (idx % 256).astype(np.uint8)
     nib = np.zeros(2 * ((n + 1) // 2), dtype=np.int64)
-    nib[:n] = idx // 256
+    nib[:n] = idx // 256 if bits == 12 else idx
     hi = (nib[0::2] + 16 * nib[1::2]).astype(np.uint8)   # even group -> low nibble
-    return lo, hi
+    if bits == 4:
+        return None, hi
+    return (idx % 256).astype(np.uint8), hi
 
 
 # --------------------------------------------------------------------------
@@ -138,8 +150,8 @@ def n_scale_blocks(k_in: int, scale_block: int) -> int:
 
 def dequant_exact(n_out: int, k_in: int, indices: Sequence[np.ndarray],
                   codebooks: Sequence[np.ndarray], scales: np.ndarray,
-                  scale_block: int) -> np.ndarray:
-    """Exact dequantized weight, float64, shape ``[n_out, k_in]``.
+                  scale_block: int, stage_scales: Optional[Sequence[float]] = None) -> np.ndarray:
+    """Dequantized weight, float64, shape ``[n_out, k_in]``.
 
     orka README, "How it works": a group decodes to the scale times the sum of
     its codebook entries; with residual stages t = 0..S-1 (orka's RVQ, GLQ
@@ -148,21 +160,44 @@ def dequant_exact(n_out: int, k_in: int, indices: Sequence[np.ndarray],
         w[r, 8g + j] = s[r, (8g) // scale_block] * sum_t cb_t[idx_t[r, g], j].
 
     Readings: the scale multiplies the stage sum; one block scale is shared by
-    all stages; there is no separate residual scale.  All values are fp16, so
-    the sum of at most four of them and its product with an fp16 scale are
-    exact in float64 -- the result does not depend on summation order (the
-    sign of an exact zero included: it is -0 only when every term is -0).
+    all stages.  All values are fp16, so the sum of at most four of them and
+    its product with an fp16 scale are exact in float64 -- the result does not
+    depend on summation order (the sign of an exact zero included: it is -0
+    only when every term is -0).
+
+    ``stage_scales`` (optional, one float32 per stage) is the residual scale
+    of GLQ's two-stage call ("Inference kernels": an inverse residual scale)
+    and of its stacked trellis stages (a residual scale fitted per layer):
+
+        w[r, 8g + j] = s[r, blk] * sum_t r_t * cb_t[idx_t[r, g], j].
+
+    Readings: one scalar per stage per tensor, multiplying that stage's
+    codebook entry, any stage (the primary included) may carry one, and
+    omitting them means r_t = 1.  With them the value is no longer exact in
+    float64 in general, so it is defined by this evaluation order: each
+    product r_t * c_t (exact in float64: 24 + 11 significant bits), summed in
+    stage order starting from stage 0's product, each addition rounded to
+    float64, then one float64 multiplication by the block scale.  With every
+    r_t = 1 this is the exact value above, bit for bit.
     """
     if k_in % GROUP:
         raise ValueError("k_in must be a multiple of 8")
     g_per_row = k_in // GROUP
     s = np.asarray(scales, dtype=np.float16).astype(np.float64).reshape(n_out, -1)
+    if stage_scales is not None:
+        rs = np.asarray(stage_scales, dtype=np.float32).astype(np.float64)
+        if rs.size < len(codebooks):
+            raise ValueError("one stage scale per stage")
+        if not np.all(np.isfinite(rs)):
+            raise ValueError("stage scales must be finite")
     acc = None
-    for idx, cb in zip(indices, codebooks):
+    for t, (idx, cb) in enumerate(zip(indices, codebooks)):
         cb64 = np.asarray(cb, dtype=np.float16).astype(np.float64).reshape(-1, GROUP)
         ix = np.asarray(idx, dtype=np.int64).reshape(n_out, g_per_row)
         term = cb64[ix]
-        # The sum starts from stage 0's entry itself (not from +0), so a lone
+        if stage_scales is not None:
+            term = rs[t] * term          # exact: 24-bit times 11-bit significand
+        # The sum starts from stage 0's term itself (not from +0), so a lone
         # -0.0 entry stays -0.0; an exact zero sum of mixed-sign terms is +0.
         acc = term if acc is None else acc + term
     if acc is None:
@@ -174,16 +209,19 @@ def dequant_exact(n_out: int, k_in: int, indices: Sequence[np.ndarray],
     return w
 
 
-def dequant_fp16(n_out, k_in, indices, codebooks, scales, scale_block) -> np.ndarray:
-    """fp16 dequantized weight: the exact value rounded once to nearest-even.
+def dequant_fp16(n_out, k_in, indices, codebooks, scales, scale_block,
+                 stage_scales=None) -> np.ndarray:
+    """fp16 dequantized weight: the float64 value rounded once to nearest-even.
 
-    Reading: the pages fix no rounding; the result is the exact float64 value
-    of :func:`dequant_exact` converted once to IEEE binary16 with
+    Reading: the pages fix no rounding; the result is the float64 value of
+    :func:`dequant_exact` (exact without stage scales, the stated evaluation
+    order with them) converted once to IEEE binary16 with
     round-to-nearest-even (numpy's float64 -> float16 cast rounds once; the
     tests check it against Python's own half-float packing).  Subnormals are
     kept, overflow gives +/-inf, a zero result keeps the sign IEEE gives it.
     """
-    return dequant_exact(n_out, k_in, indices, codebooks, scales, scale_block).astype(np.float16)
+    return dequant_exact(n_out, k_in, indices, codebooks, scales, scale_block,
+                         stage_scales).astype(np.float16)
 
 
 # --------------------------------------------------------------------------
@@ -289,33 +327,43 @@ def rht_ref(x: np.ndarray, signs: np.ndarray, max_block: int) -> np.ndarray:
 # c-5  storage cost
 # --------------------------------------------------------------------------
 
-def compressed_bytes(n_out: int, k_in: int, n_stages: int, bits: int, scale_block: int,
-                     include_codebooks: bool = True) -> int:
+def _stage_widths(n_stages: int, bits) -> list:
+    if isinstance(bits, (int, np.integer)):
+        widths = [int(bits)] * n_stages
+    else:
+        widths = [int(b) for b in bits]
+        if len(widths) != n_stages:
+            raise ValueError("one index width per stage")
+    for b in widths:
+        if b not in (4, 8, 12, 16):
+            raise ValueError(f"unsupported index width {b}")
+    return widths
+
+
+def compressed_bytes(n_out: int, k_in: int, n_stages: int, bits: Union[int, Sequence[int]],
+                     scale_block: int, include_codebooks: bool = True) -> int:
     """Bytes of the stored weight: index planes, fp16 scales and (optionally)
     the fp16 codebooks, each counted once.
 
-    Per stage: 12-bit = one byte per group plus one byte per two groups
-    (ceil), 8-bit = one byte per group, 16-bit = two bytes per group.
+    ``bits`` is one index width for every stage or a list of per-stage widths
+    (GLQ "Bit widths": a 16-bit primary with 8- or 16-bit residual stages;
+    orka's ``rvq-12-4``: 12 then 4).  Per stage: 16-bit = two bytes per
+    group, 12-bit = one byte per group plus one byte per two groups (ceil),
+    8-bit = one byte per group, 4-bit = one byte per two groups (ceil).
     """
     groups = n_out * (k_in // GROUP)
-    if bits == 8:
-        per_stage = groups
-    elif bits == 12:
-        per_stage = groups + (groups + 1) // 2
-    elif bits == 16:
-        per_stage = 2 * groups
-    else:
-        raise ValueError(f"unsupported index width {bits}")
-    total = n_stages * per_stage + 2 * n_out * n_scale_blocks(k_in, scale_block)
+    per_width = {4: (groups + 1) // 2, 8: groups, 12: groups + (groups + 1) // 2, 16: 2 * groups}
+    widths = _stage_widths(n_stages, bits)
+    total = sum(per_width[b] for b in widths) + 2 * n_out * n_scale_blocks(k_in, scale_block)
     if include_codebooks:
-        total += n_stages * (1 << bits) * GROUP * 2
+        total += sum((1 << b) * GROUP * 2 for b in widths)
     return total
 
 
-def bits_per_weight(n_out: int, k_in: int, n_stages: int, bits: int, scale_block: int,
-                    include_codebooks: bool = False) -> float:
-    """Stored bits per weight: S*b/8 for the indices (12 bits per 8 weights is
-    1.5 per stage) plus 16 bits per scale block, plus optionally the
-    codebooks spread over the tensor."""
+def bits_per_weight(n_out: int, k_in: int, n_stages: int, bits: Union[int, Sequence[int]],
+                    scale_block: int, include_codebooks: bool = False) -> float:
+    """Stored bits per weight: b/8 per stage for the indices (12 bits per 8
+    weights is 1.5 per stage) plus 16 bits per scale block, plus optionally
+    the codebooks spread over the tensor."""
     return 8.0 * compressed_bytes(n_out, k_in, n_stages, bits, scale_block,
                                   include_codebooks) / (n_out * k_in)

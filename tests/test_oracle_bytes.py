@@ -48,3 +48,34 @@ def test_bits_per_weight():
 def test_odd_group_count_pads_a_nibble():
     # 3 groups of 12-bit: 3 lo bytes + 2 hi bytes
     assert oracle.compressed_bytes(1, 24, 1, 12, 24, include_codebooks=False) == 3 + 2 + 2
+
+
+def test_rvq_12_4_is_two_bits_per_weight():
+    """orka README quick start: the rvq-12-4 mode gives about 2 bits per
+    weight -- 12 + 4 index bits per group of 8 weights, plus the scales."""
+    assert oracle.bits_per_weight(576, 576, 2, [12, 4], 576) == 2.0 + 16 / 576
+    assert oracle.bits_per_weight(4096, 4096, 2, [12, 4], 128) == 2.125
+    # stage bytes by hand: 12-bit = 1.5 B/group, 4-bit = 0.5 B/group
+    g = 576 * 72
+    assert oracle.compressed_bytes(576, 576, 2, [12, 4], 128, include_codebooks=False) == g * 3 // 2 + g // 2 + 2 * 576 * 5
+    assert oracle.compressed_bytes(576, 576, 2, [12, 4], 128) == g * 2 + 2 * 576 * 5 + 4096 * 16 + 16 * 16
+
+
+@pytest.mark.parametrize("widths,bpw", [([16], 2), ([16, 8], 3), ([16, 16], 4), ([16, 16, 8], 5),
+                                        ([16, 16, 16], 6), ([16, 16, 16, 8], 7), ([16, 16, 16, 16], 8)])
+def test_glq_bit_width_ladder(widths, bpw):
+    """GLQ "Bit widths" table: a 16-bit primary, then 16- or 8-bit residual
+    stages, gives 2..8 bits per weight (indices only; one scale per row adds
+    16/K)."""
+    k = 8192
+    assert oracle.bits_per_weight(1024, k, len(widths), widths, k) == bpw + 16 / k
+
+
+def test_4bit_odd_groups_and_codebook():
+    # 3 groups of 4-bit: 2 bytes (pad nibble), one 16-entry fp16 codebook of 8-vectors = 256 B
+    assert oracle.compressed_bytes(1, 24, 1, 4, 24, include_codebooks=False) == 2 + 2
+    assert oracle.compressed_bytes(1, 24, 1, 4, 24) == 2 + 2 + 256
+    with pytest.raises(ValueError):
+        oracle.compressed_bytes(1, 24, 2, [12], 24)
+    with pytest.raises(ValueError):
+        oracle.compressed_bytes(1, 24, 1, [10], 24)

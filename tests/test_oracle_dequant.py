@@ -152,3 +152,96 @@ def test_residual_sum_matches_stagewise_sum():
     a = oracle.dequant_exact(n, k, idx[:1], cbs[:1], sc, k)
     b = oracle.dequant_exact(n, k, idx[1:], cbs[1:], sc, k)
     assert np.array_equal(both, a + b)
+
+
+# ---------------------------------------------------------------------------
+# residual ladders: per-stage widths and per-stage residual scales
+# ---------------------------------------------------------------------------
+
+def _stage_cases():
+    with open(os.path.join(GOLDEN, "stage_scale_hand.json")) as f:
+        return json.load(f)["cases"]
+
+
+def _sparse_codebooks(case):
+    cbs = []
+    for spec in case["codebooks_sparse"]:
+        cb = np.zeros((spec["rows"], 8), np.float16)
+        for row, vals in spec["set"].items():
+            cb[int(row)] = vals
+        cbs.append(cb)
+    return cbs
+
+
+@pytest.mark.parametrize("case", _stage_cases(), ids=lambda c: c["name"])
+def test_stage_scale_hand(case):
+    idx = [np.array(i) for i in case["indices"]]
+    cbs = _sparse_codebooks(case)
+    sc = np.array(case["scales"], dtype=np.float16)
+    rs = np.array(case["stage_scales"], dtype=np.float32)
+    assert np.array_equal(rs.astype(np.float64), np.array(case["stage_scales"]))  # fp32-exact inputs
+    w = oracle.dequant_fp16(case["n_out"], case["k_in"], idx, cbs, sc, case["scale_block"], stage_scales=rs)
+    if "w" in case:
+        want = np.array(case["w"], dtype=np.float16)
+        assert np.array_equal(w.view(np.uint16), want.view(np.uint16))
+        w64 = oracle.dequant_exact(case["n_out"], case["k_in"], idx, cbs, sc, case["scale_block"], rs)
+        assert np.array_equal(np.signbit(w64), np.signbit(np.array(case["w"])))
+        assert np.array_equal(w64, np.array(case["w"]))
+    else:
+        assert w.view(np.uint16).tolist() == case["w_bits"]
+        # the tie is real: the exact rational value rounds to the other neighbour
+        q = sum(Fraction(float(rs[t])) * Fraction(float(cbs[t][idx[t][0], 0])) for t in range(2))
+        q *= Fraction(float(sc[0, 0]))
+        assert fraction_to_half_bits(q) == case["exact_real_bits"]
+
+
+def test_unit_stage_scales_change_nothing():
+    """r_t = 1 for every stage gives the plain decode bit for bit (ladder of
+    mixed widths, subnormal-heavy codebooks, negative scales)."""
+    rng = np.random.default_rng(29)
+    n, k, bs = 6, 64, 32
+    widths = [16, 8, 4]
+    cbs = [(rng.standard_normal((1 << b, 8)) * 10.0 ** rng.integers(-7, 1, (1 << b, 8))).astype(np.float16)
+           for b in widths]
+    idx = [rng.integers(0, 1 << b, n * k // 8) for b in widths]
+    sc = rng.uniform(-1.5, 1.5, (n, 2)).astype(np.float16)
+    a = oracle.dequant_exact(n, k, idx, cbs, sc, bs)
+    b = oracle.dequant_exact(n, k, idx, cbs, sc, bs, stage_scales=np.ones(3, np.float32))
+    assert np.array_equal(a, b) and np.array_equal(np.signbit(a), np.signbit(b))
+
+
+def test_stage_scale_fraction_brute_force():
+    """12+4 and 16+8 ladders with float32 residual scales on random tiny
+    tensors: the oracle's fp16 equals the exact rational value rounded by
+    hand (the float64 evaluation order only matters within 2^-50 of a tie,
+    which random data does not reach), and its float64 value is within
+    2^-50 relative of the exact one."""
+    rng = np.random.default_rng(41)
+    n, k, bs = 3, 32, 16
+    for widths in ([12, 4], [16, 8], [8, 8, 4, 4]):
+        for _ in range(3):
+            cbs = [(rng.standard_normal((1 << b, 8)) * 0.02 * 0.3 ** t).astype(np.float16)
+                   for t, b in enumerate(widths)]
+            idx = [rng.integers(0, 1 << b, n * k // 8) for b in widths]
+            sc = rng.uniform(0.5, 1.5, (n, 2)).astype(np.float16)
+            rs = rng.uniform(-3.0, 3.0, len(widths)).astype(np.float32)
+            w = oracle.dequant_fp16(n, k, idx, cbs, sc, bs, stage_scales=rs)
+            w64 = oracle.dequant_exact(n, k, idx, cbs, sc, bs, stage_scales=rs)
+            for r in range(n):
+                for c in range(k):
+                    f = r * (k // 8) + c // 8
+                    tot = sum(Fraction(float(rs[t])) * Fraction(float(cbs[t][idx[t][f], c % 8]))
+                              for t in range(len(widths)))
+                    q = Fraction(float(sc[r, c // bs])) * tot
+                    assert abs(Fraction(float(w64[r, c])) - q) <= abs(q) * Fraction(1, 2 ** 50)
+                    assert int(w.view(np.uint16)[r, c]) == fraction_to_half_bits(q), (widths, r, c)
+
+
+def test_stage_scales_validated():
+    cb = [np.ones((16, 8), np.float16)] * 2
+    idx = [np.zeros(1, np.int64)] * 2
+    sc = np.ones((1, 1), np.float16)
+    with pytest.raises(ValueError):
+        oracle.dequant_exact(1, 8, idx, cb, sc, 8, stage_scales=[1.0])
+    with pytest.raises(ValueError):
+        oracle.dequant_exact(1, 8, idx, cb, sc, 8, stage_scales=[1.0, float("inf")])

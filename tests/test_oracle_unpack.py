@@ -17,7 +17,7 @@ def _golden():
 @pytest.mark.parametrize("case", _golden(), ids=lambda c: c["note"][:24])
 def test_hand_planes_unpack(case):
     """Planes worked by hand decode to the stated indices (no use of pack)."""
-    lo = np.array(case["lo"], dtype=np.uint8)
+    lo = None if case["lo"] is None else np.array(case["lo"], dtype=np.uint8)
     hi = None if case["hi"] is None else np.array(case["hi"], dtype=np.uint8)
     got = oracle.unpack_indices(case["bits"], len(case["indices"]), lo=lo, hi=hi)
     assert got.tolist() == case["indices"]
@@ -26,7 +26,10 @@ def test_hand_planes_unpack(case):
 @pytest.mark.parametrize("case", _golden(), ids=lambda c: c["note"][:24])
 def test_hand_indices_pack(case):
     lo, hi = oracle.pack_indices(case["indices"], case["bits"])
-    assert lo.tolist() == case["lo"]
+    if case["lo"] is None:
+        assert lo is None
+    else:
+        assert lo.tolist() == case["lo"]
     if case["hi"] is None:
         assert hi is None
     else:
@@ -87,3 +90,34 @@ def test_rejects_bad_width_and_range():
         oracle.pack_indices([4096], 12)
     with pytest.raises(ValueError):
         oracle.pack_indices([-1], 8)
+
+
+def test_exhaustive_4bit_roundtrip():
+    """Every 4-bit value survives pack -> unpack at both nibble positions."""
+    vals = np.arange(16)
+    for seq in (np.repeat(vals, 2), np.tile(vals, 3), vals[:15], vals[::-1]):
+        lo, hi = oracle.pack_indices(seq, 4)
+        assert lo is None and hi.size == (seq.size + 1) // 2
+        assert np.array_equal(oracle.unpack_indices(4, seq.size, hi=hi), seq)
+
+
+def test_12bit_is_8bit_plane_plus_4bit_plane():
+    """Structure of the bit-planes: a 12-bit index is the 8-bit index of its
+    low plane plus 256 times the 4-bit index of its nibble plane."""
+    rng = np.random.default_rng(17)
+    n = 999
+    lo = rng.integers(0, 256, n, dtype=np.uint8)
+    hi = rng.integers(0, 256, (n + 1) // 2, dtype=np.uint8)
+    i12 = oracle.unpack_indices(12, n, lo=lo, hi=hi)
+    assert np.array_equal(i12, oracle.unpack_indices(8, n, lo=lo) + 256 * oracle.unpack_indices(4, n, hi=hi))
+
+
+def test_4bit_brute_force_bits():
+    n = 5
+    for f in range(n):
+        for bit in range(4):
+            hi = np.zeros((n + 1) // 2, dtype=np.uint8)
+            hi[f // 2] = 1 << (bit + 4 * (f % 2))
+            want = np.zeros(n, dtype=np.int64)
+            want[f] = 1 << bit
+            assert np.array_equal(oracle.unpack_indices(4, n, hi=hi), want), (f, bit)
