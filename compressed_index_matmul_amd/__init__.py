@@ -24,7 +24,7 @@ import numpy as np
 
 __all__ = [
     "VQError", "VQWeight", "lib", "LIB_PATH", "vq_version", "vq_validate", "vq_compressed_bytes",
-    "vq_unpack_dequant", "vq_gemv", "vq_gemm", "rht_apply", "VQ_F32", "VQ_BF16", "EXPORTS",
+    "vq_unpack_dequant", "vq_gemv", "vq_gemm", "rht_apply", "VQ_F32", "VQ_BF16", "VQ_STAGE_SCALES", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvqmm.so")
@@ -34,6 +34,9 @@ EXPORTS = ("vq_version", "vq_status_string", "vq_validate", "vq_compressed_bytes
            "vq_unpack_dequant", "vq_gemv", "vq_gemm", "rht_apply")
 
 _ptr4 = ctypes.c_void_p * MAX_STAGES
+_int4 = ctypes.c_int32 * MAX_STAGES
+_flt4 = ctypes.c_float * MAX_STAGES
+VQ_STAGE_SCALES = 1
 
 
 class VQWeightDesc(ctypes.Structure):
@@ -44,12 +47,14 @@ class VQWeightDesc(ctypes.Structure):
         ("n_stages", ctypes.c_int32),
         ("idx_bits", ctypes.c_int32),
         ("scale_block", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
         ("idx_lo", _ptr4),
         ("idx_hi", _ptr4),
         ("idx16", _ptr4),
         ("codebook", _ptr4),
         ("scales", ctypes.c_void_p),
+        ("stage_bits", _int4),
+        ("stage_scale", _flt4),
     ]
 
 
@@ -127,15 +132,20 @@ class VQWeight:
     """A compressed weight resident in device memory plus its descriptor.
 
     The tensors are kept alive by this object; the descriptor holds their
-    raw device addresses.
+    raw device addresses.  ``stage_bits`` (optional) gives each stage its own
+    index width (4, 8, 12 or 16); ``stage_scales`` (optional) one float
+    residual scale per stage.
     """
 
     def __init__(self, n_out: int, k_in: int, n_stages: int, idx_bits: int, scale_block: int,
                  codebooks: Sequence, scales, lo: Sequence = (), hi: Sequence = (),
-                 idx16: Sequence = (), device="cuda"):
+                 idx16: Sequence = (), device="cuda", stage_bits: Optional[Sequence[int]] = None,
+                 stage_scales: Optional[Sequence[float]] = None):
         import torch
         self.n_out, self.k_in, self.n_stages, self.idx_bits = n_out, k_in, n_stages, idx_bits
         self.scale_block = scale_block
+        self.stage_bits = None if stage_bits is None else [int(b) for b in stage_bits]
+        self.stage_scales = None if stage_scales is None else [float(np.float32(r)) for r in stage_scales]
         self.device = torch.device(device)
         self.codebooks = [_as_device(c, self.device, torch.float16) for c in codebooks]
         self.scales = _as_device(scales, self.device, torch.float16)
@@ -148,7 +158,12 @@ class VQWeight:
     def _fill_desc(self):
         d = self.desc
         d.n_out, d.k_in, d.n_stages, d.idx_bits = self.n_out, self.k_in, self.n_stages, self.idx_bits
-        d.scale_block, d.reserved = self.scale_block, 0
+        d.scale_block = self.scale_block
+        d.flags = 0 if self.stage_scales is None else VQ_STAGE_SCALES
+        for t in range(MAX_STAGES):
+            d.stage_bits[t] = self.stage_bits[t] if self.stage_bits is not None and t < len(self.stage_bits) else 0
+            d.stage_scale[t] = (self.stage_scales[t] if self.stage_scales is not None and t < len(self.stage_scales)
+                                else 1.0)
         for t in range(MAX_STAGES):
             d.idx_lo[t] = self.lo[t].data_ptr() if t < len(self.lo) and self.lo[t] is not None else None
             d.idx_hi[t] = self.hi[t].data_ptr() if t < len(self.hi) and self.hi[t] is not None else None

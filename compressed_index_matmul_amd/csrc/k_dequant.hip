@@ -7,6 +7,14 @@
 // fp16 factor need < 53 significant bits), and rounded once to fp16 with
 // integer arithmetic on the bit pattern, so the result is the correctly
 // rounded value whatever the summation order.  Write-bandwidth bound.
+//
+// Residual ladders (per-stage widths) and stage scales (GLQ page, "Inference
+// kernels": the inverse residual scale of the two-stage call) take the
+// BITS = 0 instantiation: each stage's width is read at run time, each
+// entry is multiplied by its stage scale in float64 (exact: 24 + 11
+// significant bits), the products are added from stage 0 up with float64
+// rounding and the sum is multiplied by the block scale in float64 -- a
+// fixed order, so the fp16 result is reproducible bit for bit.
 #include "vqmm_device.h"
 #include "vqmm_internal.h"
 
@@ -22,8 +30,11 @@ struct DequantArgs {
   uint16_t *w_out;    // [N][K] or null
   int64_t total;      // N * G
   int G, S, bits, bs, nblk, k;
+  int sb[VQ_MAX_STAGES];    // index width of each stage
+  float rs[VQ_MAX_STAGES];  // stage scales
 };
 
+// BITS: the width of every stage, or 0 for per-stage widths and scales.
 template <int BITS>
 __global__ __launch_bounds__(256) void k_unpack_dequant(DequantArgs a) {
   const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -32,7 +43,7 @@ __global__ __launch_bounds__(256) void k_unpack_dequant(DequantArgs a) {
   const int g = (int)(f - r * a.G);
   double acc[8];
   for (int t = 0; t < a.S; ++t) {
-    uint32_t idx = load_index(BITS, a.lo[t], a.hi[t], a.i16[t], (size_t)f);
+    uint32_t idx = load_index(BITS ? BITS : a.sb[t], a.lo[t], a.hi[t], a.i16[t], (size_t)f);
     if (a.idx_out) a.idx_out[(int64_t)t * a.total + f] = (uint16_t)idx;
     if (a.w_out) {
       const uint4 v = reinterpret_cast<const uint4 *>(a.cb[t])[idx];
@@ -40,7 +51,8 @@ __global__ __launch_bounds__(256) void k_unpack_dequant(DequantArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         double c = (double)h2f((h[j >> 1] >> ((j & 1) * 16)) & 0xffffu);
-        acc[j] = (t == 0) ? c : acc[j] + c;  // exact: sum starts at stage 0
+        if (BITS == 0) c *= (double)a.rs[t];  // exact product
+        acc[j] = (t == 0) ? c : acc[j] + c;  // sum starts at stage 0
       }
     }
   }
@@ -72,8 +84,14 @@ hipError_t launch_unpack_dequant(const WView &w, uint16_t *idx_out, uint16_t *w_
   a.bs = w.bs;
   a.nblk = w.nblk;
   a.k = w.k;
+  for (int t = 0; t < VQ_MAX_STAGES; ++t) {
+    a.sb[t] = t < w.S ? w.sb[t] : 0;
+    a.rs[t] = w.rs[t];
+  }
   const unsigned blocks = (unsigned)((a.total + 255) / 256);
-  if (w.bits == 8)
+  if (!plain_format(w))
+    hipLaunchKernelGGL(k_unpack_dequant<0>, dim3(blocks), dim3(256), 0, s, a);
+  else if (w.bits == 8)
     hipLaunchKernelGGL(k_unpack_dequant<8>, dim3(blocks), dim3(256), 0, s, a);
   else if (w.bits == 12)
     hipLaunchKernelGGL(k_unpack_dequant<12>, dim3(blocks), dim3(256), 0, s, a);

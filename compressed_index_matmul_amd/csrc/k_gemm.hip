@@ -35,7 +35,25 @@ struct GemmArgs {
   int gshift;  // log2(scale_block / 8) when a power of two, else -1
   int tiles_m, tiles_n, per_xcd;
   uint64_t smagic;  // ceil(2^32 / (scale_block / 32)): K step -> scale block by a multiply
+  int sb[VQ_MAX_STAGES];     // index width of each stage
+  float rs[VQ_MAX_STAGES];   // stage scales
+  int cboff[VQ_MAX_STAGES];  // first LDS codebook row of each stage (BITS = 0 kernels)
+  int cbrows;                // codebook rows of all stages
 };
+
+// LDS codebook rows of the BITS = 0 (per-stage widths) kernels: 128 KiB.
+constexpr int kLadderCbRows = 8192;
+
+// Copy the codebooks of a ladder of per-stage widths into LDS, stage t from
+// row a.cboff[t] (plain loads; the caller synchronises).
+__device__ __forceinline__ void stage_ladder_codebooks(const GemmArgs &a, uint4 *s_cb, int tid, int nthreads) {
+  for (int i = tid; i < a.cbrows; i += nthreads) {
+    int t = 0;
+#pragma unroll
+    for (int u = 1; u < VQ_MAX_STAGES; ++u) t += (u < a.S && i >= a.cboff[u]) ? 1 : 0;
+    s_cb[i] = reinterpret_cast<const uint4 *>(a.cb[t])[i - a.cboff[t]];
+  }
+}
 
 // Scale block of group g (8 columns): g / (scale_block / 8).
 __device__ __forceinline__ int scale_blk(const GemmArgs &a, int g) {
@@ -46,19 +64,25 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Decode group g of W row `row` to 8 bf16 (packed in a uint4).  Stage sum and
-// scale in fp32 (summation starts from stage 0).
+// scale in fp32 (summation starts from stage 0).  BITS = 0: per-stage widths
+// (a.sb), each entry times its stage scale.
 template <int S, int BITS, bool CB_LDS>
 __device__ __forceinline__ uint4 decode_group_bf16(const GemmArgs &a, const uint4 *s_cb, int row, int g) {
   const size_t f = (size_t)row * a.G + g;
   float w[8];
 #pragma unroll
   for (int t = 0; t < S; ++t) {
-    const uint32_t idx = load_index(BITS, a.lo[t], a.hi[t], a.i16[t], f);
-    const uint4 v = CB_LDS ? s_cb[(t << BITS) + idx] : reinterpret_cast<const uint4 *>(a.cb[t])[idx];
+    const uint32_t idx = load_index(BITS ? BITS : a.sb[t], a.lo[t], a.hi[t], a.i16[t], f);
+    const uint4 v = CB_LDS ? s_cb[(BITS ? (t << BITS) : a.cboff[t]) + idx] : reinterpret_cast<const uint4 *>(a.cb[t])[idx];
     const uint32_t hv[4] = {v.x, v.y, v.z, v.w};
+    const float r = BITS ? 1.f : a.rs[t];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float c0 = h2f(hv[e] & 0xffffu), c1 = h2f(hv[e] >> 16);
+      float c0 = h2f(hv[e] & 0xffffu), c1 = h2f(hv[e] >> 16);
+      if (BITS == 0) {
+        c0 *= r;
+        c1 *= r;
+      }
       w[2 * e] = (t == 0) ? c0 : w[2 * e] + c0;
       w[2 * e + 1] = (t == 0) ? c1 : w[2 * e + 1] + c1;
     }
@@ -137,6 +161,29 @@ __device__ __forceinline__ uint4 group_to_bf16(const uint4 (&v)[S], float sf) {
   return pk;
 }
 
+// 8 weights of one group as bf16 with stage scales: sum of each stage vector
+// times its scale (fp32, from stage 0), times the block scale, rounded to bf16.
+template <int S>
+__device__ __forceinline__ uint4 group_to_bf16_scaled(const uint4 (&v)[S], float sf, const float *rs) {
+  float w[8];
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    const uint32_t ht[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float c0 = h2f(ht[e] & 0xffffu) * rs[t], c1 = h2f(ht[e] >> 16) * rs[t];
+      w[2 * e] = t == 0 ? c0 : w[2 * e] + c0;
+      w[2 * e + 1] = t == 0 ? c1 : w[2 * e + 1] + c1;
+    }
+  }
+  uint4 pk;
+  pk.x = pack_bf16(sf * w[0], sf * w[1]);
+  pk.y = pack_bf16(sf * w[2], sf * w[3]);
+  pk.z = pack_bf16(sf * w[4], sf * w[5]);
+  pk.w = pack_bf16(sf * w[6], sf * w[7]);
+  return pk;
+}
+
 // Everything one thread needs from global memory for one K step (4 groups,
 // 32 columns) of the large-M kernel: index bits of its two groups for every
 // stage, their scales, and the wave's A fragments (x) for the step.
@@ -184,8 +231,9 @@ __device__ __forceinline__ void gemm_load_step(const GemmArgs &a, int ks, int dg
 #pragma unroll
     for (int t = 0; t < S; ++t) {
       uint32_t i0 = 0, i1 = 0;
-      if (g0 < a.G) i0 = load_index(BITS, a.lo[t], a.hi[t], a.i16[t], f);
-      if (g0 + 1 < a.G) i1 = load_index(BITS, a.lo[t], a.hi[t], a.i16[t], f + 1);
+      const int bt = BITS ? BITS : a.sb[t];
+      if (g0 < a.G) i0 = load_index(bt, a.lo[t], a.hi[t], a.i16[t], f);
+      if (g0 + 1 < a.G) i1 = load_index(bt, a.lo[t], a.hi[t], a.i16[t], f + 1);
       R.lo[t] = i0 | (i1 << 16);  // unpacked form for the ragged path
     }
     R.sc[0] = g0 < a.G ? a.sc[o.scrow + scale_blk(a, g0)] : 0;
@@ -265,7 +313,7 @@ __device__ __forceinline__ void gemm_decode_store(const GemmArgs &a, const uint4
         idx = (R.lo[t] >> (8 * u)) & 0xffu;
         if (BITS == 12) idx |= ((R.hi[t] >> (4 * u)) & 0xfu) << 8;
       }
-      v[t] = CB_LDS ? s_cb[(t << BITS) + idx] : reinterpret_cast<const uint4 *>(a.cb[t])[idx];
+      v[t] = CB_LDS ? s_cb[(BITS ? (t << BITS) : a.cboff[t]) + idx] : reinterpret_cast<const uint4 *>(a.cb[t])[idx];
     }
     uint4 pk = group_to_bf16<S>(v, h2f(R.sc[u]));
     if (!wok || (!ALIGNED && g >= a.G)) pk = make_uint4(0, 0, 0, 0);
@@ -284,7 +332,7 @@ __device__ __forceinline__ void gemm_decode_store(const GemmArgs &a, const uint4
 // scales, x fragments) run four steps ahead in a ring of four register sets.
 template <int S, int BITS, bool CB_LDS, bool ALIGNED>
 __global__ __launch_bounds__(256) void k_gemm_large(GemmArgs a) {
-  __shared__ uint4 s_cb[CB_LDS ? (S << BITS) : 1];
+  __shared__ uint4 s_cb[CB_LDS ? (BITS ? (S << BITS) : kLadderCbRows) : 1];
   __shared__ __attribute__((aligned(16))) uint16_t s_w[2][kLN * kWP];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -295,12 +343,16 @@ __global__ __launch_bounds__(256) void k_gemm_large(GemmArgs a) {
   const int n0 = (L % a.tiles_n) * kLN;
 
   if (CB_LDS) {
-    constexpr int CBN = S << BITS;
+    if constexpr (BITS != 0) {
+      constexpr int CBN = S << BITS;
 #pragma unroll 4
-    for (int r = 0; r < CBN / 256; ++r) {
-      const int blk = (r * 4 + wave) * 64;
-      lds_direct_16(reinterpret_cast<const uint4 *>(a.cb[blk >> BITS]) + (blk & ((1 << BITS) - 1)) + lane,
-                    s_cb + blk);
+      for (int r = 0; r < CBN / 256; ++r) {
+        const int blk = (r * 4 + wave) * 64;
+        lds_direct_16(reinterpret_cast<const uint4 *>(a.cb[blk >> BITS]) + (blk & ((1 << BITS) - 1)) + lane,
+                      s_cb + blk);
+      }
+    } else {
+      stage_ladder_codebooks(a, s_cb, tid, 256);  // visible after the barrier below
     }
   }
   const int drow = tid >> 1;     // W-tile row decoded by this thread
@@ -351,14 +403,15 @@ __global__ __launch_bounds__(256) void k_gemm_large(GemmArgs a) {
           idx = (R.lo[t] >> (8 * u)) & 0xffu;
           if (BITS == 12) idx |= ((R.hi[t] >> (4 * u)) & 0xfu) << 8;
         }
-        v[u][t] = CB_LDS ? s_cb[(t << BITS) + idx] : reinterpret_cast<const uint4 *>(a.cb[t])[idx];
+        v[u][t] = CB_LDS ? s_cb[(BITS ? (t << BITS) : a.cboff[t]) + idx] : reinterpret_cast<const uint4 *>(a.cb[t])[idx];
       }
   };
   // decode group u of step ks (gathered vectors v) and store it in tile wt
   // (aligned path: W rows past n only feed output columns that are never
   // stored, so they are decoded from the clamped row and not zeroed)
   auto decode = [&](int ks, int u, const StepRegs<S> &R, const uint4 (&v)[S], uint16_t *wt) {
-    uint4 pk = group_to_bf16<S>(v, h2f(R.sc[ALIGNED ? 0 : u]));
+    const float sf = h2f(R.sc[ALIGNED ? 0 : u]);
+    uint4 pk = BITS ? group_to_bf16<S>(v, sf) : group_to_bf16_scaled<S>(v, sf, a.rs);
     const int g = ks * 4 + dg + u;
     if (!ALIGNED && (!wok || g >= a.G)) pk = make_uint4(0, 0, 0, 0);
     *reinterpret_cast<uint4 *>(&wt[drow * kWP + 8 * (dg + u)]) = pk;
@@ -771,7 +824,7 @@ __global__ __launch_bounds__(256) void k_gemm_wide(GemmArgs a) {
         const uint32_t hw = s < 2 ? Q.hi[t].x : Q.hi[t].y;
         idx |= ((hw >> (4 * (4 * (s & 1) + g))) & 0xfu) << 8;
       }
-      vg[t] = s_cb[(t << BITS) + idx];
+      vg[t] = s_cb[(BITS ? (t << BITS) : a.cboff[t]) + idx];
     }
   };
   // the four groups of the thread's row in step s of quad Q
@@ -1006,7 +1059,7 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_small(GemmArgs a) {
         idx = (R.lo[t] >> (8 * r)) & 0xffu;
         if (BITS == 12) idx |= ((R.hi[t] >> (4 * r)) & 0xfu) << 8;
       }
-      const uint4 v = CB_LDS ? s_cb[(t << BITS) + idx] : reinterpret_cast<const uint4 *>(a.cb[t])[idx];
+      const uint4 v = CB_LDS ? s_cb[(BITS ? (t << BITS) : a.cboff[t]) + idx] : reinterpret_cast<const uint4 *>(a.cb[t])[idx];
       const uint32_t hv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -1218,7 +1271,7 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_few(GemmArgs a, int units
         const uint32_t hw = s < 2 ? Q.hi[t].x : Q.hi[t].y;
         idx |= ((hw >> (4 * (4 * (s & 1) + q))) & 0xfu) << 8;
       }
-      v[t] = s_cb[(t << BITS) + idx];
+      v[t] = s_cb[(BITS ? (t << BITS) : a.cboff[t]) + idx];
     }
     const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, group_to_bf16<S>(v, h2f(Q.sc)));
 #pragma unroll
@@ -1308,17 +1361,22 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_few(GemmArgs a, int units
 }
 
 // General small-M path (any K % 8 == 0, any scale block): one group per lane
-// per 32-column K step, byte-wise index loads.
+// per 32-column K step, byte-wise index loads.  BITS = 0: residual ladders
+// of per-stage widths and stage scales.
 template <int S, int BITS, bool CB_LDS>
 __global__ __launch_bounds__(kSWaves * 64) void k_gemm_small_gen(GemmArgs a) {
-  __shared__ uint4 s_cb[CB_LDS ? (S << BITS) : 1];
+  __shared__ uint4 s_cb[CB_LDS ? (BITS ? (S << BITS) : kLadderCbRows) : 1];
   __shared__ float s_red[kSWaves][16][17];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   if (CB_LDS) {
-    for (int i = tid; i < (S << BITS); i += kSWaves * 64)
-      s_cb[i] = reinterpret_cast<const uint4 *>(a.cb[i >> BITS])[i & ((1 << BITS) - 1)];
+    if constexpr (BITS != 0) {
+      for (int i = tid; i < (S << BITS); i += kSWaves * 64)
+        s_cb[i] = reinterpret_cast<const uint4 *>(a.cb[i >> BITS])[i & ((1 << BITS) - 1)];
+    } else {
+      stage_ladder_codebooks(a, s_cb, tid, kSWaves * 64);
+    }
     __syncthreads();
   }
   const int nks = (a.G + 3) / 4;
@@ -1378,6 +1436,13 @@ static GemmArgs make_gemm_args(const WView &w, const uint16_t *x, int m, float *
   a.gshift = (gb & (gb - 1)) == 0 ? __builtin_ctz((unsigned)gb) : -1;
   const uint64_t spb = w.bs % 32 == 0 ? (uint64_t)(w.bs / 32) : 1;
   a.smagic = ((uint64_t(1) << 32) + spb - 1) / spb;
+  a.cbrows = 0;
+  for (int t = 0; t < VQ_MAX_STAGES; ++t) {
+    a.sb[t] = t < w.S ? w.sb[t] : 0;
+    a.rs[t] = w.rs[t];
+    a.cboff[t] = a.cbrows;
+    if (t < w.S) a.cbrows += 1 << w.sb[t];
+  }
   return a;
 }
 
@@ -1471,8 +1536,45 @@ static void launch_gemm_bits(const WView &w, const GemmArgs &a, hipStream_t s) {
   }
 }
 
+// Residual ladders of per-stage widths and stage scales (BITS = 0): the
+// general slab kernel for 1..16 tokens, the 256 x 128 tile kernel on its
+// unaligned path above; codebooks in LDS when every stage fits (no 16-bit
+// stage, at most 128 KiB together).
+template <int S, bool CB_LDS>
+static void launch_gemm_ladder_s(const GemmArgs &a0, hipStream_t s) {
+  GemmArgs a = a0;
+  if (a.m <= 16) {
+    const int nslabs = (a.n + 15) / 16;
+    int nwg = device_cu_count();
+    if (nwg > nslabs) nwg = nslabs;
+    hipLaunchKernelGGL((k_gemm_small_gen<S, 0, CB_LDS>), dim3(nwg), dim3(kSWaves * 64), 0, s, a);
+  } else {
+    a.tiles_m = (a.m + kLM - 1) / kLM;
+    a.tiles_n = (a.n + kLN - 1) / kLN;
+    a.per_xcd = (a.tiles_m * a.tiles_n + 7) / 8;
+    hipLaunchKernelGGL((k_gemm_large<S, 0, CB_LDS, false>), dim3(8 * a.per_xcd), dim3(256), 0, s, a);
+  }
+}
+
+template <bool CB_LDS>
+static void launch_gemm_ladder(const WView &w, const GemmArgs &a, hipStream_t s) {
+  switch (w.S) {
+    case 1: launch_gemm_ladder_s<1, CB_LDS>(a, s); break;
+    case 2: launch_gemm_ladder_s<2, CB_LDS>(a, s); break;
+    case 3: launch_gemm_ladder_s<3, CB_LDS>(a, s); break;
+    default: launch_gemm_ladder_s<4, CB_LDS>(a, s); break;
+  }
+}
+
 hipError_t launch_gemm(const WView &w, const uint16_t *x, int m, float *y, hipStream_t s) {
   const GemmArgs a = make_gemm_args(w, x, m, y);
+  if (!plain_format(w)) {
+    bool fits = a.cbrows <= kLadderCbRows;
+    for (int t = 0; t < w.S; ++t) fits = fits && w.sb[t] != 16;
+    if (fits) launch_gemm_ladder<true>(w, a, s);
+    else launch_gemm_ladder<false>(w, a, s);
+    return hipGetLastError();
+  }
   if (w.bits == 8) launch_gemm_bits<8>(w, a, s);
   else if (w.bits == 12) launch_gemm_bits<12>(w, a, s);
   else launch_gemm_bits<16>(w, a, s);

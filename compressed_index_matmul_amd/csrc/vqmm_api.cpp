@@ -2,6 +2,7 @@
 // dispatch to the kernel launchers, status mapping.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <mutex>
 
@@ -17,28 +18,32 @@ int g_cu_count[kMaxDevices];
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool valid_width(int b) { return b == 4 || b == 8 || b == 12 || b == 16; }
+
 // Full descriptor check; fills `v` on success.  Touches no device state.
 int check_weight(const vq_weight *w, WView *v) {
   if (!w) return VQ_ERR_NULL;
   if (w->n_out < 1 || w->k_in < 8 || (w->k_in % 8) != 0) return VQ_ERR_SHAPE;
   if ((int64_t)w->n_out * w->k_in >= ((int64_t)1 << 31)) return VQ_ERR_SHAPE;
   if (w->n_stages < 1 || w->n_stages > VQ_MAX_STAGES) return VQ_ERR_SHAPE;
-  if (w->idx_bits != 8 && w->idx_bits != 12 && w->idx_bits != 16) return VQ_ERR_UNSUPPORTED;
   if (w->scale_block < 8 || (w->scale_block % 8) != 0) return VQ_ERR_SHAPE;
+  if ((w->flags & ~VQ_STAGE_SCALES) != 0) return VQ_ERR_UNSUPPORTED;
+  int sb[VQ_MAX_STAGES];
+  for (int t = 0; t < w->n_stages; ++t) {
+    sb[t] = w->stage_bits[t] != 0 ? w->stage_bits[t] : w->idx_bits;
+    if (!valid_width(sb[t])) return VQ_ERR_UNSUPPORTED;
+    if ((w->flags & VQ_STAGE_SCALES) && !std::isfinite(w->stage_scale[t])) return VQ_ERR_VALUE;
+  }
   for (int t = 0; t < w->n_stages; ++t) {
     if (!w->codebook[t]) return VQ_ERR_NULL;
     if (!aligned16(w->codebook[t])) return VQ_ERR_ALIGN;
-    if (w->idx_bits == 16) {
-      if (!w->idx16[t]) return VQ_ERR_NULL;
-      if (!aligned16(w->idx16[t])) return VQ_ERR_ALIGN;
-    } else {
-      if (!w->idx_lo[t]) return VQ_ERR_NULL;
-      if (!aligned16(w->idx_lo[t])) return VQ_ERR_ALIGN;
-      if (w->idx_bits == 12) {
-        if (!w->idx_hi[t]) return VQ_ERR_NULL;
-        if (!aligned16(w->idx_hi[t])) return VQ_ERR_ALIGN;
-      }
-    }
+    const bool need16 = sb[t] == 16;
+    const bool need_lo = sb[t] == 8 || sb[t] == 12;
+    const bool need_hi = sb[t] == 4 || sb[t] == 12;
+    if ((need16 && !w->idx16[t]) || (need_lo && !w->idx_lo[t]) || (need_hi && !w->idx_hi[t])) return VQ_ERR_NULL;
+    if ((need16 && !aligned16(w->idx16[t])) || (need_lo && !aligned16(w->idx_lo[t])) ||
+        (need_hi && !aligned16(w->idx_hi[t])))
+      return VQ_ERR_ALIGN;
   }
   if (!w->scales) return VQ_ERR_NULL;
   if (!aligned16(w->scales)) return VQ_ERR_ALIGN;
@@ -48,7 +53,18 @@ int check_weight(const vq_weight *w, WView *v) {
     v->k = w->k_in;
     v->G = w->k_in / 8;
     v->S = w->n_stages;
-    v->bits = w->idx_bits;
+    v->uniform = true;
+    v->scaled = false;
+    for (int t = 0; t < VQ_MAX_STAGES; ++t) v->rs[t] = 1.0f;
+    for (int t = 0; t < w->n_stages; ++t) {
+      v->sb[t] = sb[t];
+      v->uniform = v->uniform && sb[t] == sb[0];
+      if (w->flags & VQ_STAGE_SCALES) {
+        v->rs[t] = w->stage_scale[t];
+        v->scaled = v->scaled || w->stage_scale[t] != 1.0f;
+      }
+    }
+    v->bits = v->uniform ? sb[0] : 0;
     v->bs = w->scale_block > w->k_in ? w->k_in : w->scale_block;
     v->nblk = (w->k_in + v->bs - 1) / v->bs;
     for (int t = 0; t < w->n_stages; ++t) {
@@ -94,6 +110,7 @@ const char *vq_status_string(int status) {
     case VQ_ERR_UNSUPPORTED: return "request outside what the kernels implement";
     case VQ_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
     case VQ_ERR_HIP: return "HIP runtime error";
+    case VQ_ERR_VALUE: return "a scalar argument value is invalid";
     default: return "unknown status";
   }
 }
@@ -105,11 +122,13 @@ int64_t vq_compressed_bytes(const vq_weight *w) {
   const int st = check_weight(w, &v);
   if (st != VQ_OK) return st;
   const int64_t groups = (int64_t)v.n * v.G;
-  int64_t per_stage;
-  if (v.bits == 8) per_stage = groups;
-  else if (v.bits == 12) per_stage = groups + (groups + 1) / 2;
-  else per_stage = 2 * groups;
-  return v.S * per_stage + 2 * (int64_t)v.n * v.nblk + (int64_t)v.S * ((int64_t)1 << v.bits) * 16;
+  int64_t total = 2 * (int64_t)v.n * v.nblk;
+  for (int t = 0; t < v.S; ++t) {
+    const int b = v.sb[t];
+    total += b == 16 ? 2 * groups : b == 12 ? groups + (groups + 1) / 2 : b == 8 ? groups : (groups + 1) / 2;
+    total += ((int64_t)1 << b) * 16;
+  }
+  return total;
 }
 
 int vq_unpack_dequant(const vq_weight *w, uint16_t *idx_out, uint16_t *w_out, void *stream) {

@@ -202,13 +202,51 @@ __device__ __forceinline__ void buf_store_f32(float v, buf_t r, uint32_t voff, u
 #endif
 }
 
-// Index of flat group f of stage planes (any width).
+// Index of flat group f of stage planes (any width: 16-bit words; 12-bit
+// low byte plus nibble; 8-bit byte; 4-bit nibble).
 __device__ __forceinline__ uint32_t load_index(int bits, const uint8_t *lo, const uint8_t *hi,
                                                const uint16_t *i16, size_t f) {
   if (bits == 16) return i16[f];
+  const uint32_t nib = bits == 8 ? 0u : ((uint32_t)(hi[f >> 1] >> ((f & 1) * 4)) & 0xfu);
+  if (bits == 4) return nib;
   uint32_t v = lo[f];
-  if (bits == 12) v |= ((uint32_t)(hi[f >> 1] >> ((f & 1) * 4)) & 0xfu) << 8;
+  if (bits == 12) v |= nib << 8;
   return v;
 }
+
+// Index widths of the residual stages fixed at compile time (0 = no such
+// stage), for the kernels that keep every codebook in LDS.  A 12-bit index
+// is a low-byte plane plus a nibble plane shifted up by 8, an 8-bit index the
+// byte plane alone, a 4-bit index the nibble plane alone.  The stages'
+// codebooks sit back to back in LDS, stage t from row off(t).
+__host__ __device__ constexpr int ladder_rows(int b) { return b > 0 ? 1 << b : 0; }
+__host__ __device__ constexpr int ladder_planes(int b) { return b == 12 ? 2 : b > 0 ? 1 : 0; }
+
+template <int B0, int B1 = 0, int B2 = 0, int B3 = 0>
+struct Ladder {
+  static_assert((B0 == 4 || B0 == 8 || B0 == 12) && (B1 == 0 || B1 == 4 || B1 == 8 || B1 == 12) &&
+                    (B2 == 0 || B2 == 4 || B2 == 8 || B2 == 12) && (B3 == 0 || B3 == 4 || B3 == 8 || B3 == 12),
+                "LDS ladders take 4-, 8- and 12-bit stages");
+  static_assert((B1 > 0 || B2 == 0) && (B2 > 0 || B3 == 0), "stages are consecutive");
+  static constexpr int S = 1 + (B1 > 0) + (B2 > 0) + (B3 > 0);
+  static constexpr int kRows = ladder_rows(B0) + ladder_rows(B1) + ladder_rows(B2) + ladder_rows(B3);
+  // index loads per group chunk (one per plane)
+  static constexpr int kPlanes = ladder_planes(B0) + ladder_planes(B1) + ladder_planes(B2) + ladder_planes(B3);
+  // every stage has the same width
+  static constexpr bool kUniform = (B1 == 0 || B1 == B0) && (B2 == 0 || B2 == B0) && (B3 == 0 || B3 == B0);
+  // every stage's codebook is whole 64-row (1 KiB) blocks
+  static constexpr bool kBlocks = B0 >= 8 && (B1 == 0 || B1 >= 8) && (B2 == 0 || B2 >= 8) && (B3 == 0 || B3 >= 8);
+  __host__ __device__ static constexpr int bits(int t) { return t == 0 ? B0 : t == 1 ? B1 : t == 2 ? B2 : t == 3 ? B3 : 0; }
+  __host__ __device__ static constexpr int off(int t) {
+    return (t > 0 ? ladder_rows(B0) : 0) + (t > 1 ? ladder_rows(B1) : 0) + (t > 2 ? ladder_rows(B2) : 0);
+  }
+  __host__ __device__ static constexpr bool lo(int t) { return bits(t) == 8 || bits(t) == 12; }
+  __host__ __device__ static constexpr bool hi(int t) { return bits(t) == 4 || bits(t) == 12; }
+  __host__ __device__ static constexpr int hshift(int t) { return bits(t) == 12 ? 8 : 0; }
+  // stage owning codebook row `row` of the back-to-back layout
+  __host__ __device__ static constexpr int stage_of(int row) {
+    return (S > 1 && row >= off(1)) + (S > 2 && row >= off(2)) + (S > 3 && row >= off(3));
+  }
+};
 
 }  // namespace vqmm

@@ -16,7 +16,11 @@ struct WView {
   int k;      // k_in
   int G;      // groups per row = k / 8
   int S;      // stages
-  int bits;   // 8, 12, 16
+  int bits;   // index width of every stage when `uniform`, else 0
+  int sb[VQ_MAX_STAGES];  // index width of each stage: 4, 8, 12 or 16
+  bool uniform;           // every stage has the same width
+  bool scaled;            // some stage scale differs from 1
+  float rs[VQ_MAX_STAGES];  // stage scales (1 without VQ_STAGE_SCALES)
   int bs;     // scale_block (clamped to k when larger)
   int nblk;   // scales per row
   const uint8_t *lo[VQ_MAX_STAGES];
@@ -25,6 +29,10 @@ struct WView {
   const uint16_t *cb[VQ_MAX_STAGES];
   const uint16_t *sc;
 };
+
+// The plain formats the specialised kernels take: every stage of one width
+// (8, 12 or 16 bits) and no stage scales.
+inline bool plain_format(const WView &w) { return w.uniform && !w.scaled && w.bits >= 8; }
 
 // Compute units of the current device (cached per device).
 int device_cu_count();
@@ -38,5 +46,12 @@ hipError_t launch_gemv_token(const WView &w, const void *x, int xt, float *y, hi
 // allows it (false: not taken, nothing launched; *err set when taken).
 bool launch_gemv_tokens(const WView &w, const void *x, int batch, float *y, hipStream_t s, hipError_t *err);
 hipError_t launch_gemm(const WView &w, const uint16_t *x, int m, float *y, hipStream_t s);
+
+struct GemvArgs;
+// Ladders and stage scales on the LDS decode kernel (k_gemv_ladder.hip):
+// false when the ladder has no LDS kernel (nothing launched).  The shape
+// checks of the LDS kernel have been made by the caller.
+bool launch_gemv_lds_ladder(const WView &w, const GemvArgs &a, bool xf16, int cus, hipStream_t s);
+bool launch_gemv_tokens_ladder(const WView &w, const GemvArgs &a, int batch, int cus, hipStream_t s);
 
 }  // namespace vqmm

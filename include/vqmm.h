@@ -39,8 +39,11 @@
 extern "C" {
 #endif
 
-#define VQMM_VERSION 1
+#define VQMM_VERSION 2
 #define VQ_MAX_STAGES 4
+
+/* vq_weight.flags: stage_scale[] holds one residual scale per stage. */
+#define VQ_STAGE_SCALES 1
 
 /* Status codes returned by every entry point. */
 typedef enum vq_status {
@@ -50,43 +53,59 @@ typedef enum vq_status {
   VQ_ERR_DTYPE = -3,       /* unsupported element type for this argument */
   VQ_ERR_UNSUPPORTED = -4, /* valid request outside what the kernels implement */
   VQ_ERR_ALIGN = -5,       /* a base pointer is not 16-byte aligned */
-  VQ_ERR_HIP = -6          /* the HIP runtime reported an error */
+  VQ_ERR_HIP = -6,         /* the HIP runtime reported an error */
+  VQ_ERR_VALUE = -7        /* a scalar argument value is invalid (a non-finite stage scale) */
 } vq_status;
 
 /* Element types of activations. */
 typedef enum vq_dtype { VQ_F32 = 0, VQ_BF16 = 1 } vq_dtype;
 
 /*
- * Descriptor of one compressed weight (all pointers device memory).
+ * Descriptor of one compressed weight (array pointers are device memory).
  *
  * Groups are numbered row-major: group g of output row r is f = r*(k_in/8)+g.
- * Per stage t < n_stages, by idx_bits:
- *   8  : idx_lo[t]  uint8  [n_out*k_in/8]        index = idx_lo[t][f]
+ * Stage t < n_stages has index width b_t = stage_bits[t] when that is
+ * non-zero, else idx_bits.  By width:
+ *   16 : idx16[t]   uint16 [n_out*k_in/8]        little-endian index
+ *        (GLQ page, "How it works": one 16-bit index per 8 weights)
  *   12 : idx_lo[t]  uint8  [n_out*k_in/8]        bits 0..7 of index f
  *        idx_hi[t]  uint8  [ceil(n_out*k_in/16)] bits 8..11: low nibble of
  *                   idx_hi[t][f/2] for even f, high nibble for odd f
  *        (orka README, "How it works": 12-bit bit-planes, a low byte plus
  *        packed high bits; the nibble order is this library's reading)
- *   16 : idx16[t]   uint16 [n_out*k_in/8]        little-endian index
- *        (GLQ page, "How it works": one 16-bit index per 8 weights)
- * codebook[t] : fp16 bits [2^idx_bits][8], row-major.
+ *   8  : idx_lo[t]  uint8  [n_out*k_in/8]        index = idx_lo[t][f]
+ *   4  : idx_hi[t]  uint8  [ceil(n_out*k_in/16)] index = the nibble of f,
+ *                   packed as the 12-bit high plane (the residual stage of
+ *                   orka's rvq-12-4 mode: 12 + 4 bits per 8 weights)
+ * Mixed widths form the residual ladders of the GLQ page, "Bit widths" (a
+ * 16-bit primary plus 8- or 16-bit residual stages, up to four stages).
+ * codebook[t] : fp16 bits [2^b_t][8], row-major.
  * scales      : fp16 bits [n_out][ceil(k_in/scale_block)]; column c of row r
  *               uses scales[r][c / scale_block].  scale_block >= k_in means
  *               one scale per row.
- * Unused pointer slots are ignored.
+ * flags       : 0, or VQ_STAGE_SCALES: stage t's codebook entries are
+ *               multiplied by the float stage_scale[t] (finite), the residual
+ *               scale of the GLQ page's two-stage call ("Inference kernels"):
+ *                 w[r, 8g + j] = s[r, blk] * sum_t stage_scale[t] * cb_t[..][j].
+ *               Without the flag every stage scale is 1.
+ * Unused pointer slots and unused stage_bits / stage_scale entries are
+ * ignored.  A zero-initialised descriptor with the first block filled in
+ * describes a uniform ladder without stage scales.
  */
 typedef struct vq_weight {
   int32_t n_out;       /* N >= 1 */
   int32_t k_in;        /* K >= 8, K % 8 == 0; n_out*k_in < 2^31 */
   int32_t n_stages;    /* 1..4 */
-  int32_t idx_bits;    /* 8, 12 or 16, the same for every stage */
+  int32_t idx_bits;    /* 4, 8, 12 or 16: width of every stage without its own */
   int32_t scale_block; /* columns per scale, >= 8 and a multiple of 8 */
-  int32_t reserved;    /* set to 0 */
+  int32_t flags;       /* 0 or VQ_STAGE_SCALES */
   const uint8_t *idx_lo[VQ_MAX_STAGES];
   const uint8_t *idx_hi[VQ_MAX_STAGES];
   const uint16_t *idx16[VQ_MAX_STAGES];
   const uint16_t *codebook[VQ_MAX_STAGES];
   const uint16_t *scales;
+  int32_t stage_bits[VQ_MAX_STAGES]; /* 0 (= idx_bits), 4, 8, 12 or 16 */
+  float stage_scale[VQ_MAX_STAGES];  /* used with VQ_STAGE_SCALES */
 } vq_weight;
 
 /* Library version (VQMM_VERSION).  Host only. */
@@ -100,9 +119,9 @@ const char *vq_status_string(int status);
 int vq_validate(const vq_weight *w);
 
 /* Stored bytes of the weight: index planes + fp16 scales + fp16 codebooks,
- * each counted once (12-bit: 1.5 bytes per group per stage, rounded up per
- * plane; 8-bit: 1; 16-bit: 2).  Negative vq_status on an invalid
- * descriptor.  Host only. */
+ * each counted once (per group and stage: 16-bit 2 bytes, 12-bit 1.5, 8-bit
+ * 1, 4-bit 0.5, nibble planes rounded up).  Negative vq_status on an
+ * invalid descriptor.  Host only. */
 int64_t vq_compressed_bytes(const vq_weight *w);
 
 /*
@@ -112,7 +131,11 @@ int64_t vq_compressed_bytes(const vq_weight *w);
  *   idx_out : uint16 [n_stages][n_out][k_in/8] unpacked indices, or NULL
  *   w_out   : fp16 bits [n_out][k_in], or NULL.  Each weight is the exact
  *             value of the decode formula rounded once to fp16 (nearest,
- *             ties to even; subnormals kept, overflow to +-inf).
+ *             ties to even; subnormals kept, overflow to +-inf).  With
+ *             VQ_STAGE_SCALES the value is not exact in general and is
+ *             defined by a fixed float64 order: each stage_scale[t] * entry
+ *             (exact), summed from stage 0 up with float64 rounding, times
+ *             the block scale in float64, then rounded once to fp16.
  * At least one output must be non-NULL.  Bit-exact.
  */
 int vq_unpack_dequant(const vq_weight *w, uint16_t *idx_out, uint16_t *w_out, void *stream);

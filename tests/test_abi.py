@@ -13,7 +13,8 @@ from vqtest import ROOT, ensure_built
 
 HEADER = os.path.join(ROOT, "include", "vqmm.h")
 
-VQ_OK, VQ_ERR_NULL, VQ_ERR_SHAPE, VQ_ERR_DTYPE, VQ_ERR_UNSUPPORTED, VQ_ERR_ALIGN, VQ_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
+VQ_OK, VQ_ERR_NULL, VQ_ERR_SHAPE, VQ_ERR_DTYPE, VQ_ERR_UNSUPPORTED, VQ_ERR_ALIGN, VQ_ERR_HIP, VQ_ERR_VALUE = \
+    0, -1, -2, -3, -4, -5, -6, -7
 FAKE = 0x10000  # 16-byte aligned stand-in address, never dereferenced by validation
 
 
@@ -58,24 +59,35 @@ def test_version_matches_header(L):
 
 
 def test_status_strings(L):
-    for st in (VQ_OK, VQ_ERR_NULL, VQ_ERR_SHAPE, VQ_ERR_DTYPE, VQ_ERR_UNSUPPORTED, VQ_ERR_ALIGN, VQ_ERR_HIP):
+    for st in (VQ_OK, VQ_ERR_NULL, VQ_ERR_SHAPE, VQ_ERR_DTYPE, VQ_ERR_UNSUPPORTED, VQ_ERR_ALIGN, VQ_ERR_HIP,
+               VQ_ERR_VALUE):
         s = L.vq_status_string(st).decode()
         assert s and s != "unknown status"
     assert L.vq_status_string(12345).decode() == "unknown status"
 
 
-def fake_desc(n=64, k=64, stages=1, bits=12, bs=32):
-    from compressed_index_matmul_amd import VQWeightDesc
+def fake_desc(n=64, k=64, stages=1, bits=12, bs=32, widths=None, stage_scales=None):
+    """A descriptor of stand-in addresses; ``widths`` gives per-stage widths
+    (stage_bits), ``stage_scales`` sets VQ_STAGE_SCALES."""
+    from compressed_index_matmul_amd import VQWeightDesc, VQ_STAGE_SCALES
     d = VQWeightDesc()
     d.n_out, d.k_in, d.n_stages, d.idx_bits, d.scale_block = n, k, stages, bits, bs
+    ws = widths or [bits] * stages
     for t in range(stages):
         d.codebook[t] = FAKE
-        if bits == 16:
+        b = ws[t]
+        if widths is not None:
+            d.stage_bits[t] = b
+        if b == 16:
             d.idx16[t] = FAKE
-        else:
+        if b in (8, 12):
             d.idx_lo[t] = FAKE
-            if bits == 12:
-                d.idx_hi[t] = FAKE
+        if b in (4, 12):
+            d.idx_hi[t] = FAKE
+    if stage_scales is not None:
+        d.flags = VQ_STAGE_SCALES
+        for t, r in enumerate(stage_scales):
+            d.stage_scale[t] = r
     d.scales = FAKE
     return d
 
@@ -161,7 +173,7 @@ def test_rht_argument_checks(L):
     assert L.rht_apply(FAKE + 4, 0, 1, 64, FAKE, 64, FAKE, None) == VQ_ERR_ALIGN
 
 
-@pytest.mark.parametrize("wl", list(vqsynth.WORKLOADS))
+@pytest.mark.parametrize("wl", [w for w in vqsynth.WORKLOADS if isinstance(vqsynth.WORKLOADS[w]["bits"], int)])
 def test_compressed_bytes_match_oracle(L, wl):
     """The library's byte count equals the oracle's closed form for every
     workload shape (two independent implementations of the same arithmetic)."""
@@ -176,3 +188,67 @@ def test_compressed_bytes_match_oracle(L, wl):
 def test_compressed_bytes_ragged(L, n, k, st, bits, bs):
     d = fake_desc(n, k, st, bits, bs)
     assert L.vq_compressed_bytes(ctypes.byref(d)) == oracle.compressed_bytes(n, k, st, bits, min(bs, k) if bs > k else bs)
+
+
+@pytest.mark.parametrize("widths", [[12, 4], [8, 4], [16, 8], [16, 16, 8], [16, 16, 16, 8], [4], [4, 4, 4, 4],
+                                    [12, 12, 4], [16, 12, 8, 4]])
+def test_valid_ladders(L, widths):
+    d = fake_desc(stages=len(widths), widths=widths)
+    assert L.vq_validate(ctypes.byref(d)) == VQ_OK
+    d = fake_desc(stages=len(widths), widths=widths, stage_scales=[1.0, 0.25, -3.0, 1e-30][:len(widths)])
+    assert L.vq_validate(ctypes.byref(d)) == VQ_OK
+
+
+def test_stage_bits_zero_means_idx_bits(L):
+    d = fake_desc(stages=2, bits=16)          # stage_bits all 0 -> 16, 16
+    assert L.vq_compressed_bytes(ctypes.byref(d)) == oracle.compressed_bytes(64, 64, 2, 16, 32)
+    d.stage_bits[1] = 8                        # 16 + 8 now needs idx_lo[1]
+    assert L.vq_validate(ctypes.byref(d)) == VQ_ERR_NULL
+    d.idx_lo[1] = FAKE
+    assert L.vq_compressed_bytes(ctypes.byref(d)) == oracle.compressed_bytes(64, 64, 2, [16, 8], 32)
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda d: d.stage_bits.__setitem__(1, 6), VQ_ERR_UNSUPPORTED),
+    (lambda d: d.stage_bits.__setitem__(0, 32), VQ_ERR_UNSUPPORTED),
+    (lambda d: d.idx_hi.__setitem__(1, None), VQ_ERR_NULL),          # 4-bit stage without its nibble plane
+    (lambda d: d.idx_hi.__setitem__(1, FAKE + 1), VQ_ERR_ALIGN),
+    (lambda d: d.idx_lo.__setitem__(0, None), VQ_ERR_NULL),
+    (lambda d: setattr(d, "flags", 2), VQ_ERR_UNSUPPORTED),
+    (lambda d: (setattr(d, "flags", 1), d.stage_scale.__setitem__(1, float("inf"))), VQ_ERR_VALUE),
+    (lambda d: (setattr(d, "flags", 1), d.stage_scale.__setitem__(0, float("nan"))), VQ_ERR_VALUE),
+])
+def test_invalid_ladder(L, mutate, code):
+    d = fake_desc(stages=2, widths=[12, 4])
+    mutate(d)
+    assert L.vq_validate(ctypes.byref(d)) == code
+    assert L.vq_gemv(ctypes.byref(d), FAKE, 1, 1, FAKE, None) == code
+    assert L.vq_gemm(ctypes.byref(d), FAKE, 64, FAKE, None) == code
+    assert L.vq_unpack_dequant(ctypes.byref(d), FAKE, FAKE, None) == code
+
+
+def test_unused_stage_fields_ignored(L):
+    d = fake_desc(stages=2, widths=[12, 4])
+    d.stage_bits[3] = 7                        # beyond n_stages
+    d.stage_scale[1] = float("inf")            # no VQ_STAGE_SCALES flag
+    assert L.vq_validate(ctypes.byref(d)) == VQ_OK
+    d.flags = 1
+    d.stage_scale[1] = 0.5
+    d.stage_scale[2] = float("nan")            # beyond n_stages
+    assert L.vq_validate(ctypes.byref(d)) == VQ_OK
+
+
+@pytest.mark.parametrize("n,k,widths,bs", [(576, 576, [12, 4], 128), (3, 24, [12, 4], 24), (5, 40, [4], 8),
+                                           (7, 72, [16, 8], 72), (1, 8, [16, 16, 16, 8], 8), (9, 88, [8, 4, 12], 16)])
+def test_compressed_bytes_ladders(L, n, k, widths, bs):
+    d = fake_desc(n, k, len(widths), widths[0], bs, widths=widths)
+    assert L.vq_compressed_bytes(ctypes.byref(d)) == oracle.compressed_bytes(n, k, len(widths), widths, bs)
+
+
+@pytest.mark.parametrize("wl", ["smollm_rvq124", "llama8b_rvq124", "mlp70b_e8p3"])
+def test_ladder_workload_bytes(L, wl):
+    cfg = vqsynth.WORKLOADS[wl]
+    for _, n, k in cfg["shapes"]:
+        bs = k if cfg["scale_block"] is None else cfg["scale_block"]
+        d = fake_desc(n, k, cfg["stages"], cfg["bits"][0], bs, widths=list(cfg["bits"]))
+        assert L.vq_compressed_bytes(ctypes.byref(d)) == oracle.compressed_bytes(n, k, cfg["stages"], list(cfg["bits"]), bs)

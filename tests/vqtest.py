@@ -25,12 +25,13 @@ def device_weight(sw: vqsynth.SynthWeight, device="cuda"):
     from compressed_index_matmul_amd import VQWeight
     return VQWeight(sw.n_out, sw.k_in, sw.n_stages, sw.idx_bits, sw.scale_block,
                     codebooks=sw.codebooks, scales=sw.scales, lo=sw.lo, hi=sw.hi,
-                    idx16=sw.idx16, device=device)
+                    idx16=sw.idx16, device=device, stage_bits=sw.stage_bits,
+                    stage_scales=sw.stage_scales)
 
 
 def oracle_indices(sw: vqsynth.SynthWeight):
-    return [oracle.unpack_indices(sw.idx_bits, sw.n_groups, lo=sw.lo[t], hi=sw.hi[t], idx16=sw.idx16[t])
-            for t in range(sw.n_stages)]
+    return [oracle.unpack_indices(b, sw.n_groups, lo=sw.lo[t], hi=sw.hi[t], idx16=sw.idx16[t])
+            for t, b in enumerate(sw.widths)]
 
 
 def oracle_w64(sw: vqsynth.SynthWeight, rows=None, idx=None):
@@ -38,20 +39,24 @@ def oracle_w64(sw: vqsynth.SynthWeight, rows=None, idx=None):
     idx = oracle_indices(sw) if idx is None else idx
     g = sw.k_in // 8
     if rows is None:
-        return oracle.dequant_exact(sw.n_out, sw.k_in, idx, sw.codebooks, sw.scales, sw.scale_block)
+        return oracle.dequant_exact(sw.n_out, sw.k_in, idx, sw.codebooks, sw.scales, sw.scale_block,
+                                    sw.stage_scales)
     rows = np.asarray(rows)
     sub = [i.reshape(sw.n_out, g)[rows].reshape(-1) for i in idx]
-    return oracle.dequant_exact(len(rows), sw.k_in, sub, sw.codebooks, sw.scales[rows], sw.scale_block)
+    return oracle.dequant_exact(len(rows), sw.k_in, sub, sw.codebooks, sw.scales[rows], sw.scale_block,
+                                sw.stage_scales)
 
 
 def oracle_w16(sw: vqsynth.SynthWeight, rows=None, idx=None):
     idx = oracle_indices(sw) if idx is None else idx
     g = sw.k_in // 8
     if rows is None:
-        return oracle.dequant_fp16(sw.n_out, sw.k_in, idx, sw.codebooks, sw.scales, sw.scale_block)
+        return oracle.dequant_fp16(sw.n_out, sw.k_in, idx, sw.codebooks, sw.scales, sw.scale_block,
+                                   sw.stage_scales)
     rows = np.asarray(rows)
     sub = [i.reshape(sw.n_out, g)[rows].reshape(-1) for i in idx]
-    return oracle.dequant_fp16(len(rows), sw.k_in, sub, sw.codebooks, sw.scales[rows], sw.scale_block)
+    return oracle.dequant_fp16(len(rows), sw.k_in, sub, sw.codebooks, sw.scales[rows], sw.scale_block,
+                               sw.stage_scales)
 
 
 def sample_rows(n: int, count: int, seed: int):

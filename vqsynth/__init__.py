@@ -26,6 +26,18 @@ Workloads (one entry per weight format; shapes are nn.Linear [out, in]):
                 16-bit indices into a 65,536-entry codebook, one scale per row,
                 random +/-1 signs for the input Hadamard transform, bf16 x.
 * ``prefill``   2048 tokens x (4096x4096, 14336x4096) in the llama8b format.
+
+Residual ladders (per-stage index widths; optional per-stage residual
+scales, drawn after everything else so the formats above are unchanged):
+
+* ``smollm_rvq124``  SmolLM-135M linears in orka's rvq-12-4 mode: a 12-bit
+                     stage (4096 entries) plus a 4-bit stage (16 entries,
+                     std 0.3x), 2 bits per weight of indices.
+* ``llama8b_rvq124`` the Llama-3-8B linears in the same 12+4 format.
+* ``mlp70b_e8p3``    the 70B-MLP linears as GLQ's 3 bpw ladder: a 16-bit
+                     primary and an 8-bit residual stage whose codebook has
+                     the primary's spread, brought down by a residual scale
+                     drawn from U(0.2, 0.4); input transform as mlp70b.
 """
 
 from __future__ import annotations
@@ -45,17 +57,23 @@ class SynthWeight:
     n_out: int
     k_in: int
     n_stages: int
-    idx_bits: int
+    idx_bits: int                     # stage 0's width (every stage's for a uniform ladder)
     scale_block: int
     lo: List[Optional[np.ndarray]] = field(default_factory=list)
     hi: List[Optional[np.ndarray]] = field(default_factory=list)
     idx16: List[Optional[np.ndarray]] = field(default_factory=list)
     codebooks: List[np.ndarray] = field(default_factory=list)   # float16 [2^b, 8]
     scales: Optional[np.ndarray] = None                          # float16 [N, nblk]
+    stage_bits: Optional[List[int]] = None                       # per-stage widths (None: uniform)
+    stage_scales: Optional[np.ndarray] = None                    # float32 [S] (None: all 1)
 
     @property
     def n_groups(self) -> int:
         return self.n_out * (self.k_in // 8)
+
+    @property
+    def widths(self) -> List[int]:
+        return list(self.stage_bits) if self.stage_bits is not None else [self.idx_bits] * self.n_stages
 
 
 # name -> (shapes, stages, bits, codebook stds, scale_block (None = per row),
@@ -75,6 +93,16 @@ WORKLOADS: Dict[str, dict] = {
     "prefill": dict(shapes=[("qo", 4096, 4096), ("gate_up", 14336, 4096)], stages=2, bits=12,
                     cb_sd=(0.02, 0.006), scale_block=128, x_dtype="bf16", batches=(2048,), rht=None,
                     seed=4),
+    "smollm_rvq124": dict(shapes=[("q", 576, 576), ("k", 576, 576), ("v", 576, 576), ("o", 576, 576),
+                                  ("gate", 1536, 576), ("up", 1536, 576), ("down", 576, 1536)],
+                          stages=2, bits=(12, 4), cb_sd=(0.02, 0.006), scale_block=128, x_dtype="bf16",
+                          batches=(1,), rht=None, seed=5),
+    "llama8b_rvq124": dict(shapes=[("qo", 4096, 4096), ("gate_up", 14336, 4096), ("down", 4096, 14336)],
+                           stages=2, bits=(12, 4), cb_sd=(0.02, 0.006), scale_block=128, x_dtype="bf16",
+                           batches=(1, 16), rht=None, seed=6),
+    "mlp70b_e8p3": dict(shapes=[("gate_up", 28672, 8192), ("down", 8192, 28672)], stages=2, bits=(16, 8),
+                        cb_sd=(0.02, 0.02), scale_block=None, x_dtype="bf16", batches=(1,), rht=8192, seed=7,
+                        stage_scales=(0.2, 0.4)),
 }
 
 
@@ -93,28 +121,43 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def make_weight(name: str, n_out: int, k_in: int, n_stages: int, idx_bits: int,
+def make_weight(name: str, n_out: int, k_in: int, n_stages: int, idx_bits,
                 cb_sd: Tuple[float, ...], scale_block: Optional[int],
-                seed_seq: np.random.SeedSequence) -> SynthWeight:
-    """Draw one compressed weight.  Draw order per stage: codebook, indices;
-    then the scales."""
+                seed_seq: np.random.SeedSequence,
+                stage_scale_range: Optional[Tuple[float, float]] = None) -> SynthWeight:
+    """Draw one compressed weight.  ``idx_bits`` is one width for every stage
+    or a list of per-stage widths (4, 8, 12, 16).  Draw order per stage:
+    codebook, indices; then the scales; then, if ``stage_scale_range`` is
+    given, the residual scales of stages 1.. (uniform on the range, rounded
+    to float32; stage 0's is 1)."""
     if k_in % 8:
         raise ValueError("k_in must be a multiple of 8")
+    widths = [int(idx_bits)] * n_stages if np.isscalar(idx_bits) else [int(b) for b in idx_bits]
+    if len(widths) != n_stages:
+        raise ValueError("one index width per stage")
     bs = k_in if scale_block is None else scale_block
     rng = _rng(seed_seq)
-    w = SynthWeight(name, n_out, k_in, n_stages, idx_bits, bs)
+    w = SynthWeight(name, n_out, k_in, n_stages, widths[0], bs,
+                    stage_bits=None if len(set(widths)) == 1 else widths)
     ng = w.n_groups
-    for t in range(n_stages):
-        cb = (rng.standard_normal((1 << idx_bits, 8)) * cb_sd[t]).astype(np.float16)
+    for t, b in enumerate(widths):
+        cb = (rng.standard_normal((1 << b, 8)) * cb_sd[t]).astype(np.float16)
         w.codebooks.append(cb)
-        if idx_bits == 16:
+        if b == 16:
             w.idx16.append(rng.integers(0, 1 << 16, ng, dtype=np.uint16))
             w.lo.append(None)
             w.hi.append(None)
+        elif b == 4:
+            hi = rng.integers(0, 256, (ng + 1) // 2, dtype=np.uint8)
+            if ng % 2:
+                hi[-1] &= 0x0F
+            w.idx16.append(None)
+            w.lo.append(None)
+            w.hi.append(hi)
         else:
             w.idx16.append(None)
             w.lo.append(rng.integers(0, 256, ng, dtype=np.uint8))
-            if idx_bits == 12:
+            if b == 12:
                 hi = rng.integers(0, 256, (ng + 1) // 2, dtype=np.uint8)
                 if ng % 2:
                     hi[-1] &= 0x0F
@@ -123,6 +166,11 @@ def make_weight(name: str, n_out: int, k_in: int, n_stages: int, idx_bits: int,
                 w.hi.append(None)
     nblk = -(-k_in // bs)
     w.scales = rng.uniform(0.5, 1.5, (n_out, nblk)).astype(np.float16)
+    if stage_scale_range is not None:
+        lo_r, hi_r = stage_scale_range
+        rs = np.ones(n_stages, np.float32)
+        rs[1:] = rng.uniform(lo_r, hi_r, n_stages - 1).astype(np.float32)
+        w.stage_scales = rs
     return w
 
 
@@ -153,12 +201,13 @@ def workload_weights(workload: str, only: Optional[List[str]] = None, base_seed:
     for (nm, n, k), ss in zip(cfg["shapes"], kids[:-1]):
         if only is not None and nm not in only:
             continue
-        out.append(make_weight(nm, n, k, cfg["stages"], cfg["bits"], cfg["cb_sd"], cfg["scale_block"], ss))
+        out.append(make_weight(nm, n, k, cfg["stages"], cfg["bits"], cfg["cb_sd"], cfg["scale_block"], ss,
+                               cfg.get("stage_scales")))
     return out, kids[-1]
 
 
-def random_weight(n_out, k_in, n_stages, idx_bits, scale_block, seed, cb_sd=None):
+def random_weight(n_out, k_in, n_stages, idx_bits, scale_block, seed, cb_sd=None, stage_scale_range=None):
     """A weight of any shape/format for ragged and edge-case tests."""
     sd = cb_sd or tuple(0.02 * (0.3 ** t) for t in range(n_stages))
     return make_weight(f"r{n_out}x{k_in}", n_out, k_in, n_stages, idx_bits, sd, scale_block,
-                       np.random.SeedSequence(seed))
+                       np.random.SeedSequence(seed), stage_scale_range)
