@@ -11,7 +11,9 @@ its indices from HBM, not from the 256 MiB Infinity Cache or the L2.
 
 The same JSON line carries, under ``detail``, the other workloads measured
 the same way (70B-MLP RHT + 16-bit GEMV, batch-16 decode, 2048-token GEMM in
-TFLOP/s, tiny and SmolLM-shaped linears in microseconds, standalone dequant),
+TFLOP/s, tiny and SmolLM-shaped linears in microseconds, standalone dequant,
+and the residual-ladder formats: rvq-12-4 on the SmolLM and Llama-3-8B
+shapes, a 16 + 8-bit ladder with a residual scale on the 70B-MLP shapes),
 ``roofline`` for the dominant kernel of the headline step (HIP-event kernel
 times on the launch stream), and ``cpu_baseline``: the float64 oracle timed
 on the host on one full headline step.
@@ -202,10 +204,11 @@ def run_decode_leg(vq, workload, steps, warmup, batch=1, rht=False):
             "linears": per, "batch": batch}
 
 
-def run_gemm_leg(vq, steps, warmup):
+def run_gemm_leg(vq, steps, warmup, workload="prefill", only=None):
+    """2048-token vq_gemm over the linears of `workload` (TFLOP/s)."""
     import torch
     import vqsynth
-    ws, act_ss = vqsynth.workload_weights("prefill")
+    ws, act_ss = vqsynth.workload_weights(workload, only=only)
     kids = act_ss.spawn(len(ws))
     res = []
     for i, sw in enumerate(ws):
@@ -248,16 +251,19 @@ def run_dequant_leg(vq, steps, warmup):
 # ----------------------------------------------------------------------------
 
 def compressed_bytes(sw):
+    """Index planes + fp16 scales + fp16 codebooks, each once (per group and
+    stage: 16-bit 2 B, 12-bit 1.5 B, 8-bit 1 B, 4-bit 0.5 B)."""
     g = sw.n_out * (sw.k_in // 8)
-    per = {8: g, 12: g + (g + 1) // 2, 16: 2 * g}[sw.idx_bits]
+    per = {4: (g + 1) // 2, 8: g, 12: g + (g + 1) // 2, 16: 2 * g}
     nblk = -(-sw.k_in // sw.scale_block)
-    return sw.n_stages * per + 2 * sw.n_out * nblk + sw.n_stages * (1 << sw.idx_bits) * 16
+    return sum(per[b] + (1 << b) * 16 for b in sw.widths) + 2 * sw.n_out * nblk
 
 
 def device_weight_(sw):
     from compressed_index_matmul_amd import VQWeight
     return VQWeight(sw.n_out, sw.k_in, sw.n_stages, sw.idx_bits, sw.scale_block, codebooks=sw.codebooks,
-                    scales=sw.scales, lo=sw.lo, hi=sw.hi, idx16=sw.idx16, device="cuda")
+                    scales=sw.scales, lo=sw.lo, hi=sw.hi, idx16=sw.idx16, device="cuda",
+                    stage_bits=sw.stage_bits, stage_scales=sw.stage_scales)
 
 
 def cpu_baseline():
@@ -290,7 +296,8 @@ def cpu_baseline():
             "seconds": dt, "host_cpus": os.cpu_count()}
 
 
-KERNEL_SOURCES = ["compressed_index_matmul_amd/csrc/k_gemv.hip", "compressed_index_matmul_amd/csrc/vqmm_device.h"]
+KERNEL_SOURCES = ["compressed_index_matmul_amd/csrc/k_gemv.hip", "compressed_index_matmul_amd/csrc/gemv_kernels.h",
+                  "compressed_index_matmul_amd/csrc/vqmm_device.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemv_lds_llama8b_down_4096x14336_traffic.json")
 COPY_BYTES = 256 << 20
 
@@ -412,7 +419,16 @@ def main():
                 ("prefill_gemm_m2048", lambda: run_gemm_leg(vq, max(5, args.steps // 5), 3)),
                 ("smollm_gemv_b1", lambda: run_decode_leg(vq, "smollm", args.steps, args.warmup)),
                 ("tiny_gemv_b1", lambda: run_decode_leg(vq, "tiny", args.steps, args.warmup)),
-                ("dequant_14336x4096", lambda: run_dequant_leg(vq, args.steps, args.warmup))]
+                ("dequant_14336x4096", lambda: run_dequant_leg(vq, args.steps, args.warmup)),
+                # residual ladders: orka's rvq-12-4 (12 + 4 bits), GLQ's 3 bpw 16 + 8 with a residual scale
+                ("smollm_rvq124_gemv_b1", lambda: run_decode_leg(vq, "smollm_rvq124", args.steps, args.warmup)),
+                ("llama8b_rvq124_gemv_b1", lambda: run_decode_leg(vq, "llama8b_rvq124", args.steps, args.warmup)),
+                ("llama8b_rvq124_gemv_b16", lambda: run_decode_leg(vq, "llama8b_rvq124", args.steps, args.warmup,
+                                                                   batch=16)),
+                ("llama8b_rvq124_gemm_m2048", lambda: run_gemm_leg(vq, max(5, args.steps // 5), 3, "llama8b_rvq124",
+                                                                   only=["qo", "gate_up"])),
+                ("mlp70b_e8p3_rht_gemv_b1", lambda: run_decode_leg(vq, "mlp70b_e8p3", max(5, args.steps // 5), 3,
+                                                                   rht=True))]
         for name, fn in legs:
             if only and name not in only:
                 continue

@@ -118,30 +118,19 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
   // landed; the HBM latency of the index loads then overlaps the x
   // conversion and the barrier.  No branch surrounds an index load:
   // out-of-range chunks and rows load a valid duplicate and are discarded.
+  if constexpr (LD::kBlocks && LD::kUniform) {
 #pragma unroll
-  for (int r = 0; r < CB_ITERS; ++r) {
-    const int blk = (r * WAVES + wave) * 64;  // first codebook row of this wave's 1 KiB
-    if (blk < CBN) {
-      if constexpr (LD::kBlocks && LD::kUniform) {
+    for (int r = 0; r < CB_ITERS; ++r) {
+      const int blk = (r * WAVES + wave) * 64;  // first codebook row of this wave's 1 KiB
+      if (blk < CBN) {
         // a whole block of one stage (wave-uniform stage)
         constexpr int B = LD::bits(0);
         const uint4 *src = reinterpret_cast<const uint4 *>(a.cb[blk >> B]) + (blk & ((1 << B) - 1)) + lane;
         lds_direct_16(src, s_cb + blk);
-      } else if constexpr (LD::kBlocks) {
-        const int t = LD::stage_of(blk);
-        const uint4 *src = reinterpret_cast<const uint4 *>(a.cb[t]) + (blk - LD::off(t)) + lane;
-        lds_direct_16(src, s_cb + blk);
-      } else {
-        // 16-row (4-bit) codebooks: the block may span stages and end early;
-        // each lane copies its own row, lanes past the last row copy nothing
-        const int row = blk + lane;
-        if (row < CBN) {
-          const int t = LD::stage_of(row);
-          const uint4 *src = reinterpret_cast<const uint4 *>(a.cb[t]) + (row - LD::off(t));
-          lds_direct_16(src, s_cb + blk);
-        }
       }
     }
+  } else {
+    stage_ladder_lds<LD, WAVES>(a.cb, s_cb, wave, lane);  // mixed widths
   }
   sched_fence();
   // (waves whose x chunks all lie past the end of x load none: a

@@ -88,6 +88,17 @@ __device__ __forceinline__ void lds_direct_16(const void *src, void *lds_wave_ba
 #endif
 }
 
+// A wave-uniform pointer as a value held in scalar registers.  Selecting
+// between such values cannot be folded back into a load from a computed
+// address in the kernel-argument block (which, with a per-lane selector,
+// becomes a vector load and a wait).
+__device__ __forceinline__ const void *uniform_ptr(const void *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const void *>(((uint64_t)hi << 32) | lo);
+}
+
 // Scheduling fence: the compiler may not move instructions across it (keeps
 // prefetch loads where they are issued instead of sinking them to their use).
 __device__ __forceinline__ void sched_fence() {
@@ -248,5 +259,40 @@ struct Ladder {
     return (S > 1 && row >= off(1)) + (S > 2 && row >= off(2)) + (S > 3 && row >= off(3));
   }
 };
+
+// Copy the codebooks of a mixed-width ladder LD into LDS, back to back (stage
+// t from row LD::off(t)), with LDS-direct loads: NW waves, 64 rows (1 KiB)
+// per wave and load.  A block inside one stage is one load from a
+// wave-uniform stage; a block that spans stages or ends early (16-row 4-bit
+// codebooks) is copied row by row, lanes past the last row masked off.  The
+// stage pointers are selected among values held in scalar registers (an
+// index into the argument array would become a vector load and a wait
+// before every block).  The caller waits for the loads and synchronises.
+template <class LD, int NW>
+__device__ __forceinline__ void stage_ladder_lds(const uint16_t *const *cb, uint4 *s_cb, int wave, int lane) {
+  constexpr int S = LD::S;
+  constexpr int CBN = LD::kRows;
+  const uint4 *cb0 = static_cast<const uint4 *>(uniform_ptr(cb[0]));
+  const uint4 *cb1 = static_cast<const uint4 *>(uniform_ptr(S > 1 ? cb[1] : cb[0]));
+  const uint4 *cb2 = static_cast<const uint4 *>(uniform_ptr(S > 2 ? cb[2] : cb[0]));
+  const uint4 *cb3 = static_cast<const uint4 *>(uniform_ptr(S > 3 ? cb[3] : cb[0]));
+  auto cbp = [&](int t) { return t == 0 ? cb0 : t == 1 ? cb1 : t == 2 ? cb2 : cb3; };
+#pragma unroll
+  for (int r = 0; r < (CBN + NW * 64 - 1) / (NW * 64); ++r) {
+    const int blk = (r * NW + wave) * 64;  // wave-uniform
+    if (blk < CBN) {
+      const int t0 = LD::stage_of(blk);
+      if (blk + 64 <= LD::off(t0) + ladder_rows(LD::bits(t0))) {
+        lds_direct_16(cbp(t0) + (blk - LD::off(t0)) + lane, s_cb + blk);
+      } else {
+        const int row = blk + lane;
+        if (row < CBN) {
+          const int t = LD::stage_of(row);
+          lds_direct_16(cbp(t) + (row - LD::off(t)), s_cb + blk);
+        }
+      }
+    }
+  }
+}
 
 }  // namespace vqmm

@@ -218,3 +218,33 @@ def test_ladder_workload_rht_gemv_mlp70b(vq):
         rows = sample_rows(sw.n_out, 48, 400 + i)
         y_ref, bound = oracle.matmul_ref(oracle_w64(sw, rows), oracle.rht_ref(x64, signs, 8192))
         assert_within(y.cpu().numpy()[:, rows], y_ref, bound, f"mlp70b_e8p3/{sw.name}")
+
+
+# shapes that route to each tuned matrix-core kernel: the 1..64-token unit
+# kernel (N/16 units >= half the CUs, K % 256, 128-column scale blocks), the
+# 256 x 128 tile kernel, and the 256 x 256 wide kernel (one tile per CU)
+TUNED = {"few": (4096, 1024, 128, (1, 16, 17, 64)), "tile": (1000, 1024, 128, (300,)),
+         "wide": (8192, 256, 128, (2048,))}
+
+
+@pytest.mark.parametrize("fmt", [((12, 4), None), ((8, 4), (0.5, 1.5)), ((12, 4), (0.2, 0.4)), ((12, 12), (0.2, 0.4)),
+                                 ((12,), (0.5, 2.0)), ((8, 8), (-2.0, -0.5))], ids=fmt_id)
+@pytest.mark.parametrize("kern", list(TUNED))
+def test_ladder_tuned_gemm_kernels(vq, fmt, kern):
+    import torch
+    widths, rs = fmt
+    n, k, bs, ms = TUNED[kern]
+    sw = make(widths, rs, n, k, bs, seed=97 + n, first_scale=1.5 if rs else None)
+    w = device_weight(sw)
+    rows = sample_rows(n, 64, 7)
+    w64 = oracle_w64(sw, rows)
+    for m in ms:
+        xs, x64 = vqsynth.make_x(m, k, "bf16", np.random.SeedSequence(1000 + m))
+        y = vq.vq_gemm(w, x_to_device(xs, "bf16"))
+        torch.cuda.synchronize()
+        y_ref, bound = oracle.matmul_ref(w64, x64)
+        assert_within(y.cpu().numpy()[:, rows], y_ref, bound, f"{fmt_id(fmt)} {kern} m={m} sampled rows")
+        if kern == "wide":  # every W row for a few tokens
+            toks = sample_rows(m, 8, 3)
+            y_ref2, bound2 = oracle.matmul_ref(oracle_w64(sw), x64[toks])
+            assert_within(y.cpu().numpy()[toks], y_ref2, bound2, f"{fmt_id(fmt)} wide token rows")
