@@ -18,7 +18,8 @@ from the two source pages:
   stages on a 16-bit primary), and the two-stage call of "Inference kernels",
   which passes an inverse residual scale.
 * orka README, quick start: the ``rvq-12-4`` quant mode (a 12-bit primary
-  stage and a 4-bit residual stage, about 2 bits per weight).
+  stage and a 4-bit residual stage, about 2 bits per weight); "How it works"
+  and the ``correct`` command: the decode may add a sparse correction.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
 leg may import this package.  It shares no code with the HIP library and
@@ -45,6 +46,7 @@ __all__ = [
     "n_scale_blocks",
     "dequant_exact",
     "dequant_fp16",
+    "sparse_dense",
     "matmul_ref",
     "within_tolerance",
     "rht_blocks",
@@ -150,7 +152,8 @@ def n_scale_blocks(k_in: int, scale_block: int) -> int:
 
 def dequant_exact(n_out: int, k_in: int, indices: Sequence[np.ndarray],
                   codebooks: Sequence[np.ndarray], scales: np.ndarray,
-                  scale_block: int, stage_scales: Optional[Sequence[float]] = None) -> np.ndarray:
+                  scale_block: int, stage_scales: Optional[Sequence[float]] = None,
+                  sparse=None) -> np.ndarray:
     """Dequantized weight, float64, shape ``[n_out, k_in]``.
 
     orka README, "How it works": a group decodes to the scale times the sum of
@@ -206,22 +209,54 @@ def dequant_exact(n_out: int, k_in: int, indices: Sequence[np.ndarray],
     for g in range(g_per_row):
         blk = (GROUP * g) // scale_block
         w[:, GROUP * g:GROUP * (g + 1)] = s[:, blk:blk + 1] * acc[:, g, :]
+    if sparse is not None:
+        rowptr, col, val = _check_sparse(n_out, k_in, sparse)
+        for r in range(n_out):
+            for j in range(rowptr[r], rowptr[r + 1]):
+                w[r, col[j]] = w[r, col[j]] + val[j]
     return w
 
 
+def _check_sparse(n_out: int, k_in: int, sparse):
+    rowptr, col, val = sparse
+    rowptr = np.asarray(rowptr, dtype=np.int64)
+    col = np.asarray(col, dtype=np.int64)
+    val = np.asarray(val, dtype=np.float16).astype(np.float64)
+    if rowptr.shape != (n_out + 1,) or rowptr[0] != 0 or np.any(np.diff(rowptr) < 0):
+        raise ValueError("rowptr must have n_out + 1 non-decreasing entries starting at 0")
+    nnz = int(rowptr[-1])
+    if col.size < nnz or val.size < nnz:
+        raise ValueError("col and val need rowptr[n_out] entries")
+    if nnz and (col[:nnz].min() < 0 or col[:nnz].max() >= k_in):
+        raise ValueError("column out of range")
+    return rowptr, col, val
+
+
+def sparse_dense(n_out: int, k_in: int, sparse) -> np.ndarray:
+    """The sparse correction alone as a dense float64 [n_out, k_in] matrix
+    (entries of one row added in storage order)."""
+    rowptr, col, val = _check_sparse(n_out, k_in, sparse)
+    d = np.zeros((n_out, k_in), dtype=np.float64)
+    for r in range(n_out):
+        for j in range(rowptr[r], rowptr[r + 1]):
+            d[r, col[j]] += val[j]
+    return d
+
+
 def dequant_fp16(n_out, k_in, indices, codebooks, scales, scale_block,
-                 stage_scales=None) -> np.ndarray:
+                 stage_scales=None, sparse=None) -> np.ndarray:
     """fp16 dequantized weight: the float64 value rounded once to nearest-even.
 
     Reading: the pages fix no rounding; the result is the float64 value of
     :func:`dequant_exact` (exact without stage scales, the stated evaluation
-    order with them) converted once to IEEE binary16 with
+    order with them, plus the sparse correction if any) converted once to
+    IEEE binary16 with
     round-to-nearest-even (numpy's float64 -> float16 cast rounds once; the
     tests check it against Python's own half-float packing).  Subnormals are
     kept, overflow gives +/-inf, a zero result keeps the sign IEEE gives it.
     """
     return dequant_exact(n_out, k_in, indices, codebooks, scales, scale_block,
-                         stage_scales).astype(np.float16)
+                         stage_scales, sparse).astype(np.float16)
 
 
 # --------------------------------------------------------------------------

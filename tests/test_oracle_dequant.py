@@ -245,3 +245,83 @@ def test_stage_scales_validated():
         oracle.dequant_exact(1, 8, idx, cb, sc, 8, stage_scales=[1.0])
     with pytest.raises(ValueError):
         oracle.dequant_exact(1, 8, idx, cb, sc, 8, stage_scales=[1.0, float("inf")])
+
+
+# ---------------------------------------------------------------------------
+# sparse correction
+# ---------------------------------------------------------------------------
+
+def _sparse_case():
+    with open(os.path.join(GOLDEN, "sparse_hand.json")) as f:
+        return json.load(f)["cases"][0]
+
+
+def test_sparse_hand():
+    c = _sparse_case()
+    cb = np.array(c["codebook"], np.float16)
+    sp = (np.array(c["rowptr"]), np.array(c["col"]), np.array(c["val"], np.float16))
+    w = oracle.dequant_fp16(c["n_out"], c["k_in"], [np.array(c["indices"])], [cb],
+                            np.array(c["scales"], np.float16), c["scale_block"], sparse=sp)
+    want = np.array(c["w"], np.float16)
+    assert np.array_equal(w.view(np.uint16), want.view(np.uint16))
+
+
+def test_sparse_alone_and_linearity():
+    """With an all-zero codebook the weight is the correction alone; in
+    general the correction adds exactly (small dyadic-free values whose sums
+    are exact in float64)."""
+    rng = np.random.default_rng(8)
+    n, k = 7, 64
+    nnz_row = rng.integers(0, 6, n)
+    rowptr = np.concatenate([[0], np.cumsum(nnz_row)])
+    col = np.concatenate([np.sort(rng.choice(k, m, replace=False)) for m in nnz_row]).astype(np.int64)
+    val = (rng.standard_normal(rowptr[-1]) * 0.1).astype(np.float16)
+    sp = (rowptr, col, val)
+    idx = [rng.integers(0, 256, n * k // 8)]
+    sc = rng.uniform(0.5, 1.5, (n, 2)).astype(np.float16)
+    zero = [np.zeros((256, 8), np.float16)]
+    assert np.array_equal(oracle.dequant_exact(n, k, idx, zero, sc, 32, sparse=sp), oracle.sparse_dense(n, k, sp))
+    cb = [(rng.standard_normal((256, 8)) * 0.02).astype(np.float16)]
+    base = oracle.dequant_exact(n, k, idx, cb, sc, 32)
+    withc = oracle.dequant_exact(n, k, idx, cb, sc, 32, sparse=sp)
+    dense = oracle.sparse_dense(n, k, sp)
+    assert np.allclose(withc, base + dense, rtol=0, atol=1e-15)
+    assert np.array_equal(withc[dense == 0], base[dense == 0])
+    empty = (np.zeros(n + 1, np.int64), np.zeros(0, np.int64), np.zeros(0, np.float16))
+    assert np.array_equal(oracle.dequant_exact(n, k, idx, cb, sc, 32, sparse=empty), base)
+
+
+def test_sparse_fraction_brute_force():
+    """Exact rational decode + correction, rounded by hand, equals the oracle's
+    fp16 (12+4 ladder with stage scales and a correction with repeated
+    columns)."""
+    rng = np.random.default_rng(21)
+    n, k, bs = 3, 32, 16
+    cbs = [(rng.standard_normal((1 << b, 8)) * 0.02).astype(np.float16) for b in (12, 4)]
+    idx = [rng.integers(0, 1 << b, n * k // 8) for b in (12, 4)]
+    sc = rng.uniform(0.5, 1.5, (n, 2)).astype(np.float16)
+    rs = np.array([1.0, 0.3], np.float32)
+    rowptr = np.array([0, 4, 4, 9])
+    col = np.array([0, 5, 5, 31, 1, 2, 2, 2, 30])
+    val = (rng.standard_normal(9) * 0.01).astype(np.float16)
+    sp = (rowptr, col, val)
+    w = oracle.dequant_fp16(n, k, idx, cbs, sc, bs, stage_scales=rs, sparse=sp)
+    for r in range(n):
+        for c in range(k):
+            f = r * (k // 8) + c // 8
+            q = Fraction(float(sc[r, c // bs])) * sum(Fraction(float(rs[t])) * Fraction(float(cbs[t][idx[t][f], c % 8]))
+                                                     for t in range(2))
+            q += sum(Fraction(float(val[j])) for j in range(rowptr[r], rowptr[r + 1]) if col[j] == c)
+            assert int(w.view(np.uint16)[r, c]) == fraction_to_half_bits(q), (r, c)
+
+
+def test_sparse_validated():
+    cb = [np.ones((256, 8), np.float16)]
+    idx = [np.zeros(2, np.int64)]
+    sc = np.ones((1, 1), np.float16)
+    for bad in [([0, 2], [0, 16], [1.0, 1.0]),       # column out of range
+                ([1, 2], [0, 1], [1.0, 1.0]),        # rowptr[0] != 0
+                ([0, 3], [0, 1], [1.0, 1.0]),        # too few entries
+                ([0], [], [])]:                      # wrong rowptr length
+        with pytest.raises(ValueError):
+            oracle.dequant_exact(1, 16, idx, cb, sc, 16, sparse=tuple(np.array(v) for v in bad))

@@ -113,3 +113,24 @@ def test_tolerance_predicate():
     assert ok.all() and abs(worst - 1.0) < 1e-9
     ok, _ = oracle.within_tolerance(y_ref + np.array([0.0201, 0.0, 0.0]), y_ref, bound)
     assert not ok[0] and ok[1:].all()
+
+
+def test_one_hot_recovers_corrected_column():
+    """One-hot x = e_k picks column k of the decoded weight plus its sparse
+    correction exactly."""
+    rng = np.random.default_rng(33)
+    n, k = 9, 40
+    cb = [(rng.standard_normal((256, 8)) * 0.02).astype(np.float16)]
+    idx = [rng.integers(0, 256, n * k // 8)]
+    sc = rng.uniform(0.5, 1.5, (n, 5)).astype(np.float16)
+    rowptr = np.array([0, 1, 1, 3, 3, 3, 4, 4, 4, 6])
+    col = np.array([7, 7, 7, 39, 0, 7])
+    val = np.array([0.5, -0.25, 0.125, 1.0, 2.0, -1.0], np.float16)
+    w64 = oracle.dequant_exact(n, k, idx, cb, sc, 8, sparse=(rowptr, col, val))
+    plain = oracle.dequant_exact(n, k, idx, cb, sc, 8)
+    x = np.zeros((1, k))
+    x[0, 7] = 1.0
+    y, _ = oracle.matmul_ref(w64, x)
+    assert np.array_equal(y[0], w64[:, 7])
+    assert y[0, 0] == plain[0, 7] + 0.5 and y[0, 2] == plain[2, 7] + (-0.25 + 0.125) and y[0, 8] == plain[8, 7] - 1.0
+    assert y[0, 1] == plain[1, 7]
