@@ -12,8 +12,9 @@ its indices from HBM, not from the 256 MiB Infinity Cache or the L2.
 The same JSON line carries, under ``detail``, the other workloads measured
 the same way (70B-MLP RHT + 16-bit GEMV, batch-16 decode, 2048-token GEMM in
 TFLOP/s, tiny and SmolLM-shaped linears in microseconds, standalone dequant,
-and the residual-ladder formats: rvq-12-4 on the SmolLM and Llama-3-8B
-shapes, a 16 + 8-bit ladder with a residual scale on the 70B-MLP shapes),
+the residual-ladder formats: rvq-12-4 on the SmolLM and Llama-3-8B
+shapes, a 16 + 8-bit ladder with a residual scale on the 70B-MLP shapes,
+and the headline format with a 0.5 % sparse correction),
 ``roofline`` for the dominant kernel of the headline step (HIP-event kernel
 times on the launch stream), and ``cpu_baseline``: the float64 oracle timed
 on the host on one full headline step.
@@ -256,14 +257,15 @@ def compressed_bytes(sw):
     g = sw.n_out * (sw.k_in // 8)
     per = {4: (g + 1) // 2, 8: g, 12: g + (g + 1) // 2, 16: 2 * g}
     nblk = -(-sw.k_in // sw.scale_block)
-    return sum(per[b] + (1 << b) * 16 for b in sw.widths) + 2 * sw.n_out * nblk
+    sp = 0 if sw.sparse is None else 4 * (sw.n_out + 1) + 6 * int(sw.sparse[0][-1])
+    return sum(per[b] + (1 << b) * 16 for b in sw.widths) + 2 * sw.n_out * nblk + sp
 
 
 def device_weight_(sw):
     from compressed_index_matmul_amd import VQWeight
     return VQWeight(sw.n_out, sw.k_in, sw.n_stages, sw.idx_bits, sw.scale_block, codebooks=sw.codebooks,
                     scales=sw.scales, lo=sw.lo, hi=sw.hi, idx16=sw.idx16, device="cuda",
-                    stage_bits=sw.stage_bits, stage_scales=sw.stage_scales)
+                    stage_bits=sw.stage_bits, stage_scales=sw.stage_scales, sparse=sw.sparse)
 
 
 def cpu_baseline():
@@ -428,7 +430,11 @@ def main():
                 ("llama8b_rvq124_gemm_m2048", lambda: run_gemm_leg(vq, max(5, args.steps // 5), 3, "llama8b_rvq124",
                                                                    only=["qo", "gate_up"])),
                 ("mlp70b_e8p3_rht_gemv_b1", lambda: run_decode_leg(vq, "mlp70b_e8p3", max(5, args.steps // 5), 3,
-                                                                   rht=True))]
+                                                                   rht=True)),
+                # sparse correction (0.5 % of the weights) on the headline format
+                ("llama8b_sparse_gemv_b1", lambda: run_decode_leg(vq, "llama8b_sparse", args.steps, args.warmup)),
+                ("llama8b_sparse_gemv_b16", lambda: run_decode_leg(vq, "llama8b_sparse", args.steps, args.warmup,
+                                                                   batch=16))]
         for name, fn in legs:
             if only and name not in only:
                 continue

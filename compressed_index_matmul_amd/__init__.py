@@ -55,6 +55,11 @@ class VQWeightDesc(ctypes.Structure):
         ("scales", ctypes.c_void_p),
         ("stage_bits", _int4),
         ("stage_scale", _flt4),
+        ("sp_nnz", ctypes.c_int32),
+        ("sp_reserved", ctypes.c_int32),
+        ("sp_rowptr", ctypes.c_void_p),
+        ("sp_col", ctypes.c_void_p),
+        ("sp_val", ctypes.c_void_p),
     ]
 
 
@@ -134,13 +139,14 @@ class VQWeight:
     The tensors are kept alive by this object; the descriptor holds their
     raw device addresses.  ``stage_bits`` (optional) gives each stage its own
     index width (4, 8, 12 or 16); ``stage_scales`` (optional) one float
-    residual scale per stage.
+    residual scale per stage; ``sparse`` (optional) a CSR correction
+    ``(rowptr, col, val)`` added to the decoded weight.
     """
 
     def __init__(self, n_out: int, k_in: int, n_stages: int, idx_bits: int, scale_block: int,
                  codebooks: Sequence, scales, lo: Sequence = (), hi: Sequence = (),
                  idx16: Sequence = (), device="cuda", stage_bits: Optional[Sequence[int]] = None,
-                 stage_scales: Optional[Sequence[float]] = None):
+                 stage_scales: Optional[Sequence[float]] = None, sparse=None):
         import torch
         self.n_out, self.k_in, self.n_stages, self.idx_bits = n_out, k_in, n_stages, idx_bits
         self.scale_block = scale_block
@@ -152,6 +158,12 @@ class VQWeight:
         self.lo = [None if v is None else _as_device(v, self.device, torch.uint8) for v in lo]
         self.hi = [None if v is None else _as_device(v, self.device, torch.uint8) for v in hi]
         self.idx16 = [None if v is None else _as_device(v, self.device, torch.int16) for v in idx16]
+        self.sparse = None
+        if sparse is not None:
+            rp, cl, vl = sparse
+            self.sparse = (_as_device(np.asarray(rp, np.int32), self.device, torch.int32),
+                           _as_device(np.asarray(cl, np.int32), self.device, torch.int32),
+                           _as_device(np.asarray(vl, np.float16), self.device, torch.float16))
         self.desc = VQWeightDesc()
         self._fill_desc()
 
@@ -170,6 +182,11 @@ class VQWeight:
             d.idx16[t] = self.idx16[t].data_ptr() if t < len(self.idx16) and self.idx16[t] is not None else None
             d.codebook[t] = self.codebooks[t].data_ptr() if t < len(self.codebooks) else None
         d.scales = self.scales.data_ptr()
+        nnz = 0 if self.sparse is None else int(self.sparse[1].numel())
+        d.sp_nnz, d.sp_reserved = nnz, 0
+        d.sp_rowptr = self.sparse[0].data_ptr() if nnz else None
+        d.sp_col = self.sparse[1].data_ptr() if nnz else None
+        d.sp_val = self.sparse[2].data_ptr() if nnz else None
 
     def clone(self) -> "VQWeight":
         """Another copy of the same weight at distinct device addresses."""
@@ -180,12 +197,14 @@ class VQWeight:
         w.lo = [None if v is None else v.clone() for v in self.lo]
         w.hi = [None if v is None else v.clone() for v in self.hi]
         w.idx16 = [None if v is None else v.clone() for v in self.idx16]
+        w.sparse = None if self.sparse is None else tuple(t.clone() for t in self.sparse)
         w.desc = VQWeightDesc()
         w._fill_desc()
         return w
 
     def nbytes_device(self) -> int:
-        ts = [*self.codebooks, self.scales, *[v for v in self.lo + self.hi + self.idx16 if v is not None]]
+        ts = [*self.codebooks, self.scales, *[v for v in self.lo + self.hi + self.idx16 if v is not None],
+              *(self.sparse or ())]
         return sum(t.numel() * t.element_size() for t in ts)
 
     def ref(self):

@@ -6,7 +6,10 @@
 // formed in float64, where they are exact (at most four fp16 terms and an
 // fp16 factor need < 53 significant bits), and rounded once to fp16 with
 // integer arithmetic on the bit pattern, so the result is the correctly
-// rounded value whatever the summation order.  Write-bandwidth bound.
+// rounded value whatever the summation order.  Write-bandwidth bound.  A
+// sparse correction (orka README, "How it works": the decode plus a sparse
+// correction) is added to the float64 value entry by entry, in storage
+// order, before the one rounding.
 //
 // Residual ladders (per-stage widths) and stage scales (GLQ page, "Inference
 // kernels": the inverse residual scale of the two-stage call) take the
@@ -32,6 +35,10 @@ struct DequantArgs {
   int G, S, bits, bs, nblk, k;
   int sb[VQ_MAX_STAGES];    // index width of each stage
   float rs[VQ_MAX_STAGES];  // stage scales
+  int sp_nnz;               // sparse correction (CSR over rows), 0 = none
+  const int32_t *sp_rowptr;
+  const int32_t *sp_col;
+  const uint16_t *sp_val;
 };
 
 // BITS: the width of every stage, or 0 for per-stage widths and scales.
@@ -58,11 +65,34 @@ __global__ __launch_bounds__(256) void k_unpack_dequant(DequantArgs a) {
   }
   if (!a.w_out) return;
   const double s = (double)h2f(a.sc[r * a.nblk + (8 * g) / a.bs]);
+  double wv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) wv[j] = s * acc[j];
+  if (a.sp_nnz > 0) {
+    // entries of row r in this group's columns: lower bound of column 8g in
+    // the row's ascending columns, then forward in storage order (each
+    // addition rounded to float64); the row range is clamped to the arrays
+    const int lo = min(max(a.sp_rowptr[r], 0), a.sp_nnz);
+    const int hi = min(max(a.sp_rowptr[r + 1], lo), a.sp_nnz);
+    int b0 = lo, b1 = hi;
+    while (b0 < b1) {
+      const int mid = (b0 + b1) >> 1;
+      if (a.sp_col[mid] < 8 * g) b0 = mid + 1;
+      else b1 = mid;
+    }
+    for (int j = b0; j < hi; ++j) {
+      const int c = a.sp_col[j] - 8 * g;
+      if (c >= 8) break;
+      if (c < 0) continue;
+      const double v = (double)h2f(a.sp_val[j]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q == c) wv[q] = wv[q] + v;
+    }
+  }
   uint32_t o[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    o[j] = f64_to_f16_rne(s * acc[2 * j]) | (f64_to_f16_rne(s * acc[2 * j + 1]) << 16);
-  }
+  for (int j = 0; j < 4; ++j) o[j] = f64_to_f16_rne(wv[2 * j]) | (f64_to_f16_rne(wv[2 * j + 1]) << 16);
   reinterpret_cast<uint4 *>(a.w_out + r * (int64_t)a.k)[g] = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
@@ -88,6 +118,10 @@ hipError_t launch_unpack_dequant(const WView &w, uint16_t *idx_out, uint16_t *w_
     a.sb[t] = t < w.S ? w.sb[t] : 0;
     a.rs[t] = w.rs[t];
   }
+  a.sp_nnz = w.sp_nnz;
+  a.sp_rowptr = w.sp_rowptr;
+  a.sp_col = w.sp_col;
+  a.sp_val = w.sp_val;
   const unsigned blocks = (unsigned)((a.total + 255) / 256);
   if (!plain_format(w))
     hipLaunchKernelGGL(k_unpack_dequant<0>, dim3(blocks), dim3(256), 0, s, a);

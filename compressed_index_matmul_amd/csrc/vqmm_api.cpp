@@ -47,6 +47,11 @@ int check_weight(const vq_weight *w, WView *v) {
   }
   if (!w->scales) return VQ_ERR_NULL;
   if (!aligned16(w->scales)) return VQ_ERR_ALIGN;
+  if (w->sp_nnz < 0 || w->sp_reserved != 0) return VQ_ERR_SHAPE;
+  if (w->sp_nnz > 0) {
+    if (!w->sp_rowptr || !w->sp_col || !w->sp_val) return VQ_ERR_NULL;
+    if (!aligned16(w->sp_rowptr) || !aligned16(w->sp_col) || !aligned16(w->sp_val)) return VQ_ERR_ALIGN;
+  }
   if (v) {
     *v = WView{};
     v->n = w->n_out;
@@ -74,6 +79,10 @@ int check_weight(const vq_weight *w, WView *v) {
       v->cb[t] = w->codebook[t];
     }
     v->sc = w->scales;
+    v->sp_nnz = w->sp_nnz;
+    v->sp_rowptr = w->sp_nnz > 0 ? w->sp_rowptr : nullptr;
+    v->sp_col = w->sp_nnz > 0 ? w->sp_col : nullptr;
+    v->sp_val = w->sp_nnz > 0 ? w->sp_val : nullptr;
   }
   return VQ_OK;
 }
@@ -128,6 +137,7 @@ int64_t vq_compressed_bytes(const vq_weight *w) {
     total += b == 16 ? 2 * groups : b == 12 ? groups + (groups + 1) / 2 : b == 8 ? groups : (groups + 1) / 2;
     total += ((int64_t)1 << b) * 16;
   }
+  if (v.sp_nnz > 0) total += 4 * ((int64_t)v.n + 1) + 6 * (int64_t)v.sp_nnz;
   return total;
 }
 
@@ -151,16 +161,17 @@ int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, f
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (batch > 1 && x_dtype == VQ_BF16) {
     hipError_t e = hipSuccess;
-    if (launch_gemv_tokens(v, x, batch, y, s, &e)) return map_hip(e);
-    return map_hip(launch_gemm(v, reinterpret_cast<const uint16_t *>(x), batch, y, s));
+    if (!launch_gemv_tokens(v, x, batch, y, s, &e)) e = launch_gemm(v, reinterpret_cast<const uint16_t *>(x), batch, y, s);
+    if (e != hipSuccess) return VQ_ERR_HIP;
+  } else {
+    const size_t esz = x_dtype == VQ_F32 ? 4 : 2;
+    for (int b = 0; b < batch; ++b) {
+      const void *xb = reinterpret_cast<const char *>(x) + (size_t)b * v.k * esz;
+      st = map_hip(launch_gemv_token(v, xb, x_dtype, y + (size_t)b * v.n, s));
+      if (st != VQ_OK) return st;
+    }
   }
-  const size_t esz = x_dtype == VQ_F32 ? 4 : 2;
-  for (int b = 0; b < batch; ++b) {
-    const void *xb = reinterpret_cast<const char *>(x) + (size_t)b * v.k * esz;
-    st = map_hip(launch_gemv_token(v, xb, x_dtype, y + (size_t)b * v.n, s));
-    if (st != VQ_OK) return st;
-  }
-  return VQ_OK;
+  return map_hip(launch_sparse_add(v, x, x_dtype, batch, y, s));
 }
 
 int vq_gemm(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float *y, void *stream) {
@@ -171,7 +182,10 @@ int vq_gemm(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float *y, voi
   if (m < 1) return VQ_ERR_SHAPE;
   if ((int64_t)m * v.k >= ((int64_t)1 << 31) || (int64_t)m * v.n >= ((int64_t)1 << 31)) return VQ_ERR_SHAPE;
   if (!aligned16(x_bf16) || !aligned16(y)) return VQ_ERR_ALIGN;
-  return map_hip(launch_gemm(v, x_bf16, m, y, reinterpret_cast<hipStream_t>(stream)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = map_hip(launch_gemm(v, x_bf16, m, y, s));
+  if (st != VQ_OK) return st;
+  return map_hip(launch_sparse_add(v, x_bf16, VQ_BF16, m, y, s));
 }
 
 int rht_apply(const void *x, int32_t x_dtype, int32_t batch, int32_t n, const int8_t *signs,

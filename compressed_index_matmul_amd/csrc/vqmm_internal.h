@@ -28,6 +28,10 @@ struct WView {
   const uint16_t *i16[VQ_MAX_STAGES];
   const uint16_t *cb[VQ_MAX_STAGES];
   const uint16_t *sc;
+  int sp_nnz;              // sparse correction entries (0: none)
+  const int32_t *sp_rowptr;
+  const int32_t *sp_col;
+  const uint16_t *sp_val;
 };
 
 // The plain formats the specialised kernels take: every stage of one width
@@ -46,6 +50,10 @@ hipError_t launch_gemv_token(const WView &w, const void *x, int xt, float *y, hi
 // allows it (false: not taken, nothing launched; *err set when taken).
 bool launch_gemv_tokens(const WView &w, const void *x, int batch, float *y, hipStream_t s, hipError_t *err);
 hipError_t launch_gemm(const WView &w, const uint16_t *x, int m, float *y, hipStream_t s);
+// y[b][r] += sum_j val_j x[b][col_j] over the sparse correction's row r, for
+// m tokens of x (VQ_F32 / VQ_BF16); after the main product on the same
+// stream.  No-op without a correction.
+hipError_t launch_sparse_add(const WView &w, const void *x, int xt, int m, float *y, hipStream_t s);
 
 struct GemvArgs;
 // Ladders and stage scales on the LDS decode kernel (k_gemv_ladder.hip):

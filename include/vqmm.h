@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define VQMM_VERSION 2
+#define VQMM_VERSION 3
 #define VQ_MAX_STAGES 4
 
 /* vq_weight.flags: stage_scale[] holds one residual scale per stage. */
@@ -88,9 +88,20 @@ typedef enum vq_dtype { VQ_F32 = 0, VQ_BF16 = 1 } vq_dtype;
  *               scale of the GLQ page's two-stage call ("Inference kernels"):
  *                 w[r, 8g + j] = s[r, blk] * sum_t stage_scale[t] * cb_t[..][j].
  *               Without the flag every stage scale is 1.
+ * sp_*        : optional sparse correction added to the decoded weight (orka
+ *               README, "How it works": the decode plus a sparse correction;
+ *               its correct command adds one), CSR over output rows:
+ *                 w[r, sp_col[j]] += fp16 sp_val[j],  sp_rowptr[r] <= j < sp_rowptr[r+1],
+ *               added after the block scale, unscaled, entries of a row in
+ *               storage order (repeated columns sum).  Device data the caller
+ *               keeps consistent: sp_rowptr[0] = 0, non-decreasing,
+ *               sp_rowptr[n_out] = sp_nnz; columns ascending within a row and
+ *               < k_in.  Kernels clamp row ranges to [0, sp_nnz] and skip
+ *               columns >= k_in, so inconsistent data gives wrong values,
+ *               never an access outside these arrays.
  * Unused pointer slots and unused stage_bits / stage_scale entries are
  * ignored.  A zero-initialised descriptor with the first block filled in
- * describes a uniform ladder without stage scales.
+ * describes a uniform ladder without stage scales or correction.
  */
 typedef struct vq_weight {
   int32_t n_out;       /* N >= 1 */
@@ -106,6 +117,11 @@ typedef struct vq_weight {
   const uint16_t *scales;
   int32_t stage_bits[VQ_MAX_STAGES]; /* 0 (= idx_bits), 4, 8, 12 or 16 */
   float stage_scale[VQ_MAX_STAGES];  /* used with VQ_STAGE_SCALES */
+  int32_t sp_nnz;                    /* entries of the sparse correction, 0 = none */
+  int32_t sp_reserved;               /* set to 0 */
+  const int32_t *sp_rowptr;          /* [n_out + 1] (when sp_nnz > 0) */
+  const int32_t *sp_col;             /* [sp_nnz] */
+  const uint16_t *sp_val;            /* fp16 bits [sp_nnz] */
 } vq_weight;
 
 /* Library version (VQMM_VERSION).  Host only. */
@@ -120,8 +136,9 @@ int vq_validate(const vq_weight *w);
 
 /* Stored bytes of the weight: index planes + fp16 scales + fp16 codebooks,
  * each counted once (per group and stage: 16-bit 2 bytes, 12-bit 1.5, 8-bit
- * 1, 4-bit 0.5, nibble planes rounded up).  Negative vq_status on an
- * invalid descriptor.  Host only. */
+ * 1, 4-bit 0.5, nibble planes rounded up), plus a sparse correction's
+ * 4 (n_out + 1) + 6 sp_nnz bytes.  Negative vq_status on an invalid
+ * descriptor.  Host only. */
 int64_t vq_compressed_bytes(const vq_weight *w);
 
 /*
@@ -135,7 +152,9 @@ int64_t vq_compressed_bytes(const vq_weight *w);
  *             VQ_STAGE_SCALES the value is not exact in general and is
  *             defined by a fixed float64 order: each stage_scale[t] * entry
  *             (exact), summed from stage 0 up with float64 rounding, times
- *             the block scale in float64, then rounded once to fp16.
+ *             the block scale in float64, then rounded once to fp16.  A
+ *             sparse correction is added to that float64 value, entry by
+ *             entry in storage order, before the one rounding.
  * At least one output must be non-NULL.  Bit-exact.
  */
 int vq_unpack_dequant(const vq_weight *w, uint16_t *idx_out, uint16_t *w_out, void *stream);
@@ -154,7 +173,9 @@ int vq_unpack_dequant(const vq_weight *w, uint16_t *idx_out, uint16_t *w_out, vo
  * 2..4 bf16 tokens whose rows are short enough (k_in <= 6144, and the
  * codebooks plus every token's x fit on chip) use the same exact fp16
  * products, one launch for all tokens.  Other 2..16 bf16 tokens run on bf16
- * matrix cores as vq_gemm does, with the same error behaviour.
+ * matrix cores as vq_gemm does, with the same error behaviour.  A sparse
+ * correction adds x S^T (fp16 values times x, fp32 sums) in a second launch
+ * on the same stream.
  */
 int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, float *y,
             void *stream);
@@ -170,7 +191,8 @@ int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, f
  * k_in 2^-24) sum_k |w x| + 1e-6.  For dense activations the rounding errors
  * average out and outputs stay well inside 2e-3 * sum_k |w x| + 1e-6 (about
  * 0.07 of it at k_in = 4096 for N(0,1) inputs); a one-hot or very short x
- * can exceed that tighter bound.
+ * can exceed that tighter bound.  A sparse correction adds x S^T exactly as
+ * vq_gemv does (fp32, not rounded to bf16).
  */
 int vq_gemm(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float *y, void *stream);
 

@@ -376,7 +376,7 @@ def _stage_widths(n_stages: int, bits) -> list:
 
 
 def compressed_bytes(n_out: int, k_in: int, n_stages: int, bits: Union[int, Sequence[int]],
-                     scale_block: int, include_codebooks: bool = True) -> int:
+                     scale_block: int, include_codebooks: bool = True, sparse_nnz: int = 0) -> int:
     """Bytes of the stored weight: index planes, fp16 scales and (optionally)
     the fp16 codebooks, each counted once.
 
@@ -385,6 +385,8 @@ def compressed_bytes(n_out: int, k_in: int, n_stages: int, bits: Union[int, Sequ
     orka's ``rvq-12-4``: 12 then 4).  Per stage: 16-bit = two bytes per
     group, 12-bit = one byte per group plus one byte per two groups (ceil),
     8-bit = one byte per group, 4-bit = one byte per two groups (ceil).
+    A sparse correction of ``sparse_nnz`` entries adds its CSR arrays: int32
+    row pointers (n_out + 1), int32 columns and fp16 values.
     """
     groups = n_out * (k_in // GROUP)
     per_width = {4: (groups + 1) // 2, 8: groups, 12: groups + (groups + 1) // 2, 16: 2 * groups}
@@ -392,6 +394,8 @@ def compressed_bytes(n_out: int, k_in: int, n_stages: int, bits: Union[int, Sequ
     total = sum(per_width[b] for b in widths) + 2 * n_out * n_scale_blocks(k_in, scale_block)
     if include_codebooks:
         total += sum((1 << b) * GROUP * 2 for b in widths)
+    if sparse_nnz:
+        total += 4 * (n_out + 1) + (4 + 2) * sparse_nnz
     return total
 
 

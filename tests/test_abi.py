@@ -252,3 +252,45 @@ def test_ladder_workload_bytes(L, wl):
         bs = k if cfg["scale_block"] is None else cfg["scale_block"]
         d = fake_desc(n, k, cfg["stages"], cfg["bits"][0], bs, widths=list(cfg["bits"]))
         assert L.vq_compressed_bytes(ctypes.byref(d)) == oracle.compressed_bytes(n, k, cfg["stages"], list(cfg["bits"]), bs)
+
+
+def sparse_desc(nnz=5, **kw):
+    d = fake_desc(**kw)
+    d.sp_nnz = nnz
+    d.sp_rowptr, d.sp_col, d.sp_val = FAKE, FAKE, FAKE
+    return d
+
+
+def test_sparse_correction_fields(L):
+    d = sparse_desc()
+    assert L.vq_validate(ctypes.byref(d)) == VQ_OK
+    n, k = d.n_out, d.k_in
+    assert L.vq_compressed_bytes(ctypes.byref(d)) == oracle.compressed_bytes(n, k, 1, 12, 32, sparse_nnz=5)
+    # nnz == 0: the pointers are ignored
+    d = fake_desc()
+    d.sp_rowptr = FAKE + 3
+    assert L.vq_validate(ctypes.byref(d)) == VQ_OK
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda d: setattr(d, "sp_nnz", -1), VQ_ERR_SHAPE),
+    (lambda d: setattr(d, "sp_reserved", 1), VQ_ERR_SHAPE),
+    (lambda d: setattr(d, "sp_rowptr", None), VQ_ERR_NULL),
+    (lambda d: setattr(d, "sp_col", None), VQ_ERR_NULL),
+    (lambda d: setattr(d, "sp_val", None), VQ_ERR_NULL),
+    (lambda d: setattr(d, "sp_col", FAKE + 4), VQ_ERR_ALIGN),
+    (lambda d: setattr(d, "sp_val", FAKE + 2), VQ_ERR_ALIGN),
+])
+def test_invalid_sparse(L, mutate, code):
+    d = sparse_desc()
+    mutate(d)
+    assert L.vq_validate(ctypes.byref(d)) == code
+    assert L.vq_gemv(ctypes.byref(d), FAKE, 1, 1, FAKE, None) == code
+    assert L.vq_gemm(ctypes.byref(d), FAKE, 64, FAKE, None) == code
+    assert L.vq_unpack_dequant(ctypes.byref(d), FAKE, FAKE, None) == code
+
+
+def test_sparse_bytes_by_hand():
+    # 3 rows, 2 entries: 4 int32 row pointers + 2 int32 columns + 2 fp16 values
+    base = oracle.compressed_bytes(3, 16, 1, 8, 16)
+    assert oracle.compressed_bytes(3, 16, 1, 8, 16, sparse_nnz=2) == base + 16 + 8 + 4

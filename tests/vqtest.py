@@ -26,7 +26,21 @@ def device_weight(sw: vqsynth.SynthWeight, device="cuda"):
     return VQWeight(sw.n_out, sw.k_in, sw.n_stages, sw.idx_bits, sw.scale_block,
                     codebooks=sw.codebooks, scales=sw.scales, lo=sw.lo, hi=sw.hi,
                     idx16=sw.idx16, device=device, stage_bits=sw.stage_bits,
-                    stage_scales=sw.stage_scales)
+                    stage_scales=sw.stage_scales, sparse=sw.sparse)
+
+
+def sparse_rows(sw: vqsynth.SynthWeight, rows):
+    """The sparse correction restricted to `rows` (None: all), as CSR."""
+    if sw.sparse is None or rows is None:
+        return sw.sparse
+    rp, cl, vl = sw.sparse
+    parts_c, parts_v, ptr = [], [], [0]
+    for r in rows:
+        parts_c.append(cl[rp[r]:rp[r + 1]])
+        parts_v.append(vl[rp[r]:rp[r + 1]])
+        ptr.append(ptr[-1] + rp[r + 1] - rp[r])
+    return (np.array(ptr), np.concatenate(parts_c) if parts_c else np.zeros(0, np.int64),
+            np.concatenate(parts_v) if parts_v else np.zeros(0, np.float16))
 
 
 def oracle_indices(sw: vqsynth.SynthWeight):
@@ -40,11 +54,11 @@ def oracle_w64(sw: vqsynth.SynthWeight, rows=None, idx=None):
     g = sw.k_in // 8
     if rows is None:
         return oracle.dequant_exact(sw.n_out, sw.k_in, idx, sw.codebooks, sw.scales, sw.scale_block,
-                                    sw.stage_scales)
+                                    sw.stage_scales, sw.sparse)
     rows = np.asarray(rows)
     sub = [i.reshape(sw.n_out, g)[rows].reshape(-1) for i in idx]
     return oracle.dequant_exact(len(rows), sw.k_in, sub, sw.codebooks, sw.scales[rows], sw.scale_block,
-                                sw.stage_scales)
+                                sw.stage_scales, sparse_rows(sw, rows))
 
 
 def oracle_w16(sw: vqsynth.SynthWeight, rows=None, idx=None):
@@ -52,11 +66,11 @@ def oracle_w16(sw: vqsynth.SynthWeight, rows=None, idx=None):
     g = sw.k_in // 8
     if rows is None:
         return oracle.dequant_fp16(sw.n_out, sw.k_in, idx, sw.codebooks, sw.scales, sw.scale_block,
-                                   sw.stage_scales)
+                                   sw.stage_scales, sw.sparse)
     rows = np.asarray(rows)
     sub = [i.reshape(sw.n_out, g)[rows].reshape(-1) for i in idx]
     return oracle.dequant_fp16(len(rows), sw.k_in, sub, sw.codebooks, sw.scales[rows], sw.scale_block,
-                               sw.stage_scales)
+                               sw.stage_scales, sparse_rows(sw, rows))
 
 
 def sample_rows(n: int, count: int, seed: int):

@@ -34,6 +34,8 @@ scales, drawn after everything else so the formats above are unchanged):
                      stage (4096 entries) plus a 4-bit stage (16 entries,
                      std 0.3x), 2 bits per weight of indices.
 * ``llama8b_rvq124`` the Llama-3-8B linears in the same 12+4 format.
+* ``llama8b_sparse`` the llama8b format plus a sparse correction of 0.5 %
+                     of each row's weights (values N(0, 0.05), fp16).
 * ``mlp70b_e8p3``    the 70B-MLP linears as GLQ's 3 bpw ladder: a 16-bit
                      primary and an 8-bit residual stage whose codebook has
                      the primary's spread, brought down by a residual scale
@@ -66,6 +68,7 @@ class SynthWeight:
     scales: Optional[np.ndarray] = None                          # float16 [N, nblk]
     stage_bits: Optional[List[int]] = None                       # per-stage widths (None: uniform)
     stage_scales: Optional[np.ndarray] = None                    # float32 [S] (None: all 1)
+    sparse: Optional[Tuple[np.ndarray, np.ndarray, np.ndarray]] = None  # CSR (rowptr, col, fp16 val)
 
     @property
     def n_groups(self) -> int:
@@ -100,6 +103,9 @@ WORKLOADS: Dict[str, dict] = {
     "llama8b_rvq124": dict(shapes=[("qo", 4096, 4096), ("gate_up", 14336, 4096), ("down", 4096, 14336)],
                            stages=2, bits=(12, 4), cb_sd=(0.02, 0.006), scale_block=128, x_dtype="bf16",
                            batches=(1, 16), rht=None, seed=6),
+    "llama8b_sparse": dict(shapes=[("qo", 4096, 4096), ("gate_up", 14336, 4096), ("down", 4096, 14336)],
+                           stages=2, bits=12, cb_sd=(0.02, 0.006), scale_block=128, x_dtype="bf16",
+                           batches=(1, 16), rht=None, seed=8, sparse=0.005),
     "mlp70b_e8p3": dict(shapes=[("gate_up", 28672, 8192), ("down", 8192, 28672)], stages=2, bits=(16, 8),
                         cb_sd=(0.02, 0.02), scale_block=None, x_dtype="bf16", batches=(1,), rht=8192, seed=7,
                         stage_scales=(0.2, 0.4)),
@@ -124,12 +130,15 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 def make_weight(name: str, n_out: int, k_in: int, n_stages: int, idx_bits,
                 cb_sd: Tuple[float, ...], scale_block: Optional[int],
                 seed_seq: np.random.SeedSequence,
-                stage_scale_range: Optional[Tuple[float, float]] = None) -> SynthWeight:
+                stage_scale_range: Optional[Tuple[float, float]] = None,
+                sparse_density: float = 0.0) -> SynthWeight:
     """Draw one compressed weight.  ``idx_bits`` is one width for every stage
     or a list of per-stage widths (4, 8, 12, 16).  Draw order per stage:
     codebook, indices; then the scales; then, if ``stage_scale_range`` is
     given, the residual scales of stages 1.. (uniform on the range, rounded
-    to float32; stage 0's is 1)."""
+    to float32; stage 0's is 1); then, if ``sparse_density`` > 0, a sparse
+    correction: per row round(density * K) distinct columns (ascending),
+    values N(0, 0.05) rounded to fp16."""
     if k_in % 8:
         raise ValueError("k_in must be a multiple of 8")
     widths = [int(idx_bits)] * n_stages if np.isscalar(idx_bits) else [int(b) for b in idx_bits]
@@ -171,6 +180,13 @@ def make_weight(name: str, n_out: int, k_in: int, n_stages: int, idx_bits,
         rs = np.ones(n_stages, np.float32)
         rs[1:] = rng.uniform(lo_r, hi_r, n_stages - 1).astype(np.float32)
         w.stage_scales = rs
+    if sparse_density > 0:
+        per = max(1, int(round(sparse_density * k_in)))
+        cols = np.sort(np.argsort(rng.random((n_out, k_in)), axis=1)[:, :per], axis=1) if n_out * k_in <= (1 << 24) \
+            else np.stack([np.sort(rng.choice(k_in, per, replace=False)) for _ in range(n_out)])
+        rowptr = np.arange(n_out + 1, dtype=np.int64) * per
+        val = (rng.standard_normal(n_out * per) * 0.05).astype(np.float16)
+        w.sparse = (rowptr, cols.reshape(-1).astype(np.int64), val)
     return w
 
 
@@ -202,12 +218,13 @@ def workload_weights(workload: str, only: Optional[List[str]] = None, base_seed:
         if only is not None and nm not in only:
             continue
         out.append(make_weight(nm, n, k, cfg["stages"], cfg["bits"], cfg["cb_sd"], cfg["scale_block"], ss,
-                               cfg.get("stage_scales")))
+                               cfg.get("stage_scales"), cfg.get("sparse", 0.0)))
     return out, kids[-1]
 
 
-def random_weight(n_out, k_in, n_stages, idx_bits, scale_block, seed, cb_sd=None, stage_scale_range=None):
+def random_weight(n_out, k_in, n_stages, idx_bits, scale_block, seed, cb_sd=None, stage_scale_range=None,
+                  sparse_density=0.0):
     """A weight of any shape/format for ragged and edge-case tests."""
     sd = cb_sd or tuple(0.02 * (0.3 ** t) for t in range(n_stages))
     return make_weight(f"r{n_out}x{k_in}", n_out, k_in, n_stages, idx_bits, sd, scale_block,
-                       np.random.SeedSequence(seed), stage_scale_range)
+                       np.random.SeedSequence(seed), stage_scale_range, sparse_density)
