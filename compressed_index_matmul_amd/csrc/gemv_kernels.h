@@ -20,6 +20,10 @@ struct GemvArgs {
   int C;          // 4-group chunks per row (G / 4) -- fast path
   int sb[VQ_MAX_STAGES];    // index width of each stage
   float rs[VQ_MAX_STAGES];  // stage scales (1 when the weight has none)
+  int sp_nnz;               // sparse correction (CSR over rows), 0 = none
+  const int32_t *sp_rowptr;
+  const int32_t *sp_col;
+  const uint16_t *sp_val;
 };
 
 // ---------------------------------------------------------------------------
@@ -33,8 +37,9 @@ __host__ __device__ constexpr size_t gemv_lds_bytes(int cb_rows, int CPL, bool X
 constexpr size_t kLdsBytes = 163840;  // 160 KiB per workgroup on gfx950
 
 // LD is the stage ladder (index widths, see Ladder); RS: stage t's partial
-// dot product is multiplied by its stage scale a.rs[t].
-template <class LD, bool RS, int CPL, int WAVES, bool XF16, int D, bool XREG, bool PIPE, int T = 1>
+// dot product is multiplied by its stage scale a.rs[t]; SP: the weight has a
+// sparse correction, added to each row's sum.
+template <class LD, bool RS, int CPL, int WAVES, bool XF16, int D, bool XREG, bool PIPE, int T = 1, bool SP = false>
 __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
   constexpr int S = LD::S;
   constexpr int NT = WAVES * 64;
@@ -88,12 +93,45 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
     bhi[t] = make_buf(LD::hi(t) ? a.hi[t] : a.lo[t], (plane + 1) / 2);
   }
   const buf_t bsc = make_buf(a.sc, 2u * (uint32_t)a.n * (uint32_t)a.nblk);
+  // Sparse correction (orka README, "How it works": the decode plus a sparse
+  // correction): lane i holds the CSR range of the wave's row i (rows < 64),
+  // loaded before everything else; a row's first kSpRing entries travel in
+  // the row ring with its index planes, kSpPer per lane.  Descriptors of zero
+  // size without a correction.
+  constexpr int kSpPer = SP ? 1 : 0;
+  constexpr int kSpRing = 64 * kSpPer;
+  const bool sp = SP && a.sp_nnz > 0;  // wave-uniform
+  const buf_t bsp_ptr = make_buf(a.sp_rowptr, sp ? 4u * ((uint32_t)a.n + 1u) : 0u);
+  const buf_t bsp_col = make_buf(a.sp_col, sp ? 4u * (uint32_t)a.sp_nnz : 0u);
+  const buf_t bsp_val = make_buf(a.sp_val, sp ? 2u * (uint32_t)a.sp_nnz : 0u);
+  uint32_t sp_lo = 0, sp_hi = 0;
+  if (sp) {
+    const uint32_t ri = (uint32_t)min(row0 + min(lane, max(nrows - 1, 0)) * stride, last);
+    sp_lo = buf_u32(bsp_ptr, 4u * ri, 0);
+    sp_hi = buf_u32(bsp_ptr, 4u * ri + 4u, 0);
+  }
+  sched_fence();
+  // CSR range of the wave's row r (wave-uniform), clamped to the arrays
+  auto sp_range = [&](int r, int &lo, int &hi) {
+    if (r < 64) {
+      lo = __builtin_amdgcn_readlane((int)sp_lo, r);
+      hi = __builtin_amdgcn_readlane((int)sp_hi, r);
+    } else {
+      const int rr = min(row0 + r * stride, last);
+      lo = a.sp_rowptr[rr];
+      hi = a.sp_rowptr[rr + 1];
+    }
+    lo = min(max(lo, 0), a.sp_nnz);
+    hi = min(max(hi, lo), a.sp_nnz);
+  };
 
-  // Index planes and scales of one row (this lane's chunks).
+  // Index planes and scales of one row (this lane's chunks), and this lane's
+  // entry of the row's sparse correction.
   struct RowIdx {
     uint32_t L[CPL][S];
     uint32_t H[CPL][S];
     uint32_t SC[CPL];
+    uint32_t SPC[kSpPer], SPV[kSpPer];
   };
   auto load_row = [&](int r, RowIdx &R) {
     // past the wave's last row: that row again (an L2 hit, never stored)
@@ -107,6 +145,19 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
         if (LD::hi(t)) R.H[j][t] = buf_u16(bhi[t], vlo[j] >> 1, rb >> 1);
       }
       R.SC[j] = buf_u16(bsc, vsc[j], 2u * rr * (uint32_t)a.nblk);
+    }
+    if (sp) {
+      sched_fence();  // the index loads go out before the wait on the CSR range
+      int lo, hi;
+      sp_range(max(min(r, nrows - 1), 0), lo, hi);
+      // every load is issued by every lane (a clamped duplicate past the
+      // row's entries): the prologue's wait counts them
+#pragma unroll
+      for (int e = 0; e < kSpPer; ++e) {
+        const uint32_t j = (uint32_t)min(lo + 64 * e + lane, max(hi - 1, 0));
+        R.SPC[e] = buf_u32(bsp_col, 4u * j, 0);
+        R.SPV[e] = buf_u16(bsp_val, 2u * j, 0);
+      }
     }
   };
 
@@ -154,7 +205,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
   for (int k = 0; k < D; ++k) load_row(k, R[k]);
   sched_fence();
   constexpr int kIdxLoads = D * CPL * (LD::kPlanes + 1);
-  wait_vmem<(kIdxLoads < 63 ? kIdxLoads : 63)>();
+  constexpr int kSpLoads = kIdxLoads + 2 * kSpPer * D;  // with a correction: + columns and values
+  if (sp) wait_vmem<(kSpLoads < 63 ? kSpLoads : 63)>();
+  else wait_vmem<(kIdxLoads < 63 ? kIdxLoads : 63)>();
 
   // x -> LDS.  bf16 x becomes fp16 after a per-chunk power-of-two rescale
   // that puts the chunk's largest |x| in [2^14, 2^15): exact for every value
@@ -323,6 +376,41 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
         add(j, it);
       }
     }
+    if (sp) {
+      // x of column c, token tt, from the staged copy
+      auto x_at = [&](int tt, int c) -> float {
+        const int ch = c >> 5, p = c & 31;
+        if (XF16) {
+          const _Float16 *hx = reinterpret_cast<const _Float16 *>(&s_x[tt][(p >> 3) * CMAX + ch]);
+          return (float)hx[p & 7] * s_f[tt][ch];
+        }
+        const float *fx = reinterpret_cast<const float *>(&s_x[0][(p >> 2) * CMAX + ch]);
+        return fx[p & 3];
+      };
+      int lo, hi;
+      sp_range(r, lo, hi);
+      // the first kSpRing entries come from the ring, any further ones are
+      // loaded here
+#pragma unroll
+      for (int e = 0; e < kSpPer; ++e) {
+        const bool has = lo + 64 * e + lane < hi;
+        const int c = (int)Rr.SPC[e];
+        if (has && c >= 0 && c < a.k) {
+          const float v = h2f(Rr.SPV[e]);
+#pragma unroll
+          for (int tt = 0; tt < T; ++tt) acc[tt] = fmaf(v, x_at(tt, c), acc[tt]);
+        }
+      }
+      for (int j0 = lo + kSpRing; j0 < hi; j0 += 64) {
+        const bool has = j0 + lane < hi;
+        const int c = has ? a.sp_col[j0 + lane] : -1;
+        if (c >= 0 && c < a.k) {
+          const float v = h2f(a.sp_val[j0 + lane]);
+#pragma unroll
+          for (int tt = 0; tt < T; ++tt) acc[tt] = fmaf(v, x_at(tt, c), acc[tt]);
+        }
+      }
+    }
 #pragma unroll
     for (int tt = 0; tt < T; ++tt) {
       const float tot = wave_sum(acc[tt]);
@@ -462,14 +550,18 @@ static GemvArgs make_args(const WView &w) {
     a.sb[t] = t < w.S ? w.sb[t] : 0;
     a.rs[t] = w.rs[t];
   }
+  a.sp_nnz = w.sp_nnz;
+  a.sp_rowptr = w.sp_rowptr;
+  a.sp_col = w.sp_col;
+  a.sp_val = w.sp_val;
   return a;
 }
 
-template <class LD, bool RS, int CPL, int W, int D, bool XF16, bool XREG, bool PIPE>
+template <class LD, bool RS, int CPL, int W, int D, bool XF16, bool XREG, bool PIPE, bool SP>
 static void launch_fast_w(const GemvArgs &a, int cus, hipStream_t s) {
   const int g = (a.n + W - 1) / W;
-  hipLaunchKernelGGL((k_gemv_lds<LD, RS, CPL, W, XF16, D, XREG, PIPE>), dim3(g < cus ? g : cus), dim3(W * 64), 0,
-                     s, a);
+  hipLaunchKernelGGL((k_gemv_lds<LD, RS, CPL, W, XF16, D, XREG, PIPE, 1, SP>), dim3(g < cus ? g : cus), dim3(W * 64),
+                     0, s, a);
 }
 
 // Persistent grid of one workgroup per CU (the codebooks and x take most of
@@ -478,28 +570,28 @@ static void launch_fast_w(const GemvArgs &a, int cus, hipStream_t s) {
 // get 128 VGPRs each, 8 get 256.  Rows of 1-2 chunks per lane: 16 waves, x in
 // registers; 3-4 chunks: 8 waves, two rows in flight, pipelined gathers;
 // longer rows: 8 waves, x read from LDS per chunk.
-template <class LD, bool RS, int CPL, bool XF16>
+template <class LD, bool RS, int CPL, bool XF16, bool SP>
 static void launch_fast_c(const GemvArgs &a, int cus, hipStream_t s) {
   if constexpr (gemv_lds_bytes(LD::kRows, CPL, XF16) <= kLdsBytes) {
-    if constexpr (CPL <= 2) launch_fast_w<LD, RS, CPL, 16, 1, XF16, true, false>(a, cus, s);
-    else if constexpr (CPL <= 4 || !XF16) launch_fast_w<LD, RS, CPL, 8, 2, XF16, true, true>(a, cus, s);
-    else launch_fast_w<LD, RS, CPL, 8, 1, XF16, false, true>(a, cus, s);
+    if constexpr (CPL <= 2) launch_fast_w<LD, RS, CPL, 16, 1, XF16, true, false, SP>(a, cus, s);
+    else if constexpr (CPL <= 4 || !XF16) launch_fast_w<LD, RS, CPL, 8, 2, XF16, true, true, SP>(a, cus, s);
+    else launch_fast_w<LD, RS, CPL, 8, 1, XF16, false, true, SP>(a, cus, s);
   }
 }
 
 // One token through the LDS kernel of ladder LD (the caller has checked
 // gemv_fast_shape).
-template <class LD, bool RS, bool XF16>
+template <class LD, bool RS, bool XF16, bool SP = false>
 static void launch_fast_s(const GemvArgs &a, int cus, hipStream_t s) {
   switch ((a.C + 63) / 64) {
-    case 1: launch_fast_c<LD, RS, 1, XF16>(a, cus, s); break;
-    case 2: launch_fast_c<LD, RS, 2, XF16>(a, cus, s); break;
-    case 3: launch_fast_c<LD, RS, 3, XF16>(a, cus, s); break;
-    case 4: launch_fast_c<LD, RS, 4, XF16>(a, cus, s); break;
-    case 5: if constexpr (XF16) launch_fast_c<LD, RS, 5, XF16>(a, cus, s); break;
-    case 6: if constexpr (XF16) launch_fast_c<LD, RS, 6, XF16>(a, cus, s); break;
-    case 7: if constexpr (XF16) launch_fast_c<LD, RS, 7, XF16>(a, cus, s); break;
-    default: if constexpr (XF16) launch_fast_c<LD, RS, 8, XF16>(a, cus, s); break;
+    case 1: launch_fast_c<LD, RS, 1, XF16, SP>(a, cus, s); break;
+    case 2: launch_fast_c<LD, RS, 2, XF16, SP>(a, cus, s); break;
+    case 3: launch_fast_c<LD, RS, 3, XF16, SP>(a, cus, s); break;
+    case 4: launch_fast_c<LD, RS, 4, XF16, SP>(a, cus, s); break;
+    case 5: if constexpr (XF16) launch_fast_c<LD, RS, 5, XF16, SP>(a, cus, s); break;
+    case 6: if constexpr (XF16) launch_fast_c<LD, RS, 6, XF16, SP>(a, cus, s); break;
+    case 7: if constexpr (XF16) launch_fast_c<LD, RS, 7, XF16, SP>(a, cus, s); break;
+    default: if constexpr (XF16) launch_fast_c<LD, RS, 8, XF16, SP>(a, cus, s); break;
   }
 }
 
@@ -508,38 +600,129 @@ static void launch_fast_s(const GemvArgs &a, int cus, hipStream_t s) {
 // gathers, the LDS-bound part, are shared.  Rows of up to 3 chunks per lane
 // (K <= 6144), at most 6 chunks x tokens, codebooks and all tokens' x in the
 // LDS; other shapes take the matrix-core path.
-template <class LD, bool RS, int CPL, int T>
+template <class LD, bool RS, int CPL, int T, bool SP>
 static bool launch_tokens_c(const GemvArgs &a, int cus, hipStream_t s) {
   // chunks x tokens <= 6 keeps x in registers without spills at 256 VGPRs
   if constexpr (CPL * T <= 6 && gemv_lds_bytes(LD::kRows, CPL, true, T) <= kLdsBytes) {
     const int g = (a.n + 7) / 8;
-    hipLaunchKernelGGL((k_gemv_lds<LD, RS, CPL, 8, true, 1, true, false, T>), dim3(g < cus ? g : cus), dim3(512), 0,
-                       s, a);
+    hipLaunchKernelGGL((k_gemv_lds<LD, RS, CPL, 8, true, 1, true, false, T, SP>), dim3(g < cus ? g : cus), dim3(512),
+                       0, s, a);
     return true;
   }
   return false;
 }
 
-template <class LD, bool RS, int T>
+template <class LD, bool RS, int T, bool SP>
 static bool launch_tokens_t(const GemvArgs &a, int cus, hipStream_t s) {
   switch ((a.C + 63) / 64) {
-    case 1: return launch_tokens_c<LD, RS, 1, T>(a, cus, s);
-    case 2: return launch_tokens_c<LD, RS, 2, T>(a, cus, s);
-    case 3: return launch_tokens_c<LD, RS, 3, T>(a, cus, s);
+    case 1: return launch_tokens_c<LD, RS, 1, T, SP>(a, cus, s);
+    case 2: return launch_tokens_c<LD, RS, 2, T, SP>(a, cus, s);
+    case 3: return launch_tokens_c<LD, RS, 3, T, SP>(a, cus, s);
     default: return false;
   }
 }
 
 // 2..4 bf16 tokens through the LDS kernel of ladder LD; false when the shape
 // does not fit it (nothing launched).
-template <class LD, bool RS>
+template <class LD, bool RS, bool SP = false>
 static bool launch_tokens_s(const GemvArgs &a, int batch, int cus, hipStream_t s) {
   switch (batch) {
-    case 2: return launch_tokens_t<LD, RS, 2>(a, cus, s);
-    case 3: return launch_tokens_t<LD, RS, 3>(a, cus, s);
-    case 4: return launch_tokens_t<LD, RS, 4>(a, cus, s);
+    case 2: return launch_tokens_t<LD, RS, 2, SP>(a, cus, s);
+    case 3: return launch_tokens_t<LD, RS, 3, SP>(a, cus, s);
+    case 4: return launch_tokens_t<LD, RS, 4, SP>(a, cus, s);
     default: return false;
   }
 }
+
+// ---------------------------------------------------------------------------
+// format dispatch (templates on SP: each translation unit instantiates its
+// share -- k_gemv.hip plain formats, k_gemv_ladder.hip ladders, both without
+// a correction; k_gemv_sparse.hip both with one)
+// ---------------------------------------------------------------------------
+// Plain formats with an LDS kernel: 1-2 stages of 12 bits, 1-4 of 8 bits.
+inline bool plain_lds_format(const WView &w) {
+  return plain_format(w) && (w.bits == 8 || (w.bits == 12 && w.S <= 2));
+}
+
+template <bool SP, bool XF16>
+static void launch_lds_plain(const WView &w, const GemvArgs &a, int cus, hipStream_t s) {
+  if (w.bits == 12) {
+    if (w.S == 1) launch_fast_s<Ladder<12>, false, XF16, SP>(a, cus, s);
+    else launch_fast_s<Ladder<12, 12>, false, XF16, SP>(a, cus, s);
+  } else {
+    switch (w.S) {
+      case 1: launch_fast_s<Ladder<8>, false, XF16, SP>(a, cus, s); break;
+      case 2: launch_fast_s<Ladder<8, 8>, false, XF16, SP>(a, cus, s); break;
+      case 3: launch_fast_s<Ladder<8, 8, 8>, false, XF16, SP>(a, cus, s); break;
+      default: launch_fast_s<Ladder<8, 8, 8, 8>, false, XF16, SP>(a, cus, s); break;
+    }
+  }
+}
+
+template <bool SP>
+static bool launch_tokens_plain(const WView &w, const GemvArgs &a, int batch, int cus, hipStream_t s) {
+  if (w.bits == 12) {
+    if (w.S == 1) return launch_tokens_s<Ladder<12>, false, SP>(a, batch, cus, s);
+    if (w.S == 2) return launch_tokens_s<Ladder<12, 12>, false, SP>(a, batch, cus, s);
+    return false;
+  }
+  switch (w.S) {
+    case 1: return launch_tokens_s<Ladder<8>, false, SP>(a, batch, cus, s);
+    case 2: return launch_tokens_s<Ladder<8, 8>, false, SP>(a, batch, cus, s);
+    default: return false;
+  }
+}
+
+// Ladders with an LDS kernel of their own: 12 + 4 and 8 + 4 bits (orka
+// README quick start, the rvq-12-4 mode), and 1-2 stages of 8 or 12 bits
+// with a residual scale per stage (GLQ page, "Inference kernels").
+constexpr int ladder_pack2(int b0, int b1) { return (b0 / 4) | ((b1 / 4) << 4); }
+inline int ladder_code2(const WView &w) { return w.S > 2 ? -1 : ladder_pack2(w.sb[0], w.S > 1 ? w.sb[1] : 0); }
+
+template <bool SP, bool XF16>
+static bool launch_lds_ladder(const WView &w, const GemvArgs &a, int cus, hipStream_t s) {
+  const int code = ladder_code2(w);
+  if (!w.scaled) {
+    switch (code) {
+      case ladder_pack2(12, 4): launch_fast_s<Ladder<12, 4>, false, XF16, SP>(a, cus, s); return true;
+      case ladder_pack2(8, 4): launch_fast_s<Ladder<8, 4>, false, XF16, SP>(a, cus, s); return true;
+      default: return false;
+    }
+  }
+  switch (code) {
+    case ladder_pack2(12, 0): launch_fast_s<Ladder<12>, true, XF16, SP>(a, cus, s); return true;
+    case ladder_pack2(8, 0): launch_fast_s<Ladder<8>, true, XF16, SP>(a, cus, s); return true;
+    case ladder_pack2(12, 12): launch_fast_s<Ladder<12, 12>, true, XF16, SP>(a, cus, s); return true;
+    case ladder_pack2(8, 8): launch_fast_s<Ladder<8, 8>, true, XF16, SP>(a, cus, s); return true;
+    case ladder_pack2(12, 4): launch_fast_s<Ladder<12, 4>, true, XF16, SP>(a, cus, s); return true;
+    case ladder_pack2(8, 4): launch_fast_s<Ladder<8, 4>, true, XF16, SP>(a, cus, s); return true;
+    default: return false;
+  }
+}
+
+template <bool SP>
+static bool launch_tokens_ladder(const WView &w, const GemvArgs &a, int batch, int cus, hipStream_t s) {
+  const int code = ladder_code2(w);
+  if (!w.scaled) {
+    switch (code) {
+      case ladder_pack2(12, 4): return launch_tokens_s<Ladder<12, 4>, false, SP>(a, batch, cus, s);
+      case ladder_pack2(8, 4): return launch_tokens_s<Ladder<8, 4>, false, SP>(a, batch, cus, s);
+      default: return false;
+    }
+  }
+  switch (code) {
+    case ladder_pack2(12, 12): return launch_tokens_s<Ladder<12, 12>, true, SP>(a, batch, cus, s);
+    case ladder_pack2(12, 4): return launch_tokens_s<Ladder<12, 4>, true, SP>(a, batch, cus, s);
+    default: return false;
+  }
+}
+
+// Defined in k_gemv_ladder.hip (ladders, no correction) and k_gemv_sparse.hip
+// (plain formats and ladders with a correction): false when the format has
+// no LDS kernel (nothing launched).  The shape checks have been made.
+bool launch_gemv_lds_ladder(const WView &w, const GemvArgs &a, bool xf16, int cus, hipStream_t s);
+bool launch_gemv_tokens_ladder(const WView &w, const GemvArgs &a, int batch, int cus, hipStream_t s);
+bool launch_gemv_lds_sparse(const WView &w, const GemvArgs &a, bool xf16, int cus, hipStream_t s);
+bool launch_gemv_tokens_sparse(const WView &w, const GemvArgs &a, int batch, int cus, hipStream_t s);
 
 }  // namespace vqmm

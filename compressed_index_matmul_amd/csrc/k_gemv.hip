@@ -62,24 +62,6 @@ static bool gemv_fast_shape(const WView &w, int xt) {
   return gemv_lds_bytes(rows, cpl, xt == VQ_BF16) <= kLdsBytes;
 }
 
-// Plain formats: 1-2 stages of 12 bits, 1-4 stages of 8 bits.
-template <bool XF16>
-static void launch_fast(const WView &w, const GemvArgs &a, int cus, hipStream_t s) {
-  if (w.bits == 12) {
-    if (w.S == 1) launch_fast_s<Ladder<12>, false, XF16>(a, cus, s);
-    else launch_fast_s<Ladder<12, 12>, false, XF16>(a, cus, s);
-  } else {
-    switch (w.S) {
-      case 1: launch_fast_s<Ladder<8>, false, XF16>(a, cus, s); break;
-      case 2: launch_fast_s<Ladder<8, 8>, false, XF16>(a, cus, s); break;
-      case 3: launch_fast_s<Ladder<8, 8, 8>, false, XF16>(a, cus, s); break;
-      default: launch_fast_s<Ladder<8, 8, 8, 8>, false, XF16>(a, cus, s); break;
-    }
-  }
-}
-
-static bool plain_fast(const WView &w) { return plain_format(w) && (w.bits == 8 || (w.bits == 12 && w.S <= 2)); }
-
 // The general kernel: BITS = the width of every stage of a plain format, 0
 // for ladders and stage scales.
 template <int BITS>
@@ -102,36 +84,33 @@ bool launch_gemv_tokens(const WView &w, const void *x, int batch, float *y, hipS
   a.y = y;
   const int cus = device_cu_count();
   bool done = false;
-  if (!plain_format(w)) {
-    done = launch_gemv_tokens_ladder(w, a, batch, cus, s);
-  } else if (w.bits == 12) {
-    done = w.S == 1   ? launch_tokens_s<Ladder<12>, false>(a, batch, cus, s)
-           : w.S == 2 ? launch_tokens_s<Ladder<12, 12>, false>(a, batch, cus, s)
-                      : false;
-  } else {
-    switch (w.S) {
-      case 1: done = launch_tokens_s<Ladder<8>, false>(a, batch, cus, s); break;
-      case 2: done = launch_tokens_s<Ladder<8, 8>, false>(a, batch, cus, s); break;
-      default: done = false; break;
-    }
-  }
+  if (w.sp_nnz > 0) done = launch_gemv_tokens_sparse(w, a, batch, cus, s);
+  else if (!plain_format(w)) done = launch_gemv_tokens_ladder(w, a, batch, cus, s);
+  else done = launch_tokens_plain<false>(w, a, batch, cus, s);
   if (done) *err = hipGetLastError();
   return done;
 }
 
-hipError_t launch_gemv_token(const WView &w, const void *x, int xt, float *y, hipStream_t s) {
+hipError_t launch_gemv_token(const WView &w, const void *x, int xt, float *y, hipStream_t s, bool *sp_done) {
   GemvArgs a = make_args(w);
   a.x = x;
   a.y = y;
   const int cus = device_cu_count();
+  const bool xf16 = xt == VQ_BF16;
+  // the LDS kernel adds a sparse correction itself
+  *sp_done = true;
   if (gemv_fast_shape(w, xt)) {
-    if (plain_fast(w)) {
-      if (xt == VQ_BF16) launch_fast<true>(w, a, cus, s);
-      else launch_fast<false>(w, a, cus, s);
+    if (w.sp_nnz > 0) {
+      if (launch_gemv_lds_sparse(w, a, xf16, cus, s)) return hipGetLastError();
+    } else if (plain_lds_format(w)) {
+      if (xf16) launch_lds_plain<false, true>(w, a, cus, s);
+      else launch_lds_plain<false, false>(w, a, cus, s);
+      return hipGetLastError();
+    } else if (!plain_format(w) && launch_gemv_lds_ladder(w, a, xf16, cus, s)) {
       return hipGetLastError();
     }
-    if (!plain_format(w) && launch_gemv_lds_ladder(w, a, xt == VQ_BF16, cus, s)) return hipGetLastError();
   }
+  *sp_done = false;
   if (!plain_format(w)) launch_gen_bits<0>(w, a, xt, cus, s);
   else if (w.bits == 8) launch_gen_bits<8>(w, a, xt, cus, s);
   else if (w.bits == 12) launch_gen_bits<12>(w, a, xt, cus, s);

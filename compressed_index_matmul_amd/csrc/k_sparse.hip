@@ -4,10 +4,12 @@
 // stream.  CSR over output rows; fp16 values, fp32 products and sums in
 // storage order (fixed, no atomics).
 //
-// Few tokens (m <= 8): one wave per row, lanes split the row's entries, one
-// wave sum per token.  More tokens: one wave per (row, 64 tokens), lane =
-// token, the row's entries in storage order (value and column are
-// wave-uniform loads).  Row ranges are clamped to [0, nnz] and columns past
+// Up to 8 tokens: one wave per row, lanes split the row's entries, one wave
+// sum per token.
+// More tokens: one wave per (row, 64 tokens), lane = token, the row's
+// entries in storage order (value and column are wave-uniform loads).  The
+// decode kernel fuses the correction itself where it runs; this launch
+// serves the other paths.  Row ranges are clamped to [0, nnz] and columns past
 // the row are skipped, so inconsistent CSR data stays inside its arrays.
 #include "vqmm_device.h"
 #include "vqmm_internal.h"

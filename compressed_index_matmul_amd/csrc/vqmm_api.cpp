@@ -159,18 +159,21 @@ int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, f
   if (batch < 1 || batch > 16) return VQ_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(y)) return VQ_ERR_ALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  bool sp_done = false;  // the sparse correction was added by the product kernel
   if (batch > 1 && x_dtype == VQ_BF16) {
     hipError_t e = hipSuccess;
-    if (!launch_gemv_tokens(v, x, batch, y, s, &e)) e = launch_gemm(v, reinterpret_cast<const uint16_t *>(x), batch, y, s);
+    if (launch_gemv_tokens(v, x, batch, y, s, &e)) sp_done = true;
+    else e = launch_gemm(v, reinterpret_cast<const uint16_t *>(x), batch, y, s);
     if (e != hipSuccess) return VQ_ERR_HIP;
   } else {
     const size_t esz = x_dtype == VQ_F32 ? 4 : 2;
     for (int b = 0; b < batch; ++b) {
       const void *xb = reinterpret_cast<const char *>(x) + (size_t)b * v.k * esz;
-      st = map_hip(launch_gemv_token(v, xb, x_dtype, y + (size_t)b * v.n, s));
+      st = map_hip(launch_gemv_token(v, xb, x_dtype, y + (size_t)b * v.n, s, &sp_done));
       if (st != VQ_OK) return st;
     }
   }
+  if (sp_done) return VQ_OK;
   return map_hip(launch_sparse_add(v, x, x_dtype, batch, y, s));
 }
 

@@ -45,9 +45,11 @@ hipError_t launch_unpack_dequant(const WView &w, uint16_t *idx_out, uint16_t *w_
 hipError_t launch_rht(const void *x, int xt, int batch, int n, const int8_t *signs, int max_block,
                       float *out, hipStream_t s);
 // One token of x (fp32 or bf16, VQ_F32 / VQ_BF16) against W: y[n].
-hipError_t launch_gemv_token(const WView &w, const void *x, int xt, float *y, hipStream_t s);
+// *sp_done: the launched kernel also added the sparse correction.
+hipError_t launch_gemv_token(const WView &w, const void *x, int xt, float *y, hipStream_t s, bool *sp_done);
 // 2..4 bf16 tokens in one launch of the LDS decode kernel when the shape
-// allows it (false: not taken, nothing launched; *err set when taken).
+// allows it (false: not taken, nothing launched; *err set when taken).  The
+// kernel also adds the sparse correction.
 bool launch_gemv_tokens(const WView &w, const void *x, int batch, float *y, hipStream_t s, hipError_t *err);
 hipError_t launch_gemm(const WView &w, const uint16_t *x, int m, float *y, hipStream_t s);
 // y[b][r] += sum_j val_j x[b][col_j] over the sparse correction's row r, for
@@ -55,11 +57,5 @@ hipError_t launch_gemm(const WView &w, const uint16_t *x, int m, float *y, hipSt
 // stream.  No-op without a correction.
 hipError_t launch_sparse_add(const WView &w, const void *x, int xt, int m, float *y, hipStream_t s);
 
-struct GemvArgs;
-// Ladders and stage scales on the LDS decode kernel (k_gemv_ladder.hip):
-// false when the ladder has no LDS kernel (nothing launched).  The shape
-// checks of the LDS kernel have been made by the caller.
-bool launch_gemv_lds_ladder(const WView &w, const GemvArgs &a, bool xf16, int cus, hipStream_t s);
-bool launch_gemv_tokens_ladder(const WView &w, const GemvArgs &a, int batch, int cus, hipStream_t s);
 
 }  // namespace vqmm
