@@ -724,5 +724,9 @@ bool launch_gemv_lds_ladder(const WView &w, const GemvArgs &a, bool xf16, int cu
 bool launch_gemv_tokens_ladder(const WView &w, const GemvArgs &a, int batch, int cus, hipStream_t s);
 bool launch_gemv_lds_sparse(const WView &w, const GemvArgs &a, bool xf16, int cus, hipStream_t s);
 bool launch_gemv_tokens_sparse(const WView &w, const GemvArgs &a, int batch, int cus, hipStream_t s);
+// One stage of 16-bit indices (k_gemv_l2.hip): L2 gathers with the next
+// row's indices loading and 16 gathers per lane in flight; false when the
+// shape is not taken.
+bool launch_gemv_l2(const WView &w, const GemvArgs &a, int xt, int cus, hipStream_t s);
 
 }  // namespace vqmm

@@ -111,6 +111,7 @@ hipError_t launch_gemv_token(const WView &w, const void *x, int xt, float *y, hi
     }
   }
   *sp_done = false;
+  if (launch_gemv_l2(w, a, xt, cus, s)) return hipGetLastError();
   if (!plain_format(w)) launch_gen_bits<0>(w, a, xt, cus, s);
   else if (w.bits == 8) launch_gen_bits<8>(w, a, xt, cus, s);
   else if (w.bits == 12) launch_gen_bits<12>(w, a, xt, cus, s);
