@@ -15,8 +15,12 @@
 //     products with x, which is staged once per workgroup in LDS as fp32;
 //   * per unit the 32 products are summed, scaled and accumulated in a fixed
 //     order; one fixed-order wave reduction per row.  No atomics.
-// Taken for one stage of 16-bit indices, K % 2048 == 0 (K / 2048 units per
-// lane) up to K = 32768 (x in LDS), scale blocks of whole 32-column units.
+// Taken for one stage of 16-bit indices, or a 16-bit primary plus one
+// residual stage of 8 bits (its 4 KiB codebook in LDS) or 16 bits (L2
+// gathers too), optionally with stage scales (GLQ page, "Bit widths": the
+// 3 and 4 bpw ladders; "Inference kernels": the inverse residual scale);
+// K % 2048 == 0 (K / 2048 units per lane) up to K = 32768 (x in LDS), scale
+// blocks of whole 32-column units.
 #include "gemv_kernels.h"
 
 namespace vqmm {
@@ -25,12 +29,17 @@ namespace {
 
 constexpr int kL2Waves = 8;
 constexpr int kL2MaxK = 32768;  // fp32 x in LDS: 128 KiB
-constexpr int kL2Batch = 4;     // units whose gathers are in flight together
+// units whose gathers are in flight together (16 per lane either way)
+template <int B1> constexpr int l2_batch() { return B1 == 16 ? 2 : 4; }
+// most units per lane that fit the register file without spills
+template <int B1> constexpr int l2_max_upl() { return B1 == 0 ? 16 : B1 == 8 ? 14 : 13; }
 
-template <int UPL>
+// B1: width of the residual stage (0: none, 8 or 16); RS: stage scales.
+template <int UPL, int B1, bool RS>
 __global__ __launch_bounds__(kL2Waves * 64) void k_gemv_l2(GemvArgs a, int xt) {
   constexpr int NT = kL2Waves * 64;
   __shared__ float s_x[kL2MaxK];
+  __shared__ uint4 s_cb1[B1 == 8 ? 256 : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -47,6 +56,7 @@ __global__ __launch_bounds__(kL2Waves * 64) void k_gemv_l2(GemvArgs a, int xt) {
     }
     *reinterpret_cast<float4 *>(&s_x[i]) = v;
   }
+  if (B1 == 8 && tid < 256) s_cb1[tid] = reinterpret_cast<const uint4 *>(a.cb[1])[tid];
   __syncthreads();  // the only barrier: waves without rows may leave after it
 
   const int per_wg = (a.n + gridDim.x - 1) / gridDim.x;
@@ -60,52 +70,63 @@ __global__ __launch_bounds__(kL2Waves * 64) void k_gemv_l2(GemvArgs a, int xt) {
   const buf_t bi = make_buf(a.i16[0], 2u * (uint32_t)a.n * G);
   const buf_t bsc = make_buf(a.sc, 2u * (uint32_t)a.n * (uint32_t)a.nblk);
   const buf_t bcb = make_buf(a.cb[0], 65536u * 16u);
-  uint32_t vu[UPL], vs[UPL];
-#pragma unroll
-  for (int j = 0; j < UPL; ++j) {
-    const uint32_t u = (uint32_t)(lane + 64 * j);  // unit of 4 groups = 32 columns
-    vu[j] = 8u * u;
-    vs[j] = 2u * ((32u * u) / (uint32_t)a.bs);
-  }
+  const buf_t bi1 = make_buf(B1 == 16 ? (const void *)a.i16[1] : (const void *)a.lo[1], (B1 == 16 ? 2u : 1u) * (uint32_t)a.n * G);
+  const buf_t bcb1 = make_buf(a.cb[1], 65536u * 16u);
+  const float r0 = RS ? a.rs[0] : 1.f, r1 = RS ? a.rs[1] : 1.f;
+  // Unit lane + 64 j (4 groups = 32 columns) sits at byte 8 lane + 512 j of a
+  // row of 16-bit indices; its scale at 2 ((32 lane + 2048 j) / bs), which
+  // splits into a lane part and a wave-uniform part because bs divides 2048
+  // or is at least K (then every unit has scale 0 of its row).
+  constexpr int kBatch = l2_batch<B1>();
+  const uint32_t bs = (uint32_t)a.bs;
+  const uint32_t vsc = 2u * ((32u * (uint32_t)lane) / bs);
+  const uint32_t sstep = 2u * (2048u / bs);
 
   struct RowI {
     uint2 I[UPL];
     uint32_t S[UPL];
+    uint2 I1[B1 ? UPL : 1];  // residual indices (8-bit: four bytes in .x)
   };
   auto load_row = [&](int r, RowI &R) {
     // past the wave's last row: that row again (an L2 hit, never stored)
     const uint32_t rr = (uint32_t)(row0 + min(r, nrows - 1) * kL2Waves);
 #pragma unroll
     for (int j = 0; j < UPL; ++j) {
-      R.I[j] = buf_u64(bi, vu[j], 2u * rr * G);
-      R.S[j] = buf_u16(bsc, vs[j], 2u * rr * (uint32_t)a.nblk);
+      R.I[j] = buf_u64(bi, 8u * lane, 2u * rr * G + 512u * j);
+      R.S[j] = buf_u16(bsc, vsc, 2u * rr * (uint32_t)a.nblk + sstep * j);
+      if constexpr (B1 == 16) R.I1[j] = buf_u64(bi1, 8u * lane, 2u * rr * G + 512u * j);
+      if constexpr (B1 == 8) R.I1[j] = make_uint2(buf_u32(bi1, 4u * lane, rr * G + 256u * j), 0u);
     }
   };
   auto compute_row = [&](int r, const RowI &R) {
     float acc = 0.f;
 #pragma unroll
-    for (int j0 = 0; j0 < UPL; j0 += kL2Batch) {
-      uint4 cv[kL2Batch][4];
+    for (int j0 = 0; j0 < UPL; j0 += kBatch) {
+      uint4 cv[kBatch][4];
+      uint4 cv1[B1 == 16 ? kBatch : 1][4];
 #pragma unroll
-      for (int jj = 0; jj < kL2Batch; ++jj) {
+      for (int jj = 0; jj < kBatch; ++jj) {
         if (j0 + jj < UPL) {
           const uint2 w = R.I[j0 + jj];
           cv[jj][0] = buf_u128(bcb, (w.x & 0xffffu) << 4, 0);
           cv[jj][1] = buf_u128(bcb, (w.x >> 16) << 4, 0);
           cv[jj][2] = buf_u128(bcb, (w.y & 0xffffu) << 4, 0);
           cv[jj][3] = buf_u128(bcb, (w.y >> 16) << 4, 0);
+          if constexpr (B1 == 16) {
+            const uint2 w1 = R.I1[j0 + jj];
+            cv1[jj][0] = buf_u128(bcb1, (w1.x & 0xffffu) << 4, 0);
+            cv1[jj][1] = buf_u128(bcb1, (w1.x >> 16) << 4, 0);
+            cv1[jj][2] = buf_u128(bcb1, (w1.y & 0xffffu) << 4, 0);
+            cv1[jj][3] = buf_u128(bcb1, (w1.y >> 16) << 4, 0);
+          }
         }
       }
 #pragma unroll
-      for (int jj = 0; jj < kL2Batch; ++jj) {
+      for (int jj = 0; jj < kBatch; ++jj) {
         if (j0 + jj < UPL) {
           const int col0 = 32 * (lane + 64 * (j0 + jj));
-          float d = 0.f;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 x0 = *reinterpret_cast<const float4 *>(&s_x[col0 + 8 * q]);
-            const float4 x1 = *reinterpret_cast<const float4 *>(&s_x[col0 + 8 * q + 4]);
-            const uint4 c = cv[jj][q];
+          // products of one stage's vector with the 8 x of group q
+          auto dot8 = [&](const uint4 c, const float4 x0, const float4 x1, float d) {
             d = fmaf(h2f(c.x & 0xffffu), x0.x, d);
             d = fmaf(h2f(c.x >> 16), x0.y, d);
             d = fmaf(h2f(c.y & 0xffffu), x0.z, d);
@@ -114,7 +135,19 @@ __global__ __launch_bounds__(kL2Waves * 64) void k_gemv_l2(GemvArgs a, int xt) {
             d = fmaf(h2f(c.z >> 16), x1.y, d);
             d = fmaf(h2f(c.w & 0xffffu), x1.z, d);
             d = fmaf(h2f(c.w >> 16), x1.w, d);
+            return d;
+          };
+          float d = 0.f, d1 = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 x0 = *reinterpret_cast<const float4 *>(&s_x[col0 + 8 * q]);
+            const float4 x1 = *reinterpret_cast<const float4 *>(&s_x[col0 + 8 * q + 4]);
+            d = dot8(cv[jj][q], x0, x1, d);
+            if constexpr (B1 == 16) d1 = dot8(cv1[jj][q], x0, x1, d1);
+            if constexpr (B1 == 8) d1 = dot8(s_cb1[(R.I1[j0 + jj].x >> (8 * q)) & 0xffu], x0, x1, d1);
           }
+          // residual: its own sum, then the stage scales (1 without them)
+          if (B1 || RS) d = B1 ? fmaf(r1, d1, r0 * d) : r0 * d;
           acc = fmaf(h2f(R.S[j0 + jj]), d, acc);
         }
       }
@@ -137,37 +170,55 @@ __global__ __launch_bounds__(kL2Waves * 64) void k_gemv_l2(GemvArgs a, int xt) {
   if (r < nrows) compute_row(r, R0);
 }
 
-template <int UPL>
-void launch_u(const GemvArgs &a, int xt, int cus, hipStream_t s) {
-  int g = (a.n + kL2Waves - 1) / kL2Waves;
-  if (g > cus) g = cus;
-  hipLaunchKernelGGL((k_gemv_l2<UPL>), dim3(g), dim3(kL2Waves * 64), 0, s, a, xt);
+template <int UPL, int B1, bool RS>
+bool launch_u(const GemvArgs &a, int xt, int cus, hipStream_t s) {
+  if constexpr (UPL > l2_max_upl<B1>()) {
+    return false;
+  } else {
+    int g = (a.n + kL2Waves - 1) / kL2Waves;
+    if (g > cus) g = cus;
+    hipLaunchKernelGGL((k_gemv_l2<UPL, B1, RS>), dim3(g), dim3(kL2Waves * 64), 0, s, a, xt);
+    return true;
+  }
+}
+
+template <int B1, bool RS>
+bool launch_f(const GemvArgs &a, int xt, int cus, hipStream_t s) {
+  switch (a.k / 2048) {
+    case 1: return launch_u<1, B1, RS>(a, xt, cus, s);
+    case 2: return launch_u<2, B1, RS>(a, xt, cus, s);
+    case 3: return launch_u<3, B1, RS>(a, xt, cus, s);
+    case 4: return launch_u<4, B1, RS>(a, xt, cus, s);
+    case 5: return launch_u<5, B1, RS>(a, xt, cus, s);
+    case 6: return launch_u<6, B1, RS>(a, xt, cus, s);
+    case 7: return launch_u<7, B1, RS>(a, xt, cus, s);
+    case 8: return launch_u<8, B1, RS>(a, xt, cus, s);
+    case 9: return launch_u<9, B1, RS>(a, xt, cus, s);
+    case 10: return launch_u<10, B1, RS>(a, xt, cus, s);
+    case 11: return launch_u<11, B1, RS>(a, xt, cus, s);
+    case 12: return launch_u<12, B1, RS>(a, xt, cus, s);
+    case 13: return launch_u<13, B1, RS>(a, xt, cus, s);
+    case 14: return launch_u<14, B1, RS>(a, xt, cus, s);
+    case 15: return launch_u<15, B1, RS>(a, xt, cus, s);
+    case 16: return launch_u<16, B1, RS>(a, xt, cus, s);
+    default: return false;
+  }
 }
 
 }  // namespace
 
 bool launch_gemv_l2(const WView &w, const GemvArgs &a, int xt, int cus, hipStream_t s) {
-  if (!plain_format(w) || w.bits != 16 || w.S != 1) return false;
-  if (w.k % 2048 != 0 || w.k > kL2MaxK || w.bs % 32 != 0) return false;
-  switch (w.k / 2048) {
-    case 1: launch_u<1>(a, xt, cus, s); return true;
-    case 2: launch_u<2>(a, xt, cus, s); return true;
-    case 3: launch_u<3>(a, xt, cus, s); return true;
-    case 4: launch_u<4>(a, xt, cus, s); return true;
-    case 5: launch_u<5>(a, xt, cus, s); return true;
-    case 6: launch_u<6>(a, xt, cus, s); return true;
-    case 7: launch_u<7>(a, xt, cus, s); return true;
-    case 8: launch_u<8>(a, xt, cus, s); return true;
-    case 9: launch_u<9>(a, xt, cus, s); return true;
-    case 10: launch_u<10>(a, xt, cus, s); return true;
-    case 11: launch_u<11>(a, xt, cus, s); return true;
-    case 12: launch_u<12>(a, xt, cus, s); return true;
-    case 13: launch_u<13>(a, xt, cus, s); return true;
-    case 14: launch_u<14>(a, xt, cus, s); return true;
-    case 15: launch_u<15>(a, xt, cus, s); return true;
-    case 16: launch_u<16>(a, xt, cus, s); return true;
-    default: return false;
+  if (w.S < 1 || w.S > 2 || w.sb[0] != 16) return false;
+  if (w.k % 2048 != 0 || w.k > kL2MaxK || w.k / 2048 > 16) return false;
+  if (w.bs % 32 != 0 || (2048 % w.bs != 0 && w.bs < w.k)) return false;
+  const int b1 = w.S == 2 ? w.sb[1] : 0;
+  if (b1 != 0 && b1 != 8 && b1 != 16) return false;
+  if (!w.scaled) {
+    if (b1 == 0) return launch_f<0, false>(a, xt, cus, s);
+    return b1 == 8 ? launch_f<8, false>(a, xt, cus, s) : launch_f<16, false>(a, xt, cus, s);
   }
+  if (b1 == 0) return launch_f<0, true>(a, xt, cus, s);
+  return b1 == 8 ? launch_f<8, true>(a, xt, cus, s) : launch_f<16, true>(a, xt, cus, s);
 }
 
 }  // namespace vqmm

@@ -1,8 +1,9 @@
 """Parity of the 16-bit-index decode kernel with deep L2-gather pipelining
-(one stage of 16-bit indices into a 65,536-entry codebook, GLQ page "How it
-works" / "Bit widths") with the CPU oracle, through the C ABI.  Shapes route
-to it: K % 2048 == 0, K <= 32768, scale blocks of whole 32-column units.  The
-bar: |y - y_ref| <= 2e-3 sum|w x| + 1e-6.
+(a stage of 16-bit indices into a 65,536-entry codebook, GLQ page "How it
+works" / "Bit widths", alone or with an 8- or 16-bit residual stage and stage
+scales) with the CPU oracle, through the C ABI.  Shapes route to it: K % 2048
+== 0, K <= 32768 (less with a residual), scale blocks of 32-column units that
+divide 2048 or cover the row.  The bar: |y - y_ref| <= 2e-3 sum|w x| + 1e-6.
 """
 import numpy as np
 import pytest
@@ -65,3 +66,50 @@ def test_l2_gemv_batch_tokens(vq):
     torch.cuda.synchronize()
     y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
     assert_within(y.cpu().numpy(), y_ref, bound, "800x4096 B=3")
+
+
+# (widths, stage-scale range, N, K, scale block, x dtype): a 16-bit primary
+# with an 8-bit or a 16-bit residual, with and without stage scales; K up to
+# the most units per lane each residual width takes (14 for 8 bits, 13 for 16
+# bits), and past it (the general kernel) for the 16-bit residual
+LADDERS = [((16, 8), (0.2, 0.4), 1000, 8192, 128, "bf16"), ((16, 8), None, 333, 28672, None, "f32"),
+           ((16, 16), (0.2, 0.4), 2057, 4096, 32, "f32"), ((16, 16), None, 517, 26624, 2048, "bf16"),
+           ((16, 16), (0.3, 0.5), 260, 28672, None, "bf16"), ((16, 8), (0.25, 0.5), 7, 2048, None, "bf16")]
+
+
+@pytest.mark.parametrize("widths,rs,n,k,bs,xdt", LADDERS)
+def test_l2_gemv_ladder(vq, widths, rs, n, k, bs, xdt):
+    import torch
+    sd = (0.02, 0.02 if rs else 0.006)
+    sw = vqsynth.random_weight(n, k, 2, list(widths), bs, seed=n + 3 * k, cb_sd=sd, stage_scale_range=rs)
+    xs, x64 = vqsynth.make_x(1, k, xdt, np.random.SeedSequence(k + 7))
+    y = vq.vq_gemv(device_weight(sw), x_to_device(xs, xdt))
+    torch.cuda.synchronize()
+    rows = None if n * k <= (1 << 22) else sample_rows(n, 96, 6)
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw, rows), x64)
+    got = y.cpu().numpy() if rows is None else y.cpu().numpy()[:, rows]
+    assert_within(got, y_ref, bound, f"{widths} rs={rs} {n}x{k} bs={bs} {xdt}")
+
+
+def test_l2_gemv_block_not_dividing_2048(vq):
+    """A scale block of 96 columns takes the general kernel; same bar."""
+    import torch
+    sw = vqsynth.random_weight(300, 6144, 1, 16, 96, seed=12)
+    xs, x64 = vqsynth.make_x(1, 6144, "bf16", np.random.SeedSequence(13))
+    y = vq.vq_gemv(device_weight(sw), x_to_device(xs, "bf16"))
+    torch.cuda.synchronize()
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
+    assert_within(y.cpu().numpy(), y_ref, bound, "300x6144 bs=96")
+
+
+def test_l2_gemv_ladder_sparse(vq):
+    """16+8 with stage scales and a sparse correction (added by its own
+    kernel after the product)."""
+    import torch
+    sw = vqsynth.random_weight(700, 4096, 2, [16, 8], 128, seed=21, cb_sd=(0.02, 0.02), stage_scale_range=(0.2, 0.4),
+                               sparse_density=0.01)
+    xs, x64 = vqsynth.make_x(1, 4096, "bf16", np.random.SeedSequence(22))
+    y = vq.vq_gemv(device_weight(sw), x_to_device(xs, "bf16"))
+    torch.cuda.synchronize()
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
+    assert_within(y.cpu().numpy(), y_ref, bound, "16+8/rs sparse")
