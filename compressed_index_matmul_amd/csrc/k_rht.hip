@@ -59,6 +59,10 @@ __device__ __forceinline__ void rht_block(const RhtArgs &a, int b, int &off, int
 template <int RM, bool BF16>
 __global__ __launch_bounds__(kRhtThreads) void k_rht_vec(RhtArgs a) {
   __shared__ float buf[kRhtMaxBlock];
+  // element i lives at i ^ ((i >> 6) & 63): the six low bits are XORed with
+  // the next six, so the register-stage stores (lane stride r = 8..32
+  // floats) spread over all 64 banks, and 64-float runs stay conflict-free
+  auto at = [](int i) { return i ^ ((i >> 6) & 63); };
   const int blk = blockIdx.x % a.nblocks;
   const int row = blockIdx.x / a.nblocks;
   int off, nb;
@@ -104,37 +108,63 @@ __global__ __launch_bounds__(kRhtThreads) void k_rht_vec(RhtArgs a) {
     }
 #pragma unroll
   for (int q = 0; q < RM; ++q)
-    if (q < r) buf[i0 + q] = v[q];
-  // stages h = r, 2r, ...: two per pass on groups {i, i+h, i+2h, i+3h}
-  int h = r;
-  for (; 4 * h <= nb; h *= 4) {
+    if (q < r) buf[at(i0 + q)] = v[q];
+  // stages h = r, 2r, ...: two per pass on groups {i, i+h, i+2h, i+3h}.
+  // A pass's r/4 groups per thread are disjoint, so all their loads go out
+  // before any store (one LDS round trip per pass).
+  int h = r, lh = __builtin_ctz((unsigned)r);
+  for (; 4 * h <= nb; h *= 4, lh += 2) {
     __syncthreads();
-    for (int p = tid; p < nb / 4; p += kRhtThreads) {
-      const int i = (p / h) * 4 * h + (p % h);
-      const float x0 = buf[i], x1 = buf[i + h], x2 = buf[i + 2 * h], x3 = buf[i + 3 * h];
-      const float s0 = x0 + x1, d0 = x0 - x1, s1 = x2 + x3, d1 = x2 - x3;
-      buf[i] = s0 + s1;
-      buf[i + h] = d0 + d1;
-      buf[i + 2 * h] = s0 - s1;
-      buf[i + 3 * h] = d0 - d1;
-    }
+    float x[RM];
+    int ix[RM / 4];
+#pragma unroll
+    for (int it = 0; it < RM / 4; ++it)
+      if (4 * it < r) {  // workgroup-uniform
+        const int p = tid + it * kRhtThreads;
+        const int i = ((p >> lh) << (lh + 2)) | (p & (h - 1));
+        ix[it] = i;
+        x[4 * it] = buf[at(i)];
+        x[4 * it + 1] = buf[at(i + h)];
+        x[4 * it + 2] = buf[at(i + 2 * h)];
+        x[4 * it + 3] = buf[at(i + 3 * h)];
+      }
+#pragma unroll
+    for (int it = 0; it < RM / 4; ++it)
+      if (4 * it < r) {
+        const int i = ix[it];
+        const float x0 = x[4 * it], x1 = x[4 * it + 1], x2 = x[4 * it + 2], x3 = x[4 * it + 3];
+        const float s0 = x0 + x1, d0 = x0 - x1, s1 = x2 + x3, d1 = x2 - x3;
+        buf[at(i)] = s0 + s1;
+        buf[at(i + h)] = d0 + d1;
+        buf[at(i + 2 * h)] = s0 - s1;
+        buf[at(i + 3 * h)] = d0 - d1;
+      }
   }
   if (h < nb) {  // one stage left
     __syncthreads();
-    for (int p = tid; p < nb / 2; p += kRhtThreads) {
-      const int i = (p / h) * 2 * h + (p % h);
-      const float x0 = buf[i], x1 = buf[i + h];
-      buf[i] = x0 + x1;
-      buf[i + h] = x0 - x1;
-    }
+    float x[RM];
+    int ix[RM / 2];
+#pragma unroll
+    for (int it = 0; it < RM / 2; ++it)
+      if (2 * it < r) {
+        const int p = tid + it * kRhtThreads;
+        const int i = ((p >> lh) << (lh + 1)) | (p & (h - 1));
+        ix[it] = i;
+        x[2 * it] = buf[at(i)];
+        x[2 * it + 1] = buf[at(i + h)];
+      }
+#pragma unroll
+    for (int it = 0; it < RM / 2; ++it)
+      if (2 * it < r) {
+        buf[at(ix[it])] = x[2 * it] + x[2 * it + 1];
+        buf[at(ix[it] + h)] = x[2 * it] - x[2 * it + 1];
+      }
   }
   __syncthreads();
   const float sc = (float)(1.0 / __builtin_sqrt((double)nb));
   float4 *po = reinterpret_cast<float4 *>(a.out + base);
-  for (int i = tid; i < nb / 4; i += kRhtThreads) {
-    const float4 u = reinterpret_cast<const float4 *>(buf)[i];
-    po[i] = make_float4(u.x * sc, u.y * sc, u.z * sc, u.w * sc);
-  }
+  for (int i = tid; i < nb / 4; i += kRhtThreads)
+    po[i] = make_float4(buf[at(4 * i)] * sc, buf[at(4 * i + 1)] * sc, buf[at(4 * i + 2)] * sc, buf[at(4 * i + 3)] * sc);
 }
 
 template <int R>
