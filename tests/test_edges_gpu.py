@@ -7,7 +7,8 @@ import pytest
 
 import oracle
 import vqsynth
-from vqtest import assert_within, device_weight, ensure_built, oracle_indices, oracle_w16, oracle_w64, x_to_device
+from vqtest import (assert_within, device_weight, ensure_built, oracle_indices, oracle_w16, oracle_w64, sample_rows,
+                    x_to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -208,6 +209,23 @@ def test_gemm_tile_ragged(vq, m, n, k, st, bits, bs):
     torch.cuda.synchronize()
     y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
     assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"gemm {m}x{n}x{k} bs {bs}")
+
+
+@pytest.mark.parametrize("m,n,k,st,bits,bs", [(1900, 14300, 512, 2, 12, 128), (2048, 14336, 256, 2, 12, 128),
+                                             (2048, 8192, 256, 2, 12, 256), (1800, 12000, 512, 1, 8, 64)])
+def test_gemm_wide_row_tiles(vq, m, n, k, st, bits, bs):
+    """The 256 x 256 wide kernel at its large shapes: a partly filled last
+    round of tiles (14300, 14336 and 12000 rows at 8 token panels), one full
+    round (8192 rows), ragged tokens and rows; sampled output columns
+    (tile edges included) against the oracle."""
+    import torch
+    sw = vqsynth.random_weight(n, k, st, bits, bs, seed=m + n + k)
+    xs, x64 = _x(m, k, "bf16", m * 5 + n)
+    y = vq.vq_gemm(device_weight(sw), x_to_device(xs, "bf16"))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([sample_rows(n, 96, n), [0, 223, 224, 255, 256, n - 1]]))
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw, rows), x64)
+    assert_bf16_path(y.cpu().numpy()[:, rows], y_ref, bound, k, f"gemm {m}x{n}x{k} bs {bs}")
 
 
 @pytest.mark.parametrize("m,n,k,st,bits,bs", [(17, 4096, 512, 2, 12, 128), (40, 8200, 1024, 1, 8, 1024),
