@@ -1,11 +1,15 @@
 // Sparse correction of the products: y[b][r] += sum_j val_j x[b][col_j] over
 // the correction's row r (orka README, "How it works": the decoded weight
 // plus a sparse correction), launched after the main product on the same
-// stream.  CSR over output rows; fp16 values, fp32 products and sums in
-// storage order (fixed, no atomics).
+// stream.  CSR over output rows; fp16 values, fp32 products and sums in a
+// fixed order (no atomics).
 //
 // Up to 8 tokens: one wave per row, lanes split the row's entries, one wave
 // sum per token.
+// 9 to 64 tokens: one wave per (row, block of 16 tokens); lane = (entry
+// slot e = lane / 16, token lane % 16), slot e takes entries e, e + 4, ...
+// of the row in storage order, and the four slots are added in a fixed
+// order across lanes.
 // More tokens: one wave per (row, 64 tokens), lane = token, the row's
 // entries in storage order (value and column are wave-uniform loads).  The
 // decode kernel fuses the correction itself where it runs; this launch
@@ -62,6 +66,26 @@ __global__ __launch_bounds__(256) void k_sparse_few(SparseArgs a) {
   }
 }
 
+// tokens 16 blockIdx.y .. + 15 (those below m)
+__global__ __launch_bounds__(256) void k_sparse_mid(SparseArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (r >= a.n) return;
+  const int e = lane >> 4;
+  const int b = 16 * blockIdx.y + (lane & 15);
+  const int bc = min(b, a.m - 1);  // tokens past m load a valid row, never stored
+  int lo, hi;
+  sp_range(a, r, lo, hi);
+  float acc = 0.f;
+  for (int j = lo + e; j < hi; j += 4) {
+    const int c = a.col[j];
+    if (c >= 0 && c < a.k) acc = fmaf(h2f(a.val[j]), sp_x(a, bc, c), acc);
+  }
+  acc += __shfl_xor(acc, 16);  // slots (0 + 1), (2 + 3)
+  acc += __shfl_xor(acc, 32);  // then their sum
+  if (e == 0 && b < a.m) a.y[(size_t)b * a.n + r] += acc;
+}
+
 __global__ __launch_bounds__(256) void k_sparse_many(SparseArgs a) {
   const int lane = threadIdx.x & 63;
   const int tb = (a.m + 63) / 64;
@@ -83,11 +107,12 @@ __global__ __launch_bounds__(256) void k_sparse_many(SparseArgs a) {
 hipError_t launch_sparse_add(const WView &w, const void *x, int xt, int m, float *y, hipStream_t s) {
   if (w.sp_nnz <= 0) return hipSuccess;
   SparseArgs a{w.sp_rowptr, w.sp_col, w.sp_val, x, y, w.sp_nnz, w.n, w.k, m, xt};
-  if (m <= 8) {
+  if (m <= 64) {
     const unsigned blocks = (unsigned)((w.n + 3) / 4);
     if (m <= 1) hipLaunchKernelGGL(k_sparse_few<1>, dim3(blocks), dim3(256), 0, s, a);
     else if (m <= 4) hipLaunchKernelGGL(k_sparse_few<4>, dim3(blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(k_sparse_few<8>, dim3(blocks), dim3(256), 0, s, a);
+    else if (m <= 8) hipLaunchKernelGGL(k_sparse_few<8>, dim3(blocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_sparse_mid, dim3(blocks, (unsigned)((m + 15) / 16)), dim3(256), 0, s, a);
   } else {
     const int64_t items = (int64_t)w.n * ((m + 63) / 64);
     hipLaunchKernelGGL(k_sparse_many, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, a);

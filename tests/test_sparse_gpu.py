@@ -113,7 +113,7 @@ def test_sparse_gemv_one_hot(vq):
 
 
 @pytest.mark.parametrize("fmt", FORMATS, ids=fmt_id)
-@pytest.mark.parametrize("m", [16, 64, 300])
+@pytest.mark.parametrize("m", [16, 40, 64, 300])
 def test_sparse_gemm(vq, fmt, m):
     import torch
     sw = make(fmt, 4096, 1024, 128, 23, 0.01)
