@@ -98,6 +98,22 @@ def test_sparse_gemv(vq, fmt, xdt, batch):
     assert_within(y.cpu().numpy(), y_ref, bound, f"{fmt_id(fmt)} {xdt} B={batch}")
 
 
+@pytest.mark.parametrize("k,xdt", [(576, "bf16"), (4096, "bf16"), (4096, "f32"), (6144, "bf16")],
+                         ids=["x-copied-per-lane", "x-lds-direct", "x-gathered-f32", "x-gathered-bf16"])
+def test_sparse_mid_tokens(vq, k, xdt):
+    """9-64 tokens on the separate correction kernel: x of the token block in
+    LDS (copied by lanes when a row is not whole 1 KiB pieces, by LDS-direct
+    loads when it is) or gathered from global memory (more than 8 KiB per
+    token); 12 tokens, ragged against the 16-token block."""
+    import torch
+    sw = with_duplicates(make(((12, 12), None), 333, k, 64, 41 + k, 0.02))
+    xs, x64 = vqsynth.make_x(12, k, xdt, np.random.SeedSequence(k))
+    y = vq.vq_gemv(device_weight(sw), x_to_device(xs, xdt))
+    torch.cuda.synchronize()
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
+    assert_within(y.cpu().numpy(), y_ref, bound, f"k={k} {xdt}")
+
+
 def test_sparse_gemv_one_hot(vq):
     """x = e_c recovers the corrected column c (fp32 x, one token)."""
     import torch
