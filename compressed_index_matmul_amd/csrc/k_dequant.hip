@@ -4,9 +4,9 @@
 //
 // One thread per group.  The stage sum and the product with the scale are
 // formed in float64, where they are exact (at most four fp16 terms and an
-// fp16 factor need < 53 significant bits), and rounded once to fp16 with
-// integer arithmetic on the bit pattern, so the result is the correctly
-// rounded value whatever the summation order.  Write-bandwidth bound.  A
+// fp16 factor need < 53 significant bits), and rounded once to fp16 (round
+// to odd into float, then the hardware conversion; see f64_to_f16_rne_fast),
+// so the result is the correctly rounded value whatever the summation order.  Write-bandwidth bound.  A
 // sparse correction (orka README, "How it works": the decode plus a sparse
 // correction) is added to the float64 value entry by entry, in storage
 // order, before the one rounding.
@@ -18,6 +18,15 @@
 // significant bits), the products are added from stage 0 up with float64
 // rounding and the sum is multiplied by the block scale in float64 -- a
 // fixed order, so the fp16 result is reproducible bit for bit.
+//
+// k_dequant_lds serves the formats whose codebooks fit LDS (8- and 12-bit
+// stages, the ladders the decode kernels take) with K % 32 == 0: a
+// persistent grid stages the codebooks once per workgroup, each thread
+// takes four consecutive groups of a row at a time (one 4-byte load of low
+// bytes and one 2-byte load of nibbles per stage, the next four groups'
+// loads in flight), gathers from LDS, and writes 64 contiguous bytes.  The
+// arithmetic per group is the same float64 sequence as above, so both
+// kernels give identical bits.
 #include "vqmm_device.h"
 #include "vqmm_internal.h"
 
@@ -92,8 +101,162 @@ __global__ __launch_bounds__(256) void k_unpack_dequant(DequantArgs a) {
   }
   uint32_t o[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) o[j] = f64_to_f16_rne(wv[2 * j]) | (f64_to_f16_rne(wv[2 * j + 1]) << 16);
+  for (int j = 0; j < 4; ++j) o[j] = f64_to_f16_rne_fast(wv[2 * j]) | (f64_to_f16_rne_fast(wv[2 * j + 1]) << 16);
   reinterpret_cast<uint4 *>(a.w_out + r * (int64_t)a.k)[g] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+constexpr int kDqThreads = 1024;
+
+// value of group f (row r, group g of the row) from its stage entries (c_t
+// already gathered), in the float64 order of k_unpack_dequant, stored as 8
+// fp16
+template <int S, bool RS>
+__device__ __forceinline__ void dequant_group(const DequantArgs &a, const uint4 (&v)[S], int64_t r, int g) {
+  double acc[8];
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    const uint32_t h[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      double c = (double)h2f((h[j >> 1] >> ((j & 1) * 16)) & 0xffffu);
+      if (RS) c *= (double)a.rs[t];  // exact product
+      acc[j] = (t == 0) ? c : acc[j] + c;
+    }
+  }
+  const double sc = (double)h2f(a.sc[r * a.nblk + (8 * g) / a.bs]);
+  double wv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) wv[j] = sc * acc[j];
+  if (a.sp_nnz > 0) {
+    const int lo = min(max(a.sp_rowptr[r], 0), a.sp_nnz);
+    const int hi = min(max(a.sp_rowptr[r + 1], lo), a.sp_nnz);
+    int b0 = lo, b1 = hi;
+    while (b0 < b1) {
+      const int mid = (b0 + b1) >> 1;
+      if (a.sp_col[mid] < 8 * g) b0 = mid + 1;
+      else b1 = mid;
+    }
+    for (int j = b0; j < hi; ++j) {
+      const int c = a.sp_col[j] - 8 * g;
+      if (c >= 8) break;
+      if (c < 0) continue;
+      const double sv = (double)h2f(a.sp_val[j]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q == c) wv[q] = wv[q] + sv;
+    }
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = f64_to_f16_rne_fast(wv[2 * j]) | (f64_to_f16_rne_fast(wv[2 * j + 1]) << 16);
+  reinterpret_cast<uint4 *>(a.w_out + r * (int64_t)a.k)[g] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+template <class LD, bool RS>
+__global__ __launch_bounds__(kDqThreads) void k_dequant_lds(DequantArgs a) {
+  constexpr int S = LD::S;
+  __shared__ uint4 s_cb[LD::kRows];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t quads = a.total / 4;  // G % 4 == 0: a quad never crosses a row
+  const int64_t stride = (int64_t)gridDim.x * kDqThreads;
+  struct QIdx {
+    uint32_t lo[S];  // four low bytes
+    uint32_t hi[S];  // four nibbles
+  };
+  auto load_q = [&](int64_t q, QIdx &I) {
+    const int64_t f0 = 4 * (q < quads ? q : quads - 1);  // past the end: the last quad again
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+      I.lo[t] = LD::lo(t) ? *reinterpret_cast<const uint32_t *>(a.lo[t] + f0) : 0u;
+      I.hi[t] = LD::hi(t) ? *reinterpret_cast<const uint16_t *>(a.hi[t] + (f0 >> 1)) : 0u;
+    }
+  };
+  int64_t q = (int64_t)blockIdx.x * kDqThreads + tid;
+  QIdx cur;
+  load_q(q, cur);
+  if constexpr (LD::kUniform) {
+    constexpr int BITS = LD::bits(0);
+    constexpr int CBN = S << BITS;
+    for (int blk = wave * 64; blk < CBN; blk += kDqThreads) {  // wave-uniform
+      lds_direct_16(reinterpret_cast<const uint4 *>(uniform_ptr(a.cb[blk >> BITS])) + (blk & ((1 << BITS) - 1)) + lane,
+                    s_cb + blk);
+    }
+  } else {
+    stage_ladder_lds<LD, kDqThreads / 64>(a.cb, s_cb, wave, lane);
+  }
+  wait_all_memory();  // the codebooks (LDS-direct) have landed
+  __syncthreads();
+  for (; q < quads; q += stride) {
+    QIdx nxt;
+    load_q(q + stride, nxt);
+    const int64_t f0 = 4 * q;
+    const int64_t r = f0 / a.G;
+    const int g0 = (int)(f0 - r * a.G);
+    uint32_t id[S][4];
+#pragma unroll
+    for (int t = 0; t < S; ++t)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        uint32_t idx = 0;
+        if (LD::lo(t)) idx = (cur.lo[t] >> (8 * gg)) & 0xffu;
+        if (LD::hi(t)) idx |= ((cur.hi[t] >> (4 * gg)) & 0xfu) << LD::hshift(t);
+        id[t][gg] = idx;
+      }
+    if (a.idx_out) {
+#pragma unroll
+      for (int t = 0; t < S; ++t)
+        *reinterpret_cast<uint2 *>(a.idx_out + (int64_t)t * a.total + f0) =
+            make_uint2(id[t][0] | (id[t][1] << 16), id[t][2] | (id[t][3] << 16));
+    }
+    if (a.w_out) {
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        uint4 v[S];
+#pragma unroll
+        for (int t = 0; t < S; ++t) v[t] = s_cb[LD::off(t) + id[t][gg]];
+        dequant_group<S, RS>(a, v, r, g0 + gg);
+      }
+    }
+    cur = nxt;
+  }
+}
+
+template <class LD, bool RS>
+static void launch_dq(const DequantArgs &a, hipStream_t s) {
+  const int64_t need = (a.total / 4 + kDqThreads - 1) / kDqThreads;
+  const int cus = device_cu_count();
+  const unsigned grid = (unsigned)(need < cus ? need : cus);
+  hipLaunchKernelGGL((k_dequant_lds<LD, RS>), dim3(grid), dim3(kDqThreads), 0, s, a);
+}
+
+// the LDS kernel for this format, if it has one (false: nothing launched)
+static bool launch_dequant_lds(const WView &w, const DequantArgs &a, hipStream_t s) {
+  if (w.k % 32 != 0) return false;
+  const int b0 = w.sb[0], b1 = w.S > 1 ? w.sb[1] : 0;
+  if (w.uniform && !w.scaled) {
+    if (w.bits == 12 && w.S == 1) return launch_dq<Ladder<12>, false>(a, s), true;
+    if (w.bits == 12 && w.S == 2) return launch_dq<Ladder<12, 12>, false>(a, s), true;
+    if (w.bits == 8 && w.S == 1) return launch_dq<Ladder<8>, false>(a, s), true;
+    if (w.bits == 8 && w.S == 2) return launch_dq<Ladder<8, 8>, false>(a, s), true;
+    if (w.bits == 8 && w.S == 3) return launch_dq<Ladder<8, 8, 8>, false>(a, s), true;
+    if (w.bits == 8 && w.S == 4) return launch_dq<Ladder<8, 8, 8, 8>, false>(a, s), true;
+    return false;
+  }
+  if (w.S > 2) return false;
+  if (!w.scaled) {
+    if (b0 == 12 && b1 == 4) return launch_dq<Ladder<12, 4>, false>(a, s), true;
+    if (b0 == 8 && b1 == 4) return launch_dq<Ladder<8, 4>, false>(a, s), true;
+    return false;
+  }
+  if (b0 == 12 && b1 == 0) return launch_dq<Ladder<12>, true>(a, s), true;
+  if (b0 == 8 && b1 == 0) return launch_dq<Ladder<8>, true>(a, s), true;
+  if (b0 == 12 && b1 == 12) return launch_dq<Ladder<12, 12>, true>(a, s), true;
+  if (b0 == 8 && b1 == 8) return launch_dq<Ladder<8, 8>, true>(a, s), true;
+  if (b0 == 12 && b1 == 4) return launch_dq<Ladder<12, 4>, true>(a, s), true;
+  if (b0 == 8 && b1 == 4) return launch_dq<Ladder<8, 4>, true>(a, s), true;
+  return false;
 }
 
 hipError_t launch_unpack_dequant(const WView &w, uint16_t *idx_out, uint16_t *w_out, hipStream_t s) {
@@ -122,6 +285,7 @@ hipError_t launch_unpack_dequant(const WView &w, uint16_t *idx_out, uint16_t *w_
   a.sp_rowptr = w.sp_rowptr;
   a.sp_col = w.sp_col;
   a.sp_val = w.sp_val;
+  if (launch_dequant_lds(w, a, s)) return hipGetLastError();
   const unsigned blocks = (unsigned)((a.total + 255) / 256);
   if (!plain_format(w))
     hipLaunchKernelGGL(k_unpack_dequant<0>, dim3(blocks), dim3(256), 0, s, a);

@@ -60,6 +60,25 @@ __device__ __forceinline__ uint32_t f64_to_f16_rne(double d) {
   return sign | ((uint32_t)(E + 15) << 10) | (uint32_t)(n - 1024);
 }
 
+// The same rounding through the hardware conversions (a few instructions
+// instead of some forty): d is rounded to float with the low bit forced to
+// 1 when inexact (round to odd: the float has 24 significant bits, at least
+// two more than binary16's 11, so the float -> binary16 rounding to nearest
+// even then equals the direct one), and NaN, infinity and magnitudes from
+// 65504 up take the integer path.
+__device__ __forceinline__ uint32_t f64_to_f16_rne_fast(double d) {
+  if (!(__builtin_fabs(d) < 65504.0)) return f64_to_f16_rne(d);
+  const float f = (float)d;  // nearest, ties to even
+  uint32_t fb = __float_as_uint(f);
+  const double back = (double)f;
+  if (back != d) {
+    if (__builtin_fabs(back) > __builtin_fabs(d)) fb -= 1u;  // the float toward zero
+    fb |= 1u;                                                  // sticky bit
+  }
+  const _Float16 h = (_Float16)__uint_as_float(fb);          // nearest, ties to even
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
 // Sum over the 64 lanes of a wave in a fixed order (DPP within rows of 16,
 // then the four row totals added lane 0 + 16 + 32 + 48).  Result valid in
 // every lane.

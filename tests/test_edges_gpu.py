@@ -166,6 +166,30 @@ def test_dequant_extreme_values(vq, seed):
     assert np.array_equal(w_d.cpu().numpy().view(np.uint16), want.view(np.uint16))
 
 
+@pytest.mark.parametrize("bits,st", [(8, 2), (12, 1), (8, 4)])
+def test_dequant_random_bit_patterns(vq, bits, st):
+    """Codebooks and scales drawn as random finite fp16 bit patterns (every
+    exponent, subnormals, both signs), so the single rounding of the exact
+    value meets ties, subnormal results and overflow in bulk: every weight
+    bit-exact."""
+    import torch
+    rng = np.random.default_rng(bits * 10 + st)
+
+    def finite_bits(shape):
+        b = rng.integers(0, 1 << 16, size=shape, dtype=np.uint32).astype(np.uint16)
+        b[(b & 0x7c00) == 0x7c00] &= 0xbfff  # inf / NaN exponents -> a finite one
+        return b.view(np.float16)
+
+    sw = vqsynth.random_weight(512, 256, st, bits, 32, seed=bits + st)
+    sw.codebooks = [finite_bits(((1 << bits), 8)) for _ in range(st)]
+    sw.scales = finite_bits(sw.scales.shape)
+    _, w_d = vq.vq_unpack_dequant(device_weight(sw), want_idx=False)
+    torch.cuda.synchronize()
+    with np.errstate(over="ignore", invalid="ignore"):
+        want = oracle_w16(sw)
+    assert np.array_equal(w_d.cpu().numpy().view(np.uint16), want.view(np.uint16))
+
+
 def test_dequant_double_rounding_trap(vq):
     """The hand-derived trap (s=0.75, cb0=2+3*2^-9, cb1=2^-24) rounds once."""
     import json
