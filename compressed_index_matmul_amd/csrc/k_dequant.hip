@@ -5,7 +5,7 @@
 // One thread per group.  The stage sum and the product with the scale are
 // formed in float64, where they are exact (at most four fp16 terms and an
 // fp16 factor need < 53 significant bits), and rounded once to fp16 (round
-// to odd into float, then the hardware conversion; see f64_to_f16_rne_fast),
+// to odd into float, then the hardware conversion; see round_group_f16),
 // so the result is the correctly rounded value whatever the summation order.  Write-bandwidth bound.  A
 // sparse correction (orka README, "How it works": the decode plus a sparse
 // correction) is added to the float64 value entry by entry, in storage
@@ -49,6 +49,25 @@ struct DequantArgs {
   const int32_t *sp_col;
   const uint16_t *sp_val;
 };
+
+// The eight fp16 results of a group, two per word: one test for the group,
+// the hardware rounding when all eight are finite and below 65504, else the
+// integer rounding for all eight (both round the float64 value once, to
+// nearest even).
+__device__ __forceinline__ uint4 round_group_f16(const double (&wv)[8]) {
+  bool easy = true;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) easy = easy && __builtin_fabs(wv[j]) < 65504.0;
+  uint32_t o[4];
+  if (easy) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = f64_to_f16_rn_odd(wv[2 * j]) | (f64_to_f16_rn_odd(wv[2 * j + 1]) << 16);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = f64_to_f16_rne(wv[2 * j]) | (f64_to_f16_rne(wv[2 * j + 1]) << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
 
 // BITS: the width of every stage, or 0 for per-stage widths and scales.
 template <int BITS>
@@ -99,10 +118,7 @@ __global__ __launch_bounds__(256) void k_unpack_dequant(DequantArgs a) {
         if (q == c) wv[q] = wv[q] + v;
     }
   }
-  uint32_t o[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) o[j] = f64_to_f16_rne_fast(wv[2 * j]) | (f64_to_f16_rne_fast(wv[2 * j + 1]) << 16);
-  reinterpret_cast<uint4 *>(a.w_out + r * (int64_t)a.k)[g] = make_uint4(o[0], o[1], o[2], o[3]);
+  reinterpret_cast<uint4 *>(a.w_out + r * (int64_t)a.k)[g] = round_group_f16(wv);
 }
 
 constexpr int kDqThreads = 1024;
@@ -146,10 +162,7 @@ __device__ __forceinline__ void dequant_group(const DequantArgs &a, const uint4 
         if (q == c) wv[q] = wv[q] + sv;
     }
   }
-  uint32_t o[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) o[j] = f64_to_f16_rne_fast(wv[2 * j]) | (f64_to_f16_rne_fast(wv[2 * j + 1]) << 16);
-  reinterpret_cast<uint4 *>(a.w_out + r * (int64_t)a.k)[g] = make_uint4(o[0], o[1], o[2], o[3]);
+  reinterpret_cast<uint4 *>(a.w_out + r * (int64_t)a.k)[g] = round_group_f16(wv);
 }
 
 template <class LD, bool RS>

@@ -61,13 +61,11 @@ __device__ __forceinline__ uint32_t f64_to_f16_rne(double d) {
 }
 
 // The same rounding through the hardware conversions (a few instructions
-// instead of some forty): d is rounded to float with the low bit forced to
-// 1 when inexact (round to odd: the float has 24 significant bits, at least
-// two more than binary16's 11, so the float -> binary16 rounding to nearest
-// even then equals the direct one), and NaN, infinity and magnitudes from
-// 65504 up take the integer path.
-__device__ __forceinline__ uint32_t f64_to_f16_rne_fast(double d) {
-  if (!(__builtin_fabs(d) < 65504.0)) return f64_to_f16_rne(d);
+// instead of some forty), for finite |d| < 65504: d is rounded to float with
+// the low bit forced to 1 when inexact (round to odd: the float has 24
+// significant bits, at least two more than binary16's 11, so the float ->
+// binary16 rounding to nearest even then equals the direct one).
+__device__ __forceinline__ uint32_t f64_to_f16_rn_odd(double d) {
   const float f = (float)d;  // nearest, ties to even
   uint32_t fb = __float_as_uint(f);
   const double back = (double)f;
