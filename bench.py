@@ -268,9 +268,10 @@ def device_weight_(sw):
                     stage_bits=sw.stage_bits, stage_scales=sw.stage_scales, sparse=sw.sparse)
 
 
-def cpu_baseline():
-    """The float64 oracle on one full headline step (all three Llama-3-8B
-    linears, every row: unpack, exact dequant, matmul), single-threaded."""
+def cpu_baseline(min_seconds=10.0, max_steps=20):
+    """The float64 oracle on full headline steps (all three Llama-3-8B
+    linears, every row: unpack, exact dequant, matmul), single-threaded,
+    repeated with a fresh x each step until about min_seconds have passed."""
     import oracle
     import vqsynth
     try:
@@ -279,22 +280,26 @@ def cpu_baseline():
     except Exception:  # pragma: no cover
         lim = None
     ws, act_ss = vqsynth.workload_weights("llama8b")
-    kids = act_ss.spawn(2 * len(ws))
+    kids = act_ss.spawn(max_steps * len(ws))
     t0 = time.perf_counter()
     tot = 0
-    for i, sw in enumerate(ws):
-        _, x64 = vqsynth.make_x(1, sw.k_in, "bf16", kids[i])
-        idx = [oracle.unpack_indices(sw.idx_bits, sw.n_groups, lo=sw.lo[t], hi=sw.hi[t]) for t in range(sw.n_stages)]
-        w64 = oracle.dequant_exact(sw.n_out, sw.k_in, idx, sw.codebooks, sw.scales, sw.scale_block)
-        oracle.matmul_ref(w64, x64)
-        tot += compressed_bytes(sw)
-        del w64
+    steps = 0
+    while steps < max_steps and (steps == 0 or time.perf_counter() - t0 < min_seconds):
+        for i, sw in enumerate(ws):
+            _, x64 = vqsynth.make_x(1, sw.k_in, "bf16", kids[steps * len(ws) + i])
+            idx = [oracle.unpack_indices(sw.idx_bits, sw.n_groups, lo=sw.lo[t], hi=sw.hi[t])
+                   for t in range(sw.n_stages)]
+            w64 = oracle.dequant_exact(sw.n_out, sw.k_in, idx, sw.codebooks, sw.scales, sw.scale_block)
+            oracle.matmul_ref(w64, x64)
+            tot += compressed_bytes(sw)
+            del w64
+        steps += 1
     dt = time.perf_counter() - t0
     if lim is not None:
         lim.restore_original_limits()
     return {"value": tot / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "one full step: all three Llama-3-8B-shaped linears (every row), float64 unpack + "
-                      "exact dequant + matmul, numpy with BLAS limited to 1 thread",
+            "sample": f"{steps} full steps: all three Llama-3-8B-shaped linears (every row) with a fresh x each "
+                      "step, float64 unpack + exact dequant + matmul, numpy with BLAS limited to 1 thread",
             "seconds": dt, "host_cpus": os.cpu_count()}
 
 
