@@ -121,9 +121,11 @@ def upload_set(vq, sws, ncopies):
 # legs
 # ----------------------------------------------------------------------------
 
-def run_decode_leg(vq, workload, steps, warmup, batch=1, rht=False):
-    """GEMV (and optionally the input RHT) over all linears of a workload.
-    Returns a dict with per-step time, GB/s and per-kernel timings."""
+def run_decode_leg(vq, workload, steps, warmup, batch=1, rht=False, fused=False):
+    """GEMV (and optionally the input RHT: a separate rht_apply launch, or
+    with fused=True inside the decode kernel through vq_gemv_rht) over all
+    linears of a workload.  Returns a dict with per-step time, GB/s and
+    per-kernel timings."""
     import torch
     import vqsynth
     ws, act_ss = vqsynth.workload_weights(workload)
@@ -152,7 +154,9 @@ def run_decode_leg(vq, workload, steps, warmup, batch=1, rht=False):
         for j, w in enumerate(wset):
             if only is not None and j != only:
                 continue
-            if rht:
+            if rht and fused:
+                out.append(lambda j=j, w=w: vq.vq_gemv_rht(w, xs[j], signs[j], cfg["rht"], y=ys[j]))
+            elif rht:
                 out.append(lambda j=j: vq.rht_apply(xs[j], signs[j], cfg["rht"], out=xr[j]))
                 out.append(lambda j=j, w=w: vq.vq_gemv(w, xr[j], y=ys[j]))
             elif batch > 16:  # more tokens than vq_gemv takes: the same product through vq_gemm
@@ -183,7 +187,9 @@ def run_decode_leg(vq, workload, steps, warmup, batch=1, rht=False):
     per = []
     tot_bytes = 0
     for j, sw in enumerate(ws):
-        if rht:
+        if rht and fused:
+            g_ms = graph_time_ms([f for i in range(steps) for f in launches_of(i, only=j)]) / steps
+        elif rht:
             r_ms = graph_time_ms([lambda j=j: vq.rht_apply(xs[j], signs[j], cfg["rht"], out=xr[j])
                                   for _ in range(steps)]) / steps
             g_ms = graph_time_ms([lambda i=i, j=j: vq.vq_gemv(sets[i % ncopies][j], xr[j], y=ys[j])
@@ -191,13 +197,13 @@ def run_decode_leg(vq, workload, steps, warmup, batch=1, rht=False):
         else:
             g_ms = graph_time_ms([f for i in range(steps) for f in launches_of(i, only=j)]) / steps
         comp = compressed_bytes(sw)
-        xb = batch * sw.k_in * (4 if rht else x_bytes)
+        xb = batch * sw.k_in * (4 if rht and not fused else x_bytes) + (sw.k_in if fused else 0)  # (+ signs)
         yb = batch * sw.n_out * 4
         alg = comp + xb + yb
         tot_bytes += comp
         ent = {"shape": [sw.n_out, sw.k_in], "compressed_bytes": comp, "algorithmic_bytes": alg,
                "kernel_us_mean": g_ms * 1e3, "gbs_algorithmic": alg / (g_ms * 1e-3) / 1e9}
-        if rht:
+        if rht and not fused:
             ent["rht_us_mean"] = r_ms * 1e3
         per.append(ent)
     return {"ms_per_step": ms_step, "ms_per_step_eager": ms_eager, "compressed_bytes_per_step": tot_bytes,
@@ -436,6 +442,11 @@ def main():
                                                                    only=["qo", "gate_up"])),
                 ("mlp70b_e8p3_rht_gemv_b1", lambda: run_decode_leg(vq, "mlp70b_e8p3", max(5, args.steps // 5), 3,
                                                                    rht=True)),
+                # the same two workloads with the input transform inside the decode kernel (vq_gemv_rht)
+                ("mlp70b_rht_fused_gemv_b1", lambda: run_decode_leg(vq, "mlp70b", max(5, args.steps // 5), 3,
+                                                                    rht=True, fused=True)),
+                ("mlp70b_e8p3_rht_fused_gemv_b1", lambda: run_decode_leg(vq, "mlp70b_e8p3", max(5, args.steps // 5),
+                                                                         3, rht=True, fused=True)),
                 # sparse correction (0.5 % of the weights) on the headline format
                 ("llama8b_sparse_gemv_b1", lambda: run_decode_leg(vq, "llama8b_sparse", args.steps, args.warmup)),
                 ("llama8b_sparse_gemv_b16", lambda: run_decode_leg(vq, "llama8b_sparse", args.steps, args.warmup,

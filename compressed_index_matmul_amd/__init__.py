@@ -24,14 +24,15 @@ import numpy as np
 
 __all__ = [
     "VQError", "VQWeight", "lib", "LIB_PATH", "vq_version", "vq_validate", "vq_compressed_bytes",
-    "vq_unpack_dequant", "vq_gemv", "vq_gemm", "rht_apply", "VQ_F32", "VQ_BF16", "VQ_STAGE_SCALES", "EXPORTS",
+    "vq_unpack_dequant", "vq_gemv", "vq_gemm", "rht_apply", "vq_gemv_rht", "VQ_F32", "VQ_BF16", "VQ_STAGE_SCALES",
+    "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvqmm.so")
 VQ_F32, VQ_BF16 = 0, 1
 MAX_STAGES = 4
 EXPORTS = ("vq_version", "vq_status_string", "vq_validate", "vq_compressed_bytes",
-           "vq_unpack_dequant", "vq_gemv", "vq_gemm", "rht_apply")
+           "vq_unpack_dequant", "vq_gemv", "vq_gemm", "rht_apply", "vq_gemv_rht")
 
 _ptr4 = ctypes.c_void_p * MAX_STAGES
 _int4 = ctypes.c_int32 * MAX_STAGES
@@ -92,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.vq_gemm.argtypes, L.vq_gemm.restype = [D, P, ctypes.c_int32, P, P], ctypes.c_int
         L.rht_apply.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P, P]
         L.rht_apply.restype = ctypes.c_int
+        L.vq_gemv_rht.argtypes = [D, P, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P, P]
+        L.vq_gemv_rht.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -280,3 +283,20 @@ def rht_apply(x, signs, max_block: int, out=None, stream=None):
     _check(lib().rht_apply(x.data_ptr(), _xtype(x), b, n, signs.data_ptr(), max_block, out.data_ptr(),
                            _stream_handle(stream)), "rht_apply")
     return out
+
+
+def vq_gemv_rht(w: VQWeight, x, signs, max_block: int, y=None, stream=None):
+    """y = dequant(W) . RHT(x) with the transform inside the decode kernel:
+    x [B, K] (B <= 16) float32/bfloat16, signs int8 [K] on the device -> y
+    float32 [B, N].  Raises VQError (VQ_ERR_UNSUPPORTED) for weights the
+    16-bit decode kernel does not take."""
+    import torch
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    x = x.contiguous()
+    b = x.shape[0]
+    if y is None:
+        y = torch.empty((b, w.n_out), dtype=torch.float32, device=x.device)
+    _check(lib().vq_gemv_rht(w.ref(), x.data_ptr(), _xtype(x), b, signs.data_ptr(), max_block, y.data_ptr(),
+                             _stream_handle(stream)), "vq_gemv_rht")
+    return y

@@ -727,6 +727,11 @@ bool launch_gemv_tokens_sparse(const WView &w, const GemvArgs &a, int batch, int
 // One stage of 16-bit indices (k_gemv_l2.hip): L2 gathers with the next
 // row's indices loading and 16 gathers per lane in flight; false when the
 // shape is not taken.
-bool launch_gemv_l2(const WView &w, const GemvArgs &a, int xt, int cus, hipStream_t s);
+// The 16-bit decode kernel (k_gemv_l2.hip): whether it takes the weight, and
+// its launch (false: nothing launched); signs (null: none) and max_block
+// give the input transform it applies to x first.
+bool gemv_l2_takes(const WView &w);
+bool launch_gemv_l2(const WView &w, const GemvArgs &a, int xt, int cus, hipStream_t s, const int8_t *signs = nullptr,
+                    int max_block = 0);
 
 }  // namespace vqmm

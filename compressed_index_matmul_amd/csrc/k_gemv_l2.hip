@@ -21,6 +21,17 @@
 // 3 and 4 bpw ladders; "Inference kernels": the inverse residual scale);
 // K % 2048 == 0 (K / 2048 units per lane) up to K = 32768 (x in LDS), scale
 // blocks of whole 32-column units.
+//
+// With signs given, the kernel first applies the randomized Hadamard
+// transform of the input to its LDS copy of x (GLQ page, "How it works":
+// random sign flips, then a fast Walsh-Hadamard transform; "Bit widths":
+// block-diagonal over the greedy power-of-two blocks of at most max_block),
+// the same transform rht_apply computes: the signs multiply x as it is
+// staged, then passes of up to four butterfly stages each run in registers
+// over groups of 16 elements (one barrier per pass, every block of the row
+// in the same pass), and each block's last pass scales it by 1/sqrt(len).
+// Every workgroup transforms its own copy, so no second launch and no
+// buffer for the transformed x are needed.
 #include "gemv_kernels.h"
 
 namespace vqmm {
@@ -34,9 +45,100 @@ template <int B1> constexpr int l2_batch() { return B1 == 16 ? 2 : 4; }
 // most units per lane that fit the register file without spills
 template <int B1> constexpr int l2_max_upl() { return B1 == 0 ? 16 : B1 == 8 ? 14 : 13; }
 
+// The input transform: signs (null: none) and the largest block.
+struct RhtIn {
+  const int8_t *signs;
+  int mb;
+};
+
+// One group of a FWHT pass: the R elements base + j 2^s (j < R) of s_x,
+// R = 2^r butterfly stages in registers; the result times sc.  With s == 0
+// the elements are contiguous and move as 16-byte LDS accesses.
+template <int R>
+__device__ __forceinline__ void fwht_group(float *s_x, int base, int s, float sc) {
+  float v[R];
+  if (R >= 4 && s == 0) {
+#pragma unroll
+    for (int q = 0; q < R / 4; ++q) {
+      const float4 t = *reinterpret_cast<const float4 *>(&s_x[base + 4 * q]);
+      v[4 * q] = t.x, v[4 * q + 1] = t.y, v[4 * q + 2] = t.z, v[4 * q + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < R; ++j) v[j] = s_x[base + (j << s)];
+  }
+#pragma unroll
+  for (int h = 1; h < R; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if ((j & h) == 0) {
+        const float p0 = v[j], p1 = v[j + h];
+        v[j] = p0 + p1;
+        v[j + h] = p0 - p1;
+      }
+#pragma unroll
+  for (int j = 0; j < R; ++j) v[j] *= sc;
+  if (R >= 4 && s == 0) {
+#pragma unroll
+    for (int q = 0; q < R / 4; ++q)
+      *reinterpret_cast<float4 *>(&s_x[base + 4 * q]) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < R; ++j) s_x[base + (j << s)] = v[j];
+  }
+}
+
+// Pass s over `count` blocks of 2^lb elements from offset off (bits [s, s +
+// r) of the in-block index, r = min(4, lb - s)): the groups of all these
+// blocks spread over the NT threads; a block whose last bits these are is
+// scaled by 1/sqrt(2^lb).
+template <int NT>
+__device__ __forceinline__ void fwht_pass(float *s_x, int off, int count, int lb, int s, int tid) {
+  if (s >= lb || count <= 0) return;
+  const int r = lb - s < 4 ? lb - s : 4;
+  const bool last = s + r >= lb;
+  const float sc = last ? (float)(1.0 / __builtin_sqrt((double)(1 << lb))) : 1.f;
+  const int gpb_log = lb - r;  // log2 groups per block
+  const int groups = count << gpb_log;
+  for (int gid = tid; gid < groups; gid += NT) {
+    const int blk = gid >> gpb_log;
+    const int gi = gid & ((1 << gpb_log) - 1);
+    const int base = off + (blk << lb) + ((gi >> s) << (s + r)) + (gi & ((1 << s) - 1));
+    switch (r) {
+      case 4: fwht_group<16>(s_x, base, s, sc); break;
+      case 3: fwht_group<8>(s_x, base, s, sc); break;
+      case 2: fwht_group<4>(s_x, base, s, sc); break;
+      default: fwht_group<2>(s_x, base, s, sc); break;
+    }
+  }
+}
+
+// In-place orthonormal FWHT of every block of s_x[0, K): K / mb blocks of
+// mb, then one block per set bit of K % mb, largest first.  Passes of up to
+// four stages, one barrier each; the blocks of mb are one flat loop over
+// their groups, the few remainder blocks one loop each.
+// s0: the first in-block bit left to transform (4 when the staging has done
+// bits 0..3).
+template <int NT>
+__device__ __forceinline__ void fwht_lds(float *s_x, int K, int mb, int tid, int s0) {
+  const int nfull = K / mb, rest = K % mb;
+  int maxbits = 0;
+  for (int p = mb; p > 1; p >>= 1) ++maxbits;
+  for (int s = s0; s < maxbits; s += 4) {
+    __syncthreads();  // the previous pass (or the staging) is complete
+    fwht_pass<NT>(s_x, 0, nfull, maxbits, s, tid);
+    int off = nfull * mb;
+    for (int bit = maxbits - 1; bit >= 0; --bit)  // uniform
+      if (rest & (1 << bit)) {
+        fwht_pass<NT>(s_x, off, 1, bit, s, tid);
+        off += 1 << bit;
+      }
+  }
+}
+
 // B1: width of the residual stage (0: none, 8 or 16); RS: stage scales.
 template <int UPL, int B1, bool RS>
-__global__ __launch_bounds__(kL2Waves * 64) void k_gemv_l2(GemvArgs a, int xt) {
+__global__ __launch_bounds__(kL2Waves * 64) void k_gemv_l2(GemvArgs a, int xt, RhtIn rht) {
   constexpr int NT = kL2Waves * 64;
   __shared__ float s_x[kL2MaxK];
   __shared__ uint4 s_cb1[B1 == 8 ? 256 : 1];
@@ -45,8 +147,54 @@ __global__ __launch_bounds__(kL2Waves * 64) void k_gemv_l2(GemvArgs a, int xt) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int K = a.k;
 
-  // x -> LDS as fp32, four values per thread and step
-  for (int i = 4 * tid; i < K; i += 4 * NT) {
+  // x -> LDS as fp32 (times the signs of the input transform), four values
+  // per thread and step.  With the transform and blocks of at least 32
+  // elements (K % 2048 == 0, so every block then is), a thread stages 16
+  // consecutive elements and runs the transform's first four butterfly
+  // stages on them in registers.
+  const bool has_rht = rht.signs != nullptr;  // uniform
+  const bool rht16 = has_rht && rht.mb >= 32;
+  if (rht16) {
+    for (int g = tid; g < K / 16; g += NT) {
+      const int i = 16 * g;
+      float v[16];
+      if (xt == VQ_F32) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 t = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.x) + i + 4 * q);
+          v[4 * q] = t.x, v[4 * q + 1] = t.y, v[4 * q + 2] = t.z, v[4 * q + 3] = t.w;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const uint4 u = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.x) + i + 8 * q);
+          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[8 * q + 2 * e] = bf2f(w4[e] & 0xffffu);
+            v[8 * q + 2 * e + 1] = bf2f(w4[e] >> 16);
+          }
+        }
+      }
+      const uint4 sg = *reinterpret_cast<const uint4 *>(rht.signs + i);
+      const uint32_t s4[4] = {sg.x, sg.y, sg.z, sg.w};
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] *= (float)(int8_t)((s4[j >> 2] >> (8 * (j & 3))) & 0xffu);
+#pragma unroll
+      for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if ((j & h) == 0) {
+            const float p0 = v[j], p1 = v[j + h];
+            v[j] = p0 + p1;
+            v[j + h] = p0 - p1;
+          }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4 *>(&s_x[i + 4 * q]) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    }
+  }
+  for (int i = 4 * tid; i < (rht16 ? 0 : K); i += 4 * NT) {
     float4 v;
     if (xt == VQ_F32) {
       v = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.x) + i);
@@ -54,10 +202,18 @@ __global__ __launch_bounds__(kL2Waves * 64) void k_gemv_l2(GemvArgs a, int xt) {
       const uint2 u = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(a.x) + i);
       v = make_float4(bf2f(u.x & 0xffffu), bf2f(u.x >> 16), bf2f(u.y & 0xffffu), bf2f(u.y >> 16));
     }
+    if (has_rht) {
+      const uint32_t sg = *reinterpret_cast<const uint32_t *>(rht.signs + i);
+      v.x *= (float)(int8_t)(sg & 0xffu);
+      v.y *= (float)(int8_t)((sg >> 8) & 0xffu);
+      v.z *= (float)(int8_t)((sg >> 16) & 0xffu);
+      v.w *= (float)(int8_t)(sg >> 24);
+    }
     *reinterpret_cast<float4 *>(&s_x[i]) = v;
   }
   if (B1 == 8 && tid < 256) s_cb1[tid] = reinterpret_cast<const uint4 *>(a.cb[1])[tid];
-  __syncthreads();  // the only barrier: waves without rows may leave after it
+  if (has_rht) fwht_lds<NT>(s_x, K, rht.mb, tid, rht16 ? 4 : 0);
+  __syncthreads();  // the last barrier: waves without rows may leave after it
 
   const int per_wg = (a.n + gridDim.x - 1) / gridDim.x;
   const int blk_lo = blockIdx.x * per_wg;
@@ -171,54 +327,63 @@ __global__ __launch_bounds__(kL2Waves * 64) void k_gemv_l2(GemvArgs a, int xt) {
 }
 
 template <int UPL, int B1, bool RS>
-bool launch_u(const GemvArgs &a, int xt, int cus, hipStream_t s) {
+bool launch_u(const GemvArgs &a, int xt, RhtIn rht, int cus, hipStream_t s) {
   if constexpr (UPL > l2_max_upl<B1>()) {
     return false;
   } else {
     int g = (a.n + kL2Waves - 1) / kL2Waves;
     if (g > cus) g = cus;
-    hipLaunchKernelGGL((k_gemv_l2<UPL, B1, RS>), dim3(g), dim3(kL2Waves * 64), 0, s, a, xt);
+    hipLaunchKernelGGL((k_gemv_l2<UPL, B1, RS>), dim3(g), dim3(kL2Waves * 64), 0, s, a, xt, rht);
     return true;
   }
 }
 
 template <int B1, bool RS>
-bool launch_f(const GemvArgs &a, int xt, int cus, hipStream_t s) {
+bool launch_f(const GemvArgs &a, int xt, RhtIn rht, int cus, hipStream_t s) {
   switch (a.k / 2048) {
-    case 1: return launch_u<1, B1, RS>(a, xt, cus, s);
-    case 2: return launch_u<2, B1, RS>(a, xt, cus, s);
-    case 3: return launch_u<3, B1, RS>(a, xt, cus, s);
-    case 4: return launch_u<4, B1, RS>(a, xt, cus, s);
-    case 5: return launch_u<5, B1, RS>(a, xt, cus, s);
-    case 6: return launch_u<6, B1, RS>(a, xt, cus, s);
-    case 7: return launch_u<7, B1, RS>(a, xt, cus, s);
-    case 8: return launch_u<8, B1, RS>(a, xt, cus, s);
-    case 9: return launch_u<9, B1, RS>(a, xt, cus, s);
-    case 10: return launch_u<10, B1, RS>(a, xt, cus, s);
-    case 11: return launch_u<11, B1, RS>(a, xt, cus, s);
-    case 12: return launch_u<12, B1, RS>(a, xt, cus, s);
-    case 13: return launch_u<13, B1, RS>(a, xt, cus, s);
-    case 14: return launch_u<14, B1, RS>(a, xt, cus, s);
-    case 15: return launch_u<15, B1, RS>(a, xt, cus, s);
-    case 16: return launch_u<16, B1, RS>(a, xt, cus, s);
+    case 1: return launch_u<1, B1, RS>(a, xt, rht, cus, s);
+    case 2: return launch_u<2, B1, RS>(a, xt, rht, cus, s);
+    case 3: return launch_u<3, B1, RS>(a, xt, rht, cus, s);
+    case 4: return launch_u<4, B1, RS>(a, xt, rht, cus, s);
+    case 5: return launch_u<5, B1, RS>(a, xt, rht, cus, s);
+    case 6: return launch_u<6, B1, RS>(a, xt, rht, cus, s);
+    case 7: return launch_u<7, B1, RS>(a, xt, rht, cus, s);
+    case 8: return launch_u<8, B1, RS>(a, xt, rht, cus, s);
+    case 9: return launch_u<9, B1, RS>(a, xt, rht, cus, s);
+    case 10: return launch_u<10, B1, RS>(a, xt, rht, cus, s);
+    case 11: return launch_u<11, B1, RS>(a, xt, rht, cus, s);
+    case 12: return launch_u<12, B1, RS>(a, xt, rht, cus, s);
+    case 13: return launch_u<13, B1, RS>(a, xt, rht, cus, s);
+    case 14: return launch_u<14, B1, RS>(a, xt, rht, cus, s);
+    case 15: return launch_u<15, B1, RS>(a, xt, rht, cus, s);
+    case 16: return launch_u<16, B1, RS>(a, xt, rht, cus, s);
     default: return false;
   }
 }
 
 }  // namespace
 
-bool launch_gemv_l2(const WView &w, const GemvArgs &a, int xt, int cus, hipStream_t s) {
+bool gemv_l2_takes(const WView &w) {
   if (w.S < 1 || w.S > 2 || w.sb[0] != 16) return false;
-  if (w.k % 2048 != 0 || w.k > kL2MaxK || w.k / 2048 > 16) return false;
+  if (w.k % 2048 != 0 || w.k > kL2MaxK) return false;
   if (w.bs % 32 != 0 || (2048 % w.bs != 0 && w.bs < w.k)) return false;
   const int b1 = w.S == 2 ? w.sb[1] : 0;
   if (b1 != 0 && b1 != 8 && b1 != 16) return false;
+  const int upl = w.k / 2048;
+  return upl <= (b1 == 0 ? l2_max_upl<0>() : b1 == 8 ? l2_max_upl<8>() : l2_max_upl<16>());
+}
+
+bool launch_gemv_l2(const WView &w, const GemvArgs &a, int xt, int cus, hipStream_t s, const int8_t *signs,
+                    int max_block) {
+  if (!gemv_l2_takes(w)) return false;
+  const RhtIn rht{signs, max_block};
+  const int b1 = w.S == 2 ? w.sb[1] : 0;
   if (!w.scaled) {
-    if (b1 == 0) return launch_f<0, false>(a, xt, cus, s);
-    return b1 == 8 ? launch_f<8, false>(a, xt, cus, s) : launch_f<16, false>(a, xt, cus, s);
+    if (b1 == 0) return launch_f<0, false>(a, xt, rht, cus, s);
+    return b1 == 8 ? launch_f<8, false>(a, xt, rht, cus, s) : launch_f<16, false>(a, xt, rht, cus, s);
   }
-  if (b1 == 0) return launch_f<0, true>(a, xt, cus, s);
-  return b1 == 8 ? launch_f<8, true>(a, xt, cus, s) : launch_f<16, true>(a, xt, cus, s);
+  if (b1 == 0) return launch_f<0, true>(a, xt, rht, cus, s);
+  return b1 == 8 ? launch_f<8, true>(a, xt, rht, cus, s) : launch_f<16, true>(a, xt, rht, cus, s);
 }
 
 }  // namespace vqmm

@@ -191,6 +191,27 @@ int vq_gemm(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float *y, voi
   return map_hip(launch_sparse_add(v, x_bf16, VQ_BF16, m, y, s));
 }
 
+int vq_gemv_rht(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, const int8_t *signs,
+                int32_t max_block, float *y, void *stream) {
+  WView v;
+  int st = check_weight(w, &v);
+  if (st != VQ_OK) return st;
+  if (!x || !signs || !y) return VQ_ERR_NULL;
+  if (x_dtype != VQ_F32 && x_dtype != VQ_BF16) return VQ_ERR_DTYPE;
+  if (batch < 1 || batch > 16) return VQ_ERR_UNSUPPORTED;
+  if (max_block < 1 || max_block > 16384 || (max_block & (max_block - 1)) != 0) return VQ_ERR_SHAPE;
+  if (!gemv_rht_takes(v)) return VQ_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(signs) || !aligned16(y)) return VQ_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t esz = x_dtype == VQ_F32 ? 4 : 2;
+  for (int b = 0; b < batch; ++b) {
+    const void *xb = reinterpret_cast<const char *>(x) + (size_t)b * v.k * esz;
+    st = map_hip(launch_gemv_rht_token(v, xb, x_dtype, signs, max_block, y + (size_t)b * v.n, s));
+    if (st != VQ_OK) return st;
+  }
+  return VQ_OK;
+}
+
 int rht_apply(const void *x, int32_t x_dtype, int32_t batch, int32_t n, const int8_t *signs,
               int32_t max_block, float *out, void *stream) {
   if (!x || !signs || !out) return VQ_ERR_NULL;

@@ -47,6 +47,12 @@ hipError_t launch_rht(const void *x, int xt, int batch, int n, const int8_t *sig
 // One token of x (fp32 or bf16, VQ_F32 / VQ_BF16) against W: y[n].
 // *sp_done: the launched kernel also added the sparse correction.
 hipError_t launch_gemv_token(const WView &w, const void *x, int xt, float *y, hipStream_t s, bool *sp_done);
+// The product with the input transform applied inside the decode kernel:
+// whether the weight has such a kernel (16-bit first stage the L2 decode
+// kernel takes, no sparse correction), and one token's launch.
+bool gemv_rht_takes(const WView &w);
+hipError_t launch_gemv_rht_token(const WView &w, const void *x, int xt, const int8_t *signs, int max_block, float *y,
+                                 hipStream_t s);
 // 2..4 bf16 tokens in one launch of the LDS decode kernel when the shape
 // allows it (false: not taken, nothing launched; *err set when taken).  The
 // kernel also adds the sparse correction.

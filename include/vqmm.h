@@ -214,6 +214,30 @@ int vq_gemm(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float *y, voi
 int rht_apply(const void *x, int32_t x_dtype, int32_t batch, int32_t n, const int8_t *signs,
               int32_t max_block, float *out, void *stream);
 
+/*
+ * The decode-style product with the input transform applied inside the
+ * decode kernel (GLQ page, "Advanced", "Trellis codebook": its decode
+ * kernels run the input Hadamard transform in every decode block instead of
+ * as a separate launch):
+ *   y[b] = dequant(W) . RHT(x[b]),  RHT as rht_apply with signs, max_block,
+ * for 1..16 tokens, with no buffer for the transformed x: every workgroup
+ * transforms its own copy in LDS.  Taken for the weights the 16-bit decode
+ * kernel serves: a 16-bit first stage, at most one 8- or 16-bit residual
+ * stage, stage scales allowed, K % 2048 == 0 with K <= 32768 (26624 with a
+ * 16-bit and 28672 with an 8-bit residual), scale blocks of 32-column units
+ * that divide 2048 or cover the row, and no sparse correction; any other
+ * weight returns VQ_ERR_UNSUPPORTED with nothing launched (use rht_apply,
+ * then vq_gemv).
+ *   x         : [batch][k_in], VQ_F32 or VQ_BF16, 16-byte aligned
+ *   signs     : int8 [k_in], each +1 or -1, 16-byte aligned
+ *   max_block : power of two, 1..16384 (VQ_ERR_SHAPE otherwise)
+ *   y         : float [batch][n_out], 16-byte aligned
+ * Same bound as vq_gemv on the transformed x; the transform itself is the
+ * fp32 butterfly sequence of rht_apply up to the order of its stages.
+ */
+int vq_gemv_rht(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, const int8_t *signs,
+                int32_t max_block, float *y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

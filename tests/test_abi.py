@@ -153,6 +153,29 @@ def test_gemm_argument_checks(L):
     assert L.vq_gemm(d, FAKE + 2, 4, FAKE, None) == VQ_ERR_ALIGN
 
 
+def test_gemv_rht_argument_checks(L):
+    """The fused input transform: argument errors, and VQ_ERR_UNSUPPORTED
+    (nothing launched) for weights the 16-bit decode kernel does not take."""
+    d16 = ctypes.byref(fake_desc(n=64, k=4096, bits=16, bs=128))
+    assert L.vq_gemv_rht(d16, None, 1, 1, FAKE, 64, FAKE, None) == VQ_ERR_NULL
+    assert L.vq_gemv_rht(d16, FAKE, 1, 1, None, 64, FAKE, None) == VQ_ERR_NULL
+    assert L.vq_gemv_rht(d16, FAKE, 1, 1, FAKE, 64, None, None) == VQ_ERR_NULL
+    assert L.vq_gemv_rht(d16, FAKE, 7, 1, FAKE, 64, FAKE, None) == VQ_ERR_DTYPE
+    assert L.vq_gemv_rht(d16, FAKE, 1, 0, FAKE, 64, FAKE, None) == VQ_ERR_UNSUPPORTED
+    assert L.vq_gemv_rht(d16, FAKE, 1, 17, FAKE, 64, FAKE, None) == VQ_ERR_UNSUPPORTED
+    for mb in (0, 48, 32768):
+        assert L.vq_gemv_rht(d16, FAKE, 1, 1, FAKE, mb, FAKE, None) == VQ_ERR_SHAPE
+    assert L.vq_gemv_rht(d16, FAKE, 1, 1, FAKE + 4, 64, FAKE, None) == VQ_ERR_ALIGN
+    assert L.vq_gemv_rht(d16, FAKE + 2, 1, 1, FAKE, 64, FAKE, None) == VQ_ERR_ALIGN
+    for desc in (fake_desc(n=64, k=4096, bits=12, bs=128),            # 12-bit indices
+                 fake_desc(n=64, k=4000, bits=16, bs=32),             # K % 2048
+                 fake_desc(n=64, k=34816, bits=16, bs=128),           # K past 32768
+                 fake_desc(n=64, k=28672, stages=2, bits=16, bs=128),  # 16 + 16 past 26624
+                 fake_desc(n=64, k=4096, bits=16, bs=96),             # scale block not dividing 2048
+                 fake_desc(n=64, k=4096, stages=3, bits=16, bs=128)):  # three stages
+        assert L.vq_gemv_rht(ctypes.byref(desc), FAKE, 1, 1, FAKE, 64, FAKE, None) == VQ_ERR_UNSUPPORTED
+
+
 def test_unpack_argument_checks(L):
     d = ctypes.byref(fake_desc())
     assert L.vq_unpack_dequant(d, None, None, None) == VQ_ERR_NULL

@@ -2,7 +2,8 @@
 write exactly what the eager call writes (the kernels are deterministic, so
 bit for bit).  The output is poisoned with NaN before each replay, and eager
 work (another call, torch ops, a synchronisation) runs between replays.  The
-shapes route to the main kernels: the LDS and L2 decode GEMVs, the fused and
+shapes route to the main kernels: the LDS and L2 decode GEMVs (the latter
+also with the input transform inside), the fused and
 the multi-token sparse correction, the few-token, wide and tile GEMMs, the RHT
 and the LDS dequant."""
 import numpy as np
@@ -86,6 +87,19 @@ def test_graph_replay_rht(vq):
     signs = torch.from_numpy(vqsynth.make_signs(8192 + 2048, np.random.SeedSequence(6))).cuda()
     out = torch.empty((2, 8192 + 2048), dtype=torch.float32, device="cuda")
     replay_matches(lambda: vq.rht_apply(x, signs, 8192, out=out), out, lambda: torch.ones(10, device="cuda").cumsum(0))
+
+
+def test_graph_replay_gemv_rht(vq):
+    import torch
+    sw = vqsynth.random_weight(2048, 8192, 2, [16, 8], None, seed=8, cb_sd=(0.02, 0.02), stage_scale_range=(0.2, 0.4))
+    w = device_weight(sw)
+    x = _x(1, 8192, "bf16", 9)
+    signs = torch.from_numpy(vqsynth.make_signs(8192, np.random.SeedSequence(10))).cuda()
+    y = torch.empty((1, 2048), dtype=torch.float32, device="cuda")
+    x2 = _x(1, 8192, "bf16", 11)
+    y2 = torch.empty_like(y)
+    replay_matches(lambda: vq.vq_gemv_rht(w, x, signs, 8192, y=y), y,
+                   lambda: vq.vq_gemv_rht(w, x2, signs, 8192, y=y2))
 
 
 def test_graph_replay_dequant(vq):
