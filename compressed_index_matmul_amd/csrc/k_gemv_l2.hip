@@ -89,13 +89,16 @@ __device__ __forceinline__ void fwht_group(float *s_x, int base, int s, float sc
 }
 
 // Pass s over `count` blocks of 2^lb elements from offset off (bits [s, s +
-// r) of the in-block index, r = min(4, lb - s)): the groups of all these
+// r) of the in-block index: r = 4, or all that is left when that is at most
+// 5, so no pass of a single stage remains): the groups of all these
 // blocks spread over the NT threads; a block whose last bits these are is
 // scaled by 1/sqrt(2^lb).
 template <int NT>
-__device__ __forceinline__ void fwht_pass(float *s_x, int off, int count, int lb, int s, int tid) {
-  if (s >= lb || count <= 0) return;
-  const int r = lb - s < 4 ? lb - s : 4;
+__device__ __forceinline__ void fwht_pass(float *s_x, int off, int count, int lb, int s, int s0, int tid) {
+  // passes start at s0, s0 + 4, ...; a block is done once a pass took its
+  // last bits (at most 5 of them), so later passes skip it
+  if (s >= lb || count <= 0 || (s > s0 && lb - (s - 4) <= 5)) return;
+  const int r = lb - s <= 5 ? lb - s : 4;
   const bool last = s + r >= lb;
   const float sc = last ? (float)(1.0 / __builtin_sqrt((double)(1 << lb))) : 1.f;
   const int gpb_log = lb - r;  // log2 groups per block
@@ -105,6 +108,7 @@ __device__ __forceinline__ void fwht_pass(float *s_x, int off, int count, int lb
     const int gi = gid & ((1 << gpb_log) - 1);
     const int base = off + (blk << lb) + ((gi >> s) << (s + r)) + (gi & ((1 << s) - 1));
     switch (r) {
+      case 5: fwht_group<32>(s_x, base, s, sc); break;
       case 4: fwht_group<16>(s_x, base, s, sc); break;
       case 3: fwht_group<8>(s_x, base, s, sc); break;
       case 2: fwht_group<4>(s_x, base, s, sc); break;
@@ -124,13 +128,15 @@ __device__ __forceinline__ void fwht_lds(float *s_x, int K, int mb, int tid, int
   const int nfull = K / mb, rest = K % mb;
   int maxbits = 0;
   for (int p = mb; p > 1; p >>= 1) ++maxbits;
-  for (int s = s0; s < maxbits; s += 4) {
+  // passes at s0, s0 + 4, ...: a block's last pass takes its remaining 1..5
+  // bits (the loop stops at maxbits - 1 so a 5-bit remainder is one pass)
+  for (int s = s0; s < maxbits; s += (maxbits - s <= 5 ? 5 : 4)) {
     __syncthreads();  // the previous pass (or the staging) is complete
-    fwht_pass<NT>(s_x, 0, nfull, maxbits, s, tid);
+    fwht_pass<NT>(s_x, 0, nfull, maxbits, s, s0, tid);
     int off = nfull * mb;
     for (int bit = maxbits - 1; bit >= 0; --bit)  // uniform
       if (rest & (1 << bit)) {
-        fwht_pass<NT>(s_x, off, 1, bit, s, tid);
+        fwht_pass<NT>(s_x, off, 1, bit, s, s0, tid);
         off += 1 << bit;
       }
   }
