@@ -51,72 +51,6 @@ struct RhtIn {
   int mb;
 };
 
-// One group of a FWHT pass: the R elements base + j 2^s (j < R) of s_x,
-// R = 2^r butterfly stages in registers; the result times sc.  With s == 0
-// the elements are contiguous and move as 16-byte LDS accesses.
-template <int R>
-__device__ __forceinline__ void fwht_group(float *s_x, int base, int s, float sc) {
-  float v[R];
-  if (R >= 4 && s == 0) {
-#pragma unroll
-    for (int q = 0; q < R / 4; ++q) {
-      const float4 t = *reinterpret_cast<const float4 *>(&s_x[base + 4 * q]);
-      v[4 * q] = t.x, v[4 * q + 1] = t.y, v[4 * q + 2] = t.z, v[4 * q + 3] = t.w;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < R; ++j) v[j] = s_x[base + (j << s)];
-  }
-#pragma unroll
-  for (int h = 1; h < R; h <<= 1)
-#pragma unroll
-    for (int j = 0; j < R; ++j)
-      if ((j & h) == 0) {
-        const float p0 = v[j], p1 = v[j + h];
-        v[j] = p0 + p1;
-        v[j + h] = p0 - p1;
-      }
-#pragma unroll
-  for (int j = 0; j < R; ++j) v[j] *= sc;
-  if (R >= 4 && s == 0) {
-#pragma unroll
-    for (int q = 0; q < R / 4; ++q)
-      *reinterpret_cast<float4 *>(&s_x[base + 4 * q]) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-  } else {
-#pragma unroll
-    for (int j = 0; j < R; ++j) s_x[base + (j << s)] = v[j];
-  }
-}
-
-// Pass s over `count` blocks of 2^lb elements from offset off (bits [s, s +
-// r) of the in-block index: r = 4, or all that is left when that is at most
-// 5, so no pass of a single stage remains): the groups of all these
-// blocks spread over the NT threads; a block whose last bits these are is
-// scaled by 1/sqrt(2^lb).
-template <int NT>
-__device__ __forceinline__ void fwht_pass(float *s_x, int off, int count, int lb, int s, int s0, int tid) {
-  // passes start at s0, s0 + 4, ...; a block is done once a pass took its
-  // last bits (at most 5 of them), so later passes skip it
-  if (s >= lb || count <= 0 || (s > s0 && lb - (s - 4) <= 5)) return;
-  const int r = lb - s <= 5 ? lb - s : 4;
-  const bool last = s + r >= lb;
-  const float sc = last ? (float)(1.0 / __builtin_sqrt((double)(1 << lb))) : 1.f;
-  const int gpb_log = lb - r;  // log2 groups per block
-  const int groups = count << gpb_log;
-  for (int gid = tid; gid < groups; gid += NT) {
-    const int blk = gid >> gpb_log;
-    const int gi = gid & ((1 << gpb_log) - 1);
-    const int base = off + (blk << lb) + ((gi >> s) << (s + r)) + (gi & ((1 << s) - 1));
-    switch (r) {
-      case 5: fwht_group<32>(s_x, base, s, sc); break;
-      case 4: fwht_group<16>(s_x, base, s, sc); break;
-      case 3: fwht_group<8>(s_x, base, s, sc); break;
-      case 2: fwht_group<4>(s_x, base, s, sc); break;
-      default: fwht_group<2>(s_x, base, s, sc); break;
-    }
-  }
-}
-
 // In-place orthonormal FWHT of every block of s_x[0, K): K / mb blocks of
 // mb, then one block per set bit of K % mb, largest first.  Passes of up to
 // four stages, one barrier each; the blocks of mb are one flat loop over
@@ -162,42 +96,11 @@ __global__ __launch_bounds__(kL2Waves * 64) void k_gemv_l2(GemvArgs a, int xt, R
   const bool rht16 = has_rht && rht.mb >= 32;
   if (rht16) {
     for (int g = tid; g < K / 16; g += NT) {
-      const int i = 16 * g;
       float v[16];
-      if (xt == VQ_F32) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 t = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.x) + i + 4 * q);
-          v[4 * q] = t.x, v[4 * q + 1] = t.y, v[4 * q + 2] = t.z, v[4 * q + 3] = t.w;
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const uint4 u = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.x) + i + 8 * q);
-          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[8 * q + 2 * e] = bf2f(w4[e] & 0xffffu);
-            v[8 * q + 2 * e + 1] = bf2f(w4[e] >> 16);
-          }
-        }
-      }
-      const uint4 sg = *reinterpret_cast<const uint4 *>(rht.signs + i);
-      const uint32_t s4[4] = {sg.x, sg.y, sg.z, sg.w};
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] *= (float)(int8_t)((s4[j >> 2] >> (8 * (j & 3))) & 0xffu);
-#pragma unroll
-      for (int h = 1; h < 16; h <<= 1)
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if ((j & h) == 0) {
-            const float p0 = v[j], p1 = v[j + h];
-            v[j] = p0 + p1;
-            v[j + h] = p0 - p1;
-          }
+      rht_load16(a.x, xt == VQ_F32, rht.signs, 16 * g, v);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4 *>(&s_x[i + 4 * q]) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        *reinterpret_cast<float4 *>(&s_x[16 * g + 4 * q]) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
     }
   }
   for (int i = 4 * tid; i < (rht16 ? 0 : K); i += 4 * NT) {

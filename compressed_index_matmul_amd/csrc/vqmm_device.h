@@ -312,4 +312,113 @@ __device__ __forceinline__ void stage_ladder_lds(const uint16_t *const *cb, uint
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fast Walsh-Hadamard transform pieces (GLQ page, "How it works": random
+// sign flips, then a fast Walsh-Hadamard transform; "Bit widths": blocks of
+// powers of two), shared by rht_apply and the 16-bit decode kernel.
+// ---------------------------------------------------------------------------
+
+// Elements i .. i + 15 of x (fp32 or bf16, 16-byte aligned) times their
+// signs (int8, 16-byte aligned), then butterfly stages 1, 2, 4, 8 (the low
+// four bits of the index) in registers, Sylvester order.
+__device__ __forceinline__ void rht_load16(const void *x, bool f32, const int8_t *signs, size_t i, float (&v)[16]) {
+  if (f32) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 t = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + i + 4 * q);
+      v[4 * q] = t.x, v[4 * q + 1] = t.y, v[4 * q + 2] = t.z, v[4 * q + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint4 u = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + i + 8 * q);
+      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[8 * q + 2 * e] = bf2f(w4[e] & 0xffffu);
+        v[8 * q + 2 * e + 1] = bf2f(w4[e] >> 16);
+      }
+    }
+  }
+  const uint4 sg = *reinterpret_cast<const uint4 *>(signs + i);
+  const uint32_t s4[4] = {sg.x, sg.y, sg.z, sg.w};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] *= (float)(int8_t)((s4[j >> 2] >> (8 * (j & 3))) & 0xffu);
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if ((j & h) == 0) {
+        const float p0 = v[j], p1 = v[j + h];
+        v[j] = p0 + p1;
+        v[j + h] = p0 - p1;
+      }
+}
+
+// One group of a FWHT pass: the R elements base + j 2^s (j < R) of s_x,
+// R = 2^r butterfly stages in registers; the result times sc.  With s == 0
+// the elements are contiguous and move as 16-byte LDS accesses.
+template <int R>
+__device__ __forceinline__ void fwht_group(float *s_x, int base, int s, float sc) {
+  float v[R];
+  if (R >= 4 && s == 0) {
+#pragma unroll
+    for (int q = 0; q < R / 4; ++q) {
+      const float4 t = *reinterpret_cast<const float4 *>(&s_x[base + 4 * q]);
+      v[4 * q] = t.x, v[4 * q + 1] = t.y, v[4 * q + 2] = t.z, v[4 * q + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < R; ++j) v[j] = s_x[base + (j << s)];
+  }
+#pragma unroll
+  for (int h = 1; h < R; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if ((j & h) == 0) {
+        const float p0 = v[j], p1 = v[j + h];
+        v[j] = p0 + p1;
+        v[j + h] = p0 - p1;
+      }
+#pragma unroll
+  for (int j = 0; j < R; ++j) v[j] *= sc;
+  if (R >= 4 && s == 0) {
+#pragma unroll
+    for (int q = 0; q < R / 4; ++q)
+      *reinterpret_cast<float4 *>(&s_x[base + 4 * q]) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < R; ++j) s_x[base + (j << s)] = v[j];
+  }
+}
+
+// Pass s over `count` blocks of 2^lb elements from offset off (bits [s, s +
+// r) of the in-block index: r = 4, or all that is left when that is at most
+// 5, so no pass of a single stage remains): the groups of all these
+// blocks spread over the NT threads; a block whose last bits these are is
+// scaled by 1/sqrt(2^lb).
+template <int NT>
+__device__ __forceinline__ void fwht_pass(float *s_x, int off, int count, int lb, int s, int s0, int tid) {
+  // passes start at s0, s0 + 4, ...; a block is done once a pass took its
+  // last bits (at most 5 of them), so later passes skip it
+  if (s >= lb || count <= 0 || (s > s0 && lb - (s - 4) <= 5)) return;
+  const int r = lb - s <= 5 ? lb - s : 4;
+  const bool last = s + r >= lb;
+  const float sc = last ? (float)(1.0 / __builtin_sqrt((double)(1 << lb))) : 1.f;
+  const int gpb_log = lb - r;  // log2 groups per block
+  const int groups = count << gpb_log;
+  for (int gid = tid; gid < groups; gid += NT) {
+    const int blk = gid >> gpb_log;
+    const int gi = gid & ((1 << gpb_log) - 1);
+    const int base = off + (blk << lb) + ((gi >> s) << (s + r)) + (gi & ((1 << s) - 1));
+    switch (r) {
+      case 5: fwht_group<32>(s_x, base, s, sc); break;
+      case 4: fwht_group<16>(s_x, base, s, sc); break;
+      case 3: fwht_group<8>(s_x, base, s, sc); break;
+      case 2: fwht_group<4>(s_x, base, s, sc); break;
+      default: fwht_group<2>(s_x, base, s, sc); break;
+    }
+  }
+}
+
 }  // namespace vqmm

@@ -300,7 +300,8 @@ def test_gemv_one_hot_columns(vq):
 
 
 @pytest.mark.parametrize("n,max_block", [(1, 8192), (2, 8192), (3, 8192), (2688, 8192), (28672, 16384),
-                                         (28672, 8192), (100, 1), (4096, 64)])
+                                         (28672, 8192), (100, 1), (4096, 64), (8192, 256), (8192, 512),
+                                         (2560, 2048), (6144, 4096), (16384, 16384), (256, 8192)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_rht_sizes(vq, n, max_block, dtype):
     import torch
