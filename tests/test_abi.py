@@ -174,6 +174,11 @@ def test_gemv_rht_argument_checks(L):
                  fake_desc(n=64, k=4096, bits=16, bs=96),             # scale block not dividing 2048
                  fake_desc(n=64, k=4096, stages=3, bits=16, bs=128)):  # three stages
         assert L.vq_gemv_rht(ctypes.byref(desc), FAKE, 1, 1, FAKE, 64, FAKE, None) == VQ_ERR_UNSUPPORTED
+    sp = fake_desc(n=64, k=4096, bits=16, bs=128)  # a sparse correction: not taken either
+    sp.sp_nnz = 5
+    sp.sp_rowptr, sp.sp_col, sp.sp_val = FAKE, FAKE, FAKE
+    assert L.vq_validate(ctypes.byref(sp)) == 0
+    assert L.vq_gemv_rht(ctypes.byref(sp), FAKE, 1, 1, FAKE, 64, FAKE, None) == VQ_ERR_UNSUPPORTED
 
 
 def test_unpack_argument_checks(L):
