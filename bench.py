@@ -389,8 +389,8 @@ def main():
         traffic_summary(*args.traffic_summary)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs on a "
-              "single MI355X and has no multi-GPU path)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library runs each "
+              "product on a single MI355X and has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     import torch
     import compressed_index_matmul_amd as vq
