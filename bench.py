@@ -325,17 +325,24 @@ def kernel_source_hash():
 
 
 def traffic_probe(spec, launches=20):
-    """Launch the batch-1 decode GEMV of one Llama-3-8B-shaped linear
-    `launches` times (weights rotated through >= 512 MiB of copies), then a
-    plain 256 MiB float32 copy (`dst = src * 1`) whose HBM bytes are known."""
+    """Launch the batch-1 decode GEMV of one linear `launches` times (weights
+    rotated through >= 512 MiB of copies), then a plain 256 MiB float32 copy
+    (`dst = src * 1`) whose HBM bytes are known.  spec: "N,K" (Llama-3-8B
+    format) or "workload:N,K"."""
     import torch
     import vqsynth
     import compressed_index_matmul_amd as vq
-    n, k = (int(v) for v in spec.split(","))
-    ws, act_ss = vqsynth.workload_weights("llama8b")
+    workload, _, shape = spec.rpartition(":")
+    workload = workload or "llama8b"
+    n, k = (int(v) for v in shape.split(","))
+    ws, act_ss = vqsynth.workload_weights(workload)
     sw = [w for w in ws if (w.n_out, w.k_in) == (n, k)][0]
-    st, _ = vqsynth.make_x(1, k, "bf16", act_ss.spawn(1)[0])
-    x = torch.from_numpy(st.view(np.int16)).cuda().view(torch.bfloat16)
+    cfg = vqsynth.WORKLOADS[workload]
+    st, _ = vqsynth.make_x(1, k, cfg["x_dtype"], act_ss.spawn(1)[0])
+    if cfg["x_dtype"] == "bf16":
+        x = torch.from_numpy(st.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        x = torch.from_numpy(st).cuda()
     sets = upload_set(vq, [sw], copies_for(compressed_bytes(sw)))
     y = torch.empty((1, n), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
@@ -346,7 +353,7 @@ def traffic_probe(spec, launches=20):
     torch.cuda.synchronize()
     torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
-    print(json.dumps({"probe": [n, k], "launches": launches, "copy_bytes": COPY_BYTES}), flush=True)
+    print(json.dumps({"probe": [workload, n, k], "launches": launches, "copy_bytes": COPY_BYTES}), flush=True)
 
 
 def traffic_summary(spec, fetch_csv, write_csv, out_json):

@@ -10,8 +10,16 @@ Entry points (same names as the C ABI):
 * :func:`vq_unpack_dequant` -- unpacked indices and/or the fp16 dense weight
 * :func:`vq_gemv`           -- y = x dequant(W)^T for 1..16 tokens
 * :func:`vq_gemm`           -- the same for many bf16 tokens on matrix cores
+  (with :func:`vq_gemm_workspace_size` for its caller-owned scratch)
 * :func:`rht_apply`         -- randomized Hadamard transform of activations
+* :func:`vq_gemv_rht`       -- vq_gemv with the input transform inside the kernel
 * :func:`vq_compressed_bytes`, :func:`vq_validate`, :func:`vq_version`
+
+The C ABI cannot see buffer sizes, so every wrapper checks what it can before
+the call: each tensor is contiguous, on the weight's GPU, of the expected
+dtype and shape (a ValueError or TypeError otherwise, with nothing launched);
+:class:`VQWeight` checks every plane, codebook, scale and correction array
+against the shape and index widths it is given.
 """
 
 from __future__ import annotations
@@ -24,15 +32,15 @@ import numpy as np
 
 __all__ = [
     "VQError", "VQWeight", "lib", "LIB_PATH", "vq_version", "vq_validate", "vq_compressed_bytes",
-    "vq_unpack_dequant", "vq_gemv", "vq_gemm", "rht_apply", "vq_gemv_rht", "VQ_F32", "VQ_BF16", "VQ_STAGE_SCALES",
-    "EXPORTS",
+    "vq_unpack_dequant", "vq_gemv", "vq_gemm", "vq_gemm_workspace_size", "rht_apply", "vq_gemv_rht", "VQ_F32",
+    "VQ_BF16", "VQ_STAGE_SCALES", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvqmm.so")
 VQ_F32, VQ_BF16 = 0, 1
 MAX_STAGES = 4
 EXPORTS = ("vq_version", "vq_status_string", "vq_validate", "vq_compressed_bytes",
-           "vq_unpack_dequant", "vq_gemv", "vq_gemm", "rht_apply", "vq_gemv_rht")
+           "vq_unpack_dequant", "vq_gemv", "vq_gemm", "vq_gemm_workspace_size", "rht_apply", "vq_gemv_rht")
 
 _ptr4 = ctypes.c_void_p * MAX_STAGES
 _int4 = ctypes.c_int32 * MAX_STAGES
@@ -90,7 +98,9 @@ def lib() -> ctypes.CDLL:
         L.vq_unpack_dequant.argtypes, L.vq_unpack_dequant.restype = [D, P, P, P], ctypes.c_int
         L.vq_gemv.argtypes = [D, P, ctypes.c_int32, ctypes.c_int32, P, P]
         L.vq_gemv.restype = ctypes.c_int
-        L.vq_gemm.argtypes, L.vq_gemm.restype = [D, P, ctypes.c_int32, P, P], ctypes.c_int
+        L.vq_gemm.argtypes, L.vq_gemm.restype = [D, P, ctypes.c_int32, P, P, ctypes.c_size_t, P], ctypes.c_int
+        L.vq_gemm_workspace_size.argtypes = [D, ctypes.c_int32]
+        L.vq_gemm_workspace_size.restype = ctypes.c_size_t
         L.rht_apply.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P, P]
         L.rht_apply.restype = ctypes.c_int
         L.vq_gemv_rht.argtypes = [D, P, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P, P]
@@ -161,14 +171,65 @@ class VQWeight:
         self.lo = [None if v is None else _as_device(v, self.device, torch.uint8) for v in lo]
         self.hi = [None if v is None else _as_device(v, self.device, torch.uint8) for v in hi]
         self.idx16 = [None if v is None else _as_device(v, self.device, torch.int16) for v in idx16]
+        self.device = self.scales.device  # resolved ("cuda" -> "cuda:0")
         self.sparse = None
         if sparse is not None:
             rp, cl, vl = sparse
             self.sparse = (_as_device(np.asarray(rp, np.int32), self.device, torch.int32),
                            _as_device(np.asarray(cl, np.int32), self.device, torch.int32),
                            _as_device(np.asarray(vl, np.float16), self.device, torch.float16))
+        self._check_arrays()
         self.desc = VQWeightDesc()
         self._fill_desc()
+
+    def widths(self):
+        """Index width of each stage."""
+        sb = self.stage_bits or []
+        return [sb[t] if t < len(sb) and sb[t] else self.idx_bits for t in range(self.n_stages)]
+
+    def _check_arrays(self):
+        """Every array the descriptor will point at holds exactly what the
+        shape and the index widths say (the kernels read that many bytes and
+        cannot check it), on one device, contiguous."""
+        n, k, S = self.n_out, self.k_in, self.n_stages
+        if n < 1 or k < 8 or k % 8 or not 1 <= S <= MAX_STAGES or self.scale_block < 8:
+            raise ValueError(f"invalid weight shape n_out={n} k_in={k} n_stages={S} scale_block={self.scale_block}")
+        groups = n * (k // 8)
+        bs = min(self.scale_block, k)
+
+        def need(t, what, name, count):
+            if t is None:
+                raise ValueError(f"{name} is missing")
+            if t.device != self.device or not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous on {self.device}")
+            if t.numel() != count:
+                raise ValueError(f"{name} holds {t.numel()} {what}, the weight needs {count}")
+
+        def get(lst, t):
+            return lst[t] if t < len(lst) else None
+
+        if len(self.codebooks) < S:
+            raise ValueError(f"{S} stages need {S} codebooks, got {len(self.codebooks)}")
+        for t, b in enumerate(self.widths()):
+            if b not in (4, 8, 12, 16):
+                raise ValueError(f"stage {t}: index width {b} is not 4, 8, 12 or 16")
+            need(self.codebooks[t], "fp16 values", f"codebook[{t}]", (1 << b) * 8)
+            if b == 16:
+                need(get(self.idx16, t), "uint16 indices", f"idx16[{t}]", groups)
+            if b in (8, 12):
+                need(get(self.lo, t), "bytes", f"lo[{t}]", groups)
+            if b in (4, 12):
+                need(get(self.hi, t), "bytes", f"hi[{t}]", (groups + 1) // 2)
+        need(self.scales, "fp16 scales", "scales", n * (-(-k // bs)))
+        if self.stage_scales is not None and len(self.stage_scales) < S:
+            raise ValueError(f"{S} stages need {S} stage scales, got {len(self.stage_scales)}")
+        if self.sparse is not None:
+            rp, cl, vl = self.sparse
+            need(rp, "row pointers", "sparse rowptr", n + 1)
+            if cl.numel() != vl.numel():
+                raise ValueError("sparse columns and values differ in length")
+            for name, t in (("sparse col", cl), ("sparse val", vl)):
+                need(t, "entries", name, cl.numel())
 
     def _fill_desc(self):
         d = self.desc
@@ -234,11 +295,55 @@ def _xtype(x) -> int:
     raise TypeError(f"activations must be float32 or bfloat16, got {x.dtype}")
 
 
+def _on_gpu(t, device, name: str) -> None:
+    """t is a contiguous tensor on the GPU `device` (ValueError otherwise)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda" or t.device != device:
+        raise ValueError(f"{name} is on {t.device}; it must be on the weight's GPU {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _weight_device(w: VQWeight):
+    if w.device.type != "cuda":
+        raise ValueError(f"the weight is on {w.device}; the kernels need it on a GPU")
+    return w.device
+
+
+def _tokens(x, k: int, name: str = "x"):
+    """x as [B, k] (a 1-D x is one token)."""
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"{name} has shape {tuple(x.shape)}; expected [tokens, {k}]")
+    return x
+
+
+def _out(y, shape, device, name: str = "y"):
+    import torch
+    if y is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    _on_gpu(y, device, name)
+    if y.dtype != torch.float32 or tuple(y.shape) != tuple(shape):
+        raise ValueError(f"{name} must be float32 of shape {tuple(shape)}, got {y.dtype} {tuple(y.shape)}")
+    return y
+
+
+def _signs(signs, n: int, device):
+    import torch
+    _on_gpu(signs, device, "signs")
+    if signs.dtype != torch.int8 or signs.numel() != n:
+        raise ValueError(f"signs must be int8 of length {n}, got {signs.dtype} of length {signs.numel()}")
+
+
 def vq_unpack_dequant(w: VQWeight, want_idx: bool = True, want_w: bool = True, stream=None):
     """Returns (idx [S, N, K/8] int32-viewable uint16 as torch.int16, w fp16 [N, K])."""
     import torch
-    idx = torch.empty((w.n_stages, w.n_out, w.k_in // 8), dtype=torch.int16, device=w.device) if want_idx else None
-    wt = torch.empty((w.n_out, w.k_in), dtype=torch.float16, device=w.device) if want_w else None
+    dev = _weight_device(w)
+    idx = torch.empty((w.n_stages, w.n_out, w.k_in // 8), dtype=torch.int16, device=dev) if want_idx else None
+    wt = torch.empty((w.n_out, w.k_in), dtype=torch.float16, device=dev) if want_w else None
     _check(lib().vq_unpack_dequant(w.ref(), idx.data_ptr() if idx is not None else None,
                                    wt.data_ptr() if wt is not None else None, _stream_handle(stream)),
            "vq_unpack_dequant")
@@ -247,40 +352,60 @@ def vq_unpack_dequant(w: VQWeight, want_idx: bool = True, want_w: bool = True, s
 
 def vq_gemv(w: VQWeight, x, y=None, stream=None):
     """x: [B, K] (B <= 16) float32 or bfloat16 on the device -> y float32 [B, N]."""
-    import torch
-    if x.dim() == 1:
-        x = x.unsqueeze(0)
-    x = x.contiguous()
+    dev = _weight_device(w)
+    x = _tokens(x, w.k_in)
+    xt = _xtype(x)
+    _on_gpu(x, dev, "x")
     b = x.shape[0]
-    if y is None:
-        y = torch.empty((b, w.n_out), dtype=torch.float32, device=x.device)
-    _check(lib().vq_gemv(w.ref(), x.data_ptr(), _xtype(x), b, y.data_ptr(), _stream_handle(stream)), "vq_gemv")
+    if not 1 <= b <= 16:
+        raise ValueError(f"vq_gemv takes 1..16 tokens, got {b} (use vq_gemm)")
+    y = _out(y, (b, w.n_out), dev)
+    _check(lib().vq_gemv(w.ref(), x.data_ptr(), xt, b, y.data_ptr(), _stream_handle(stream)), "vq_gemv")
     return y
 
 
-def vq_gemm(w: VQWeight, x, y=None, stream=None):
-    """x: bfloat16 [M, K] on the device -> y float32 [M, N]."""
+def vq_gemm_workspace_size(w: VQWeight, m: int) -> int:
+    """Bytes of workspace vq_gemm needs for m tokens (0: none)."""
+    return int(lib().vq_gemm_workspace_size(w.ref(), int(m)))
+
+
+def vq_gemm(w: VQWeight, x, y=None, workspace=None, stream=None):
+    """x: bfloat16 [M, K] on the device -> y float32 [M, N].  `workspace`: a
+    uint8 device tensor of at least vq_gemm_workspace_size(w, M) bytes; None
+    allocates one from torch's caching allocator when the call needs any."""
     import torch
+    dev = _weight_device(w)
+    x = _tokens(x, w.k_in)
     if x.dtype != torch.bfloat16:
         raise TypeError("vq_gemm takes bfloat16 activations")
-    x = x.contiguous()
+    _on_gpu(x, dev, "x")
     m = x.shape[0]
-    if y is None:
-        y = torch.empty((m, w.n_out), dtype=torch.float32, device=x.device)
-    _check(lib().vq_gemm(w.ref(), x.data_ptr(), m, y.data_ptr(), _stream_handle(stream)), "vq_gemm")
+    y = _out(y, (m, w.n_out), dev)
+    need = vq_gemm_workspace_size(w, m)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    if workspace is not None:
+        _on_gpu(workspace, dev, "workspace")
+    ws_ptr = workspace.data_ptr() if workspace is not None and workspace.numel() else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().vq_gemm(w.ref(), x.data_ptr(), m, y.data_ptr(), ws_ptr, ws_bytes, _stream_handle(stream)),
+           "vq_gemm")
     return y
 
 
 def rht_apply(x, signs, max_block: int, out=None, stream=None):
     """x: [B, n] float32/bfloat16, signs int8 [n] on the device -> float32 [B, n]."""
-    import torch
     if x.dim() == 1:
         x = x.unsqueeze(0)
-    x = x.contiguous()
+    if x.dim() != 2:
+        raise ValueError(f"x has shape {tuple(x.shape)}; expected [tokens, n]")
+    xt = _xtype(x)
+    dev = x.device
+    _on_gpu(x, dev, "x")
     b, n = x.shape
-    if out is None:
-        out = torch.empty((b, n), dtype=torch.float32, device=x.device)
-    _check(lib().rht_apply(x.data_ptr(), _xtype(x), b, n, signs.data_ptr(), max_block, out.data_ptr(),
+    _signs(signs, n, dev)
+    out = _out(out, (b, n), dev, "out")
+    _check(lib().rht_apply(x.data_ptr(), xt, b, n, signs.data_ptr(), max_block, out.data_ptr(),
                            _stream_handle(stream)), "rht_apply")
     return out
 
@@ -290,13 +415,15 @@ def vq_gemv_rht(w: VQWeight, x, signs, max_block: int, y=None, stream=None):
     x [B, K] (B <= 16) float32/bfloat16, signs int8 [K] on the device -> y
     float32 [B, N].  Raises VQError (VQ_ERR_UNSUPPORTED) for weights the
     16-bit decode kernel does not take."""
-    import torch
-    if x.dim() == 1:
-        x = x.unsqueeze(0)
-    x = x.contiguous()
+    dev = _weight_device(w)
+    x = _tokens(x, w.k_in)
+    xt = _xtype(x)
+    _on_gpu(x, dev, "x")
     b = x.shape[0]
-    if y is None:
-        y = torch.empty((b, w.n_out), dtype=torch.float32, device=x.device)
-    _check(lib().vq_gemv_rht(w.ref(), x.data_ptr(), _xtype(x), b, signs.data_ptr(), max_block, y.data_ptr(),
+    if not 1 <= b <= 16:
+        raise ValueError(f"vq_gemv_rht takes 1..16 tokens, got {b}")
+    _signs(signs, w.k_in, dev)
+    y = _out(y, (b, w.n_out), dev)
+    _check(lib().vq_gemv_rht(w.ref(), x.data_ptr(), xt, b, signs.data_ptr(), max_block, y.data_ptr(),
                              _stream_handle(stream)), "vq_gemv_rht")
     return y

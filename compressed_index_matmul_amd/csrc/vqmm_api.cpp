@@ -120,6 +120,7 @@ const char *vq_status_string(int status) {
     case VQ_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
     case VQ_ERR_HIP: return "HIP runtime error";
     case VQ_ERR_VALUE: return "a scalar argument value is invalid";
+    case VQ_ERR_WORKSPACE: return "the workspace is smaller than vq_gemm_workspace_size";
     default: return "unknown status";
   }
 }
@@ -163,7 +164,7 @@ int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, f
   if (batch > 1 && x_dtype == VQ_BF16) {
     hipError_t e = hipSuccess;
     if (launch_gemv_tokens(v, x, batch, y, s, &e)) sp_done = true;
-    else e = launch_gemm(v, reinterpret_cast<const uint16_t *>(x), batch, y, s);
+    else e = launch_gemm(v, reinterpret_cast<const uint16_t *>(x), batch, y, nullptr, 0, s);
     if (e != hipSuccess) return VQ_ERR_HIP;
   } else {
     const size_t esz = x_dtype == VQ_F32 ? 4 : 2;
@@ -177,18 +178,28 @@ int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, f
   return map_hip(launch_sparse_add(v, x, x_dtype, batch, y, s));
 }
 
-int vq_gemm(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float *y, void *stream) {
+int vq_gemm(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float *y, void *workspace, size_t ws_bytes,
+            void *stream) {
   WView v;
   int st = check_weight(w, &v);
   if (st != VQ_OK) return st;
   if (!x_bf16 || !y) return VQ_ERR_NULL;
   if (m < 1) return VQ_ERR_SHAPE;
   if ((int64_t)m * v.k >= ((int64_t)1 << 31) || (int64_t)m * v.n >= ((int64_t)1 << 31)) return VQ_ERR_SHAPE;
-  if (!aligned16(x_bf16) || !aligned16(y)) return VQ_ERR_ALIGN;
+  if (ws_bytes > 0 && !workspace) return VQ_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(y) || !aligned16(workspace)) return VQ_ERR_ALIGN;
+  if (ws_bytes < gemm_workspace_bytes(v, m)) return VQ_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  st = map_hip(launch_gemm(v, x_bf16, m, y, s));
+  st = map_hip(launch_gemm(v, x_bf16, m, y, workspace, ws_bytes, s));
   if (st != VQ_OK) return st;
   return map_hip(launch_sparse_add(v, x_bf16, VQ_BF16, m, y, s));
+}
+
+size_t vq_gemm_workspace_size(const vq_weight *w, int32_t m) {
+  WView v;
+  if (check_weight(w, &v) != VQ_OK || m < 1) return 0;
+  if ((int64_t)m * v.k >= ((int64_t)1 << 31) || (int64_t)m * v.n >= ((int64_t)1 << 31)) return 0;
+  return gemm_workspace_bytes(v, m);
 }
 
 int vq_gemv_rht(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, const int8_t *signs,

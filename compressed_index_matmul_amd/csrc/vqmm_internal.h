@@ -57,7 +57,11 @@ hipError_t launch_gemv_rht_token(const WView &w, const void *x, int xt, const in
 // allows it (false: not taken, nothing launched; *err set when taken).  The
 // kernel also adds the sparse correction.
 bool launch_gemv_tokens(const WView &w, const void *x, int batch, float *y, hipStream_t s, hipError_t *err);
-hipError_t launch_gemm(const WView &w, const uint16_t *x, int m, float *y, hipStream_t s);
+// The many-token product; ws / ws_bytes: the caller's workspace (may be
+// null / 0), at least gemm_workspace_bytes(w, m) bytes.
+hipError_t launch_gemm(const WView &w, const uint16_t *x, int m, float *y, void *ws, size_t ws_bytes, hipStream_t s);
+// Workspace bytes the many-token product of m tokens needs (0: none).
+size_t gemm_workspace_bytes(const WView &w, int m);
 // y[b][r] += sum_j val_j x[b][col_j] over the sparse correction's row r, for
 // m tokens of x (VQ_F32 / VQ_BF16); after the main product on the same
 // stream.  No-op without a correction.

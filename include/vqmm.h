@@ -26,7 +26,8 @@
  *    arguments return an error with nothing enqueued and no device touched.
  *    A failed launch returns VQ_ERR_HIP.  No C++ exception crosses the ABI.
  *  - The library allocates no device memory and holds no per-call state;
- *    calls on different streams may run concurrently.
+ *    calls on different streams may run concurrently.  Scratch memory, where
+ *    a kernel needs any, is the caller's workspace (vq_gemm).
  *  - Results are deterministic: fixed reduction order, no atomics.
  */
 #ifndef VQMM_H
@@ -39,7 +40,7 @@
 extern "C" {
 #endif
 
-#define VQMM_VERSION 3
+#define VQMM_VERSION 4
 #define VQ_MAX_STAGES 4
 
 /* vq_weight.flags: stage_scale[] holds one residual scale per stage. */
@@ -54,7 +55,8 @@ typedef enum vq_status {
   VQ_ERR_UNSUPPORTED = -4, /* valid request outside what the kernels implement */
   VQ_ERR_ALIGN = -5,       /* a base pointer is not 16-byte aligned */
   VQ_ERR_HIP = -6,         /* the HIP runtime reported an error */
-  VQ_ERR_VALUE = -7        /* a scalar argument value is invalid (a non-finite stage scale) */
+  VQ_ERR_VALUE = -7,       /* a scalar argument value is invalid (a non-finite stage scale) */
+  VQ_ERR_WORKSPACE = -8    /* the caller's workspace is smaller than vq_gemm_workspace_size */
 } vq_status;
 
 /* Element types of activations. */
@@ -184,8 +186,17 @@ int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, f
  * Many-token product y = x dequant(W)^T (GLQ page, "Inference kernels":
  * tensor-core path for batched inputs).  Decoded weight tiles are rounded to
  * bf16 on chip and multiplied on bf16 matrix cores with fp32 accumulation.
- *   x : bf16 bits [m][k_in];  m >= 1
- *   y : float [m][n_out]
+ *   x         : bf16 bits [m][k_in];  m >= 1
+ *   y         : float [m][n_out]
+ *   workspace : device scratch of ws_bytes bytes owned by the caller, 16-byte
+ *               aligned, or NULL when ws_bytes == 0.  It must hold at least
+ *               vq_gemm_workspace_size(w, m) bytes (VQ_ERR_WORKSPACE
+ *               otherwise, before any HIP call); its contents on entry are
+ *               ignored and on return unspecified.  Kernels of the same call
+ *               use it in stream order (the GLQ page, "Inference kernels",
+ *               keeps split-K partials in such a scratch buffer so that the
+ *               reduction order stays fixed); two calls in flight at the same
+ *               time need two workspaces.
  * bf16 keeps 8 significant bits, so each weight carries a relative error of
  * up to 2^-8: the guaranteed bound is |y - y_exact| <= (2^-8 + 2^-23 +
  * k_in 2^-24) sum_k |w x| + 1e-6.  For dense activations the rounding errors
@@ -194,7 +205,13 @@ int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, f
  * can exceed that tighter bound.  A sparse correction adds x S^T exactly as
  * vq_gemv does (fp32, not rounded to bf16).
  */
-int vq_gemm(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float *y, void *stream);
+int vq_gemm(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float *y, void *workspace, size_t ws_bytes,
+            void *stream);
+
+/* Bytes of workspace vq_gemm needs for this weight and m tokens (0: none).
+ * Returns 0 for an invalid descriptor or m < 1 (vq_gemm then reports the
+ * error itself).  Host only; touches no device. */
+size_t vq_gemm_workspace_size(const vq_weight *w, int32_t m);
 
 /*
  * Randomized Hadamard transform of each row of x (GLQ page, "How it works":

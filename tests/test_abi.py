@@ -13,8 +13,8 @@ from vqtest import ROOT, ensure_built
 
 HEADER = os.path.join(ROOT, "include", "vqmm.h")
 
-VQ_OK, VQ_ERR_NULL, VQ_ERR_SHAPE, VQ_ERR_DTYPE, VQ_ERR_UNSUPPORTED, VQ_ERR_ALIGN, VQ_ERR_HIP, VQ_ERR_VALUE = \
-    0, -1, -2, -3, -4, -5, -6, -7
+VQ_OK, VQ_ERR_NULL, VQ_ERR_SHAPE, VQ_ERR_DTYPE, VQ_ERR_UNSUPPORTED, VQ_ERR_ALIGN, VQ_ERR_HIP, VQ_ERR_VALUE, \
+    VQ_ERR_WORKSPACE = 0, -1, -2, -3, -4, -5, -6, -7, -8
 FAKE = 0x10000  # 16-byte aligned stand-in address, never dereferenced by validation
 
 
@@ -41,7 +41,7 @@ def test_library_resolves_every_symbol():
 
 def test_header_declares_the_boundary():
     fns = header_functions()
-    for name in ("vq_unpack_dequant", "vq_gemv", "vq_gemm", "rht_apply", "vq_version",
+    for name in ("vq_unpack_dequant", "vq_gemv", "vq_gemm", "vq_gemm_workspace_size", "rht_apply", "vq_version",
                  "vq_status_string", "vq_validate", "vq_compressed_bytes"):
         assert name in fns
 
@@ -60,7 +60,7 @@ def test_version_matches_header(L):
 
 def test_status_strings(L):
     for st in (VQ_OK, VQ_ERR_NULL, VQ_ERR_SHAPE, VQ_ERR_DTYPE, VQ_ERR_UNSUPPORTED, VQ_ERR_ALIGN, VQ_ERR_HIP,
-               VQ_ERR_VALUE):
+               VQ_ERR_VALUE, VQ_ERR_WORKSPACE):
         s = L.vq_status_string(st).decode()
         assert s and s != "unknown status"
     assert L.vq_status_string(12345).decode() == "unknown status"
@@ -123,7 +123,7 @@ def test_invalid_descriptor(L, mutate, code):
     assert L.vq_validate(ctypes.byref(d)) == code
     # every compute entry point returns the same code, before any HIP call
     assert L.vq_gemv(ctypes.byref(d), FAKE, 1, 1, FAKE, None) == code
-    assert L.vq_gemm(ctypes.byref(d), FAKE, 64, FAKE, None) == code
+    assert L.vq_gemm(ctypes.byref(d), FAKE, 64, FAKE, None, 0, None) == code
     assert L.vq_unpack_dequant(ctypes.byref(d), FAKE, FAKE, None) == code
     assert L.vq_compressed_bytes(ctypes.byref(d)) == code
 
@@ -146,11 +146,34 @@ def test_gemv_argument_checks(L):
 
 def test_gemm_argument_checks(L):
     d = ctypes.byref(fake_desc())
-    assert L.vq_gemm(d, None, 4, FAKE, None) == VQ_ERR_NULL
-    assert L.vq_gemm(d, FAKE, 4, None, None) == VQ_ERR_NULL
-    assert L.vq_gemm(d, FAKE, 0, FAKE, None) == VQ_ERR_SHAPE
-    assert L.vq_gemm(d, FAKE, 1 << 30, FAKE, None) == VQ_ERR_SHAPE
-    assert L.vq_gemm(d, FAKE + 2, 4, FAKE, None) == VQ_ERR_ALIGN
+    assert L.vq_gemm(d, None, 4, FAKE, None, 0, None) == VQ_ERR_NULL
+    assert L.vq_gemm(d, FAKE, 4, None, None, 0, None) == VQ_ERR_NULL
+    assert L.vq_gemm(d, FAKE, 0, FAKE, None, 0, None) == VQ_ERR_SHAPE
+    assert L.vq_gemm(d, FAKE, 1 << 30, FAKE, None, 0, None) == VQ_ERR_SHAPE
+    assert L.vq_gemm(d, FAKE + 2, 4, FAKE, None, 0, None) == VQ_ERR_ALIGN
+    assert L.vq_gemm(d, FAKE, 4, FAKE, None, 64, None) == VQ_ERR_NULL      # bytes without a buffer
+    assert L.vq_gemm(d, FAKE, 4, FAKE, FAKE + 8, 64, None) == VQ_ERR_ALIGN
+
+
+@pytest.mark.parametrize("n,k,bits,stages,m", [(64, 64, 12, 1, 4), (4096, 4096, 12, 2, 2048), (14336, 4096, 12, 2, 2048),
+                                               (4096, 4096, 12, 2, 1), (28672, 8192, 16, 1, 64), (256, 512, 8, 1, 40)])
+def test_gemm_workspace_contract(L, n, k, bits, stages, m):
+    """vq_gemm takes any workspace of at least vq_gemm_workspace_size bytes
+    and returns VQ_ERR_WORKSPACE, before any HIP call, for one byte less."""
+    d = ctypes.byref(fake_desc(n=n, k=k, bits=bits, stages=stages, bs=128))
+    need = L.vq_gemm_workspace_size(d, m)
+    assert need % 256 == 0
+    if need:
+        assert L.vq_gemm(d, FAKE, m, FAKE, FAKE, need - 1, None) == VQ_ERR_WORKSPACE
+        assert L.vq_gemm(d, FAKE, m, FAKE, None, 0, None) == VQ_ERR_WORKSPACE
+
+
+def test_gemm_workspace_size_invalid(L):
+    assert L.vq_gemm_workspace_size(None, 16) == 0
+    d = fake_desc()
+    assert L.vq_gemm_workspace_size(ctypes.byref(d), 0) == 0
+    d.n_out = 0
+    assert L.vq_gemm_workspace_size(ctypes.byref(d), 16) == 0
 
 
 def test_gemv_rht_argument_checks(L):
@@ -251,7 +274,7 @@ def test_invalid_ladder(L, mutate, code):
     mutate(d)
     assert L.vq_validate(ctypes.byref(d)) == code
     assert L.vq_gemv(ctypes.byref(d), FAKE, 1, 1, FAKE, None) == code
-    assert L.vq_gemm(ctypes.byref(d), FAKE, 64, FAKE, None) == code
+    assert L.vq_gemm(ctypes.byref(d), FAKE, 64, FAKE, None, 0, None) == code
     assert L.vq_unpack_dequant(ctypes.byref(d), FAKE, FAKE, None) == code
 
 
@@ -314,7 +337,7 @@ def test_invalid_sparse(L, mutate, code):
     mutate(d)
     assert L.vq_validate(ctypes.byref(d)) == code
     assert L.vq_gemv(ctypes.byref(d), FAKE, 1, 1, FAKE, None) == code
-    assert L.vq_gemm(ctypes.byref(d), FAKE, 64, FAKE, None) == code
+    assert L.vq_gemm(ctypes.byref(d), FAKE, 64, FAKE, None, 0, None) == code
     assert L.vq_unpack_dequant(ctypes.byref(d), FAKE, FAKE, None) == code
 
 
