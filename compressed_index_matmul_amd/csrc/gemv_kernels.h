@@ -731,6 +731,11 @@ bool launch_gemv_tokens_sparse(const WView &w, const GemvArgs &a, int batch, int
 // its launch (false: nothing launched); signs (null: none) and max_block
 // give the input transform it applies to x first.
 bool gemv_l2_takes(const WView &w);
+// One 16-bit stage with one scale per row, the codebook streamed through LDS
+// in slices (k_gemv_cbs.hip): whether it takes the weight, and its launch for
+// one token (false: nothing launched).
+bool gemv_cbs_takes(const WView &w);
+bool launch_gemv_cbs(const WView &w, const void *x, int xt, float *y, int cus, hipStream_t s);
 bool launch_gemv_l2(const WView &w, const GemvArgs &a, int xt, int cus, hipStream_t s, const int8_t *signs = nullptr,
                     int max_block = 0);
 
