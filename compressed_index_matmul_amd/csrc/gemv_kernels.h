@@ -249,8 +249,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_lds(GemvArgs a) {
     }
   }
   // this wave's codebook part landed before its x; the barrier makes every
-  // wave's codebook part and x visible
-  __syncthreads();
+  // wave's codebook part and x visible, with the first rows' index loads
+  // still in flight (lds_barrier, not __syncthreads: that would wait for them)
+  lds_barrier();
 
   // this lane's x chunks: registers for the whole launch (XREG) or LDS reads
   // per use; the per-chunk factor, zero for chunks past the end of the row
@@ -734,8 +735,13 @@ bool gemv_l2_takes(const WView &w);
 // One 16-bit stage with one scale per row, the codebook streamed through LDS
 // in slices (k_gemv_cbs.hip): whether it takes the weight, and its launch for
 // one token (false: nothing launched).
+// With signs (max_block its largest block) the kernel applies the input
+// transform to its own copy of x first; gemv_cbs_rht_takes says whether it
+// can for this weight.
 bool gemv_cbs_takes(const WView &w);
-bool launch_gemv_cbs(const WView &w, const void *x, int xt, float *y, int cus, hipStream_t s);
+bool gemv_cbs_rht_takes(const WView &w);
+bool launch_gemv_cbs(const WView &w, const void *x, int xt, float *y, int cus, hipStream_t s,
+                     const int8_t *signs = nullptr, int max_block = 0);
 bool launch_gemv_l2(const WView &w, const GemvArgs &a, int xt, int cus, hipStream_t s, const int8_t *signs = nullptr,
                     int max_block = 0);
 

@@ -120,14 +120,16 @@ hipError_t launch_gemv_token(const WView &w, const void *x, int xt, float *y, hi
   return hipGetLastError();
 }
 
-bool gemv_rht_takes(const WView &w) { return w.sp_nnz == 0 && gemv_l2_takes(w); }
+bool gemv_rht_takes(const WView &w) { return w.sp_nnz == 0 && (gemv_cbs_rht_takes(w) || gemv_l2_takes(w)); }
 
 hipError_t launch_gemv_rht_token(const WView &w, const void *x, int xt, const int8_t *signs, int max_block, float *y,
                                  hipStream_t s) {
+  const int cus = device_cu_count();
+  if (launch_gemv_cbs(w, x, xt, y, cus, s, signs, max_block)) return hipGetLastError();
   GemvArgs a = make_args(w);
   a.x = x;
   a.y = y;
-  if (!launch_gemv_l2(w, a, xt, device_cu_count(), s, signs, max_block)) return hipErrorInvalidValue;
+  if (!launch_gemv_l2(w, a, xt, cus, s, signs, max_block)) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

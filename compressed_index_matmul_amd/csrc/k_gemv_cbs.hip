@@ -57,6 +57,8 @@ struct CbsArgs {
   int slice;            // codebook entries per pass (multiple of 64, <= kCbsMaxSlice)
   int passes;           // slices covering the 65,536 entries
   float r0;             // stage scale (1 without)
+  const int8_t *signs;  // the input transform's signs, or null: none
+  int mb;               // its largest block
 };
 
 // offset = (16-bit half h of p) * 16 + c (mod 2^32): v_mad_u32_u16, whose
@@ -131,9 +133,47 @@ __global__ __launch_bounds__(kCbsWaves * 64) void k_gemv_cbs(CbsArgs a) {
   float f;
   {
     float xv[U][16];
-    // every load of the lane's x issued before the first use (one branch
-    // on the dtype around all of them)
-    if (a.xt == VQ_F32) {
+    if (a.signs) {
+      // The input transform (GLQ page, "How it works": random sign flips,
+      // then a fast Walsh-Hadamard transform, block-diagonal over the greedy
+      // power-of-two blocks of at most mb, "Bit widths"), on this
+      // workgroup's fp32 copy of x in the LDS that slice 0 later takes: the
+      // signs multiply x as it is staged (with blocks of at least 32, 16
+      // consecutive elements per thread and their first four butterfly
+      // stages in registers), then passes of butterfly stages, each block
+      // scaled by 1/sqrt(its length) in its last pass.
+      constexpr int NT = kCbsWaves * 64;
+      float *s_x = reinterpret_cast<float *>(s_cb);
+      const bool rht16 = a.mb >= 32;  // uniform
+      if (rht16) {
+        for (int g = tid; g < a.k / 16; g += NT) {
+          float v[16];
+          rht_load16(a.x, a.xt == VQ_F32, a.signs, 16 * g, v);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4 *>(&s_x[16 * g + 4 * q]) =
+                make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        }
+      } else {
+        for (int i = tid; i < a.k; i += NT) {
+          const float v = a.xt == VQ_F32 ? reinterpret_cast<const float *>(a.x)[i]
+                                         : bf2f(reinterpret_cast<const uint16_t *>(a.x)[i]);
+          s_x[i] = v * (float)a.signs[i];
+        }
+      }
+      fwht_lds<NT>(s_x, a.k, a.mb, tid, rht16 ? 4 : 0);
+      __syncthreads();  // the last pass is complete
+#pragma unroll
+      for (int j = 0; j < U; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 t = *reinterpret_cast<const float4 *>(&s_x[16 * (pair0 + 64u * j) + 4 * q]);
+          xv[j][4 * q] = t.x, xv[j][4 * q + 1] = t.y, xv[j][4 * q + 2] = t.z, xv[j][4 * q + 3] = t.w;
+        }
+      __syncthreads();  // every lane holds its values before slice 0 overwrites them
+    } else if (a.xt == VQ_F32) {
+      // every load of the lane's x issued before the first use (one branch
+      // on the dtype around all of them)
       float4 t[U][4];
 #pragma unroll
       for (int j = 0; j < U; ++j)
@@ -188,24 +228,51 @@ __global__ __launch_bounds__(kCbsWaves * 64) void k_gemv_cbs(CbsArgs a) {
   uint32_t I[ROWS][U];
   float acc[ROWS];
 
-  // One row of one pass: the row's 2U indices against slice p (offset
-  // constant c = -16 p S), 16-byte LDS reads, then the dot products in a
-  // fixed order.
-  auto row_pass = [&](int i, uint32_t c) {
-    sched_fence();  // one row's reads in flight at a time (registers)
-    uint4 v[2 * U];
+  // A batch is half a row: the low (h = 0) or the high (h = 1) index of
+  // each of the row's U pairs.  issue: the batch's U indices against slice p
+  // (offset constant c = -16 p S) as 16-byte LDS reads; consume: their dot
+  // products in a fixed order.  The registers of I are made opaque first:
+  // nothing computed from them is hoisted out of the pass loop (that would
+  // keep 2U offsets per row live across it).
+  auto issue = [&](int i, int h, uint32_t c, uint4 (&v)[U]) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) asm volatile("" : "+v"(I[i][j]));
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const uint32_t o0 = min(mad16<0>(I[i][j], c), zero_off);
-      const uint32_t o1 = min(mad16<1>(I[i][j], c), zero_off);
-      v[2 * j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(s_cb) + o0);
-      v[2 * j + 1] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(s_cb) + o1);
+      const uint32_t o = min(h ? mad16<1>(I[i][j], c) : mad16<0>(I[i][j], c), zero_off);
+      v[j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(s_cb) + o);
     }
+  };
+  auto consume = [&](int i, int h, const uint4 (&v)[U]) {
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      acc[i] = dot8(v[2 * j], X[j][0], acc[i]);
-      acc[i] = dot8(v[2 * j + 1], X[j][1], acc[i]);
-    }
+    for (int j = 0; j < U; ++j) acc[i] = dot8(v[j], X[j][h], acc[i]);
+  };
+  // One pass over the 2 ROWS batches of rows 0 .. ROWS-1: batch b+1's reads
+  // are issued before batch b's dot products (two batches' vectors live,
+  // 8U registers).  In pass 0 (first) a row's first batch waits for that
+  // row's index loads only.
+  auto pass = [&](uint32_t c, auto first) {
+    constexpr bool kFirst = decltype(first)::value;
+    uint4 va[U], vb[U];
+    static_for<0, 2 * ROWS>([&](auto bc) {
+      constexpr int b = decltype(bc)::value;
+      constexpr int i = b / 2, h = b % 2;
+      constexpr int i1 = (b + 1) / 2, h1 = (b + 1) % 2;
+      constexpr int later1 = (ROWS - 1 - i1) * U;  // index loads issued after row i1
+      uint4(&cur)[U] = (b & 1) ? vb : va;
+      uint4(&nxt)[U] = (b & 1) ? va : vb;
+      sched_fence();
+      if constexpr (b == 0) {
+        if constexpr (kFirst) wait_vmem<((ROWS - 1) * U < 63 ? (ROWS - 1) * U : 63)>();
+        issue(0, 0, c, cur);
+      }
+      if constexpr (b + 1 < 2 * ROWS) {
+        if constexpr (kFirst && h1 == 0) wait_vmem<(later1 < 63 ? later1 : 63)>();
+        issue(i1, h1, c, nxt);
+      }
+      sched_fence();
+      consume(i, h, cur);
+    });
     sched_fence();
   };
 
@@ -235,28 +302,13 @@ __global__ __launch_bounds__(kCbsWaves * 64) void k_gemv_cbs(CbsArgs a) {
     // last are duplicates whose sums are dropped): guarded rows let the
     // compiler defer every row's dot products to a join block and keep all
     // the gathered vectors live.
-    static_for<0, ROWS>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      constexpr int later = (ROWS - 1 - i) * U;
-      wait_vmem<(later < 63 ? later : 63)>();
-      // the registers are not pass-invariant to the compiler: nothing
-      // computed from them is hoisted out of the pass loop
-#pragma unroll
-      for (int j = 0; j < U; ++j) asm volatile("" : "+v"(I[i][j]));
-      row_pass(i, 0u);
-    });
+    pass(0u, std::true_type{});
     for (int p = 1; p < a.passes; ++p) {
       __syncthreads();  // every wave is done with slice p - 1
       stage(p);
       wait_vmem<0>();
       __syncthreads();
-      const uint32_t c = 0u - 16u * (uint32_t)(p * a.slice);
-#pragma unroll
-      for (int i = 0; i < ROWS; ++i) {
-#pragma unroll
-        for (int j = 0; j < U; ++j) asm volatile("" : "+v"(I[i][j]));
-        row_pass(i, c);
-      }
+      pass(0u - 16u * (uint32_t)(p * a.slice), std::false_type{});
     }
     // Per row: the lane's sum times its rescale factor, reduced across the
     // wave in a fixed order; the K parts of a row are then added in order
@@ -289,6 +341,7 @@ __global__ __launch_bounds__(kCbsWaves * 64) void k_gemv_cbs(CbsArgs a) {
 // Rows per wave (index registers ROWS x U <= 112) for each pairs-per-lane U.
 template <int U> constexpr int cbs_rows() { return U <= 2 ? 32 : U == 8 ? 12 : 112 / U; }
 
+
 template <int U>
 void launch_u(const CbsArgs &a0, int cus, hipStream_t s) {
   CbsArgs a = a0;
@@ -298,6 +351,9 @@ void launch_u(const CbsArgs &a0, int cus, hipStream_t s) {
   a.per_wg = (a.n + grid - 1) / grid;
   hipLaunchKernelGGL((k_gemv_cbs<U, cbs_rows<U>()>), dim3(grid), dim3(kCbsWaves * 64), 0, s, a);
 }
+
+// Largest K whose fp32 copy fits the LDS for the in-kernel input transform.
+constexpr int kCbsMaxRhtK = 4 * kCbsMaxSlice;
 
 // Pairs per lane and K part for K = 1024 ppr: U divides ppr into 1, 2, 4 or
 // 8 K parts (8 waves), 4 preferred (x and indices both fit the registers
@@ -321,8 +377,11 @@ bool gemv_cbs_takes(const WView &w) {
   return cbs_pairs(w.k) != 0;
 }
 
-bool launch_gemv_cbs(const WView &w, const void *x, int xt, float *y, int cus, hipStream_t s) {
-  if (!gemv_cbs_takes(w)) return false;
+bool gemv_cbs_rht_takes(const WView &w) { return gemv_cbs_takes(w) && w.k <= kCbsMaxRhtK; }
+
+bool launch_gemv_cbs(const WView &w, const void *x, int xt, float *y, int cus, hipStream_t s, const int8_t *signs,
+                     int max_block) {
+  if (!(signs ? gemv_cbs_rht_takes(w) : gemv_cbs_takes(w))) return false;
   const int u = cbs_pairs(w.k);
   CbsArgs a{};
   a.idx = w.i16[0];
@@ -338,6 +397,8 @@ bool launch_gemv_cbs(const WView &w, const void *x, int xt, float *y, int cus, h
   a.slice = kCbsMaxSlice;
   a.passes = kCbsPasses;
   a.r0 = w.rs[0];
+  a.signs = signs;
+  a.mb = max_block;
   switch (u) {
     case 1: launch_u<1>(a, cus, s); break;
     case 2: launch_u<2>(a, cus, s); break;

@@ -45,37 +45,6 @@ template <int B1> constexpr int l2_batch() { return B1 == 16 ? 2 : 4; }
 // most units per lane that fit the register file without spills
 template <int B1> constexpr int l2_max_upl() { return B1 == 0 ? 16 : B1 == 8 ? 14 : 13; }
 
-// The input transform: signs (null: none) and the largest block.
-struct RhtIn {
-  const int8_t *signs;
-  int mb;
-};
-
-// In-place orthonormal FWHT of every block of s_x[0, K): K / mb blocks of
-// mb, then one block per set bit of K % mb, largest first.  Passes of up to
-// four stages, one barrier each; the blocks of mb are one flat loop over
-// their groups, the few remainder blocks one loop each.
-// s0: the first in-block bit left to transform (4 when the staging has done
-// bits 0..3).
-template <int NT>
-__device__ __forceinline__ void fwht_lds(float *s_x, int K, int mb, int tid, int s0) {
-  const int nfull = K / mb, rest = K % mb;
-  int maxbits = 0;
-  for (int p = mb; p > 1; p >>= 1) ++maxbits;
-  // passes at s0, s0 + 4, ...: a block's last pass takes its remaining 1..5
-  // bits (the loop stops at maxbits - 1 so a 5-bit remainder is one pass)
-  for (int s = s0; s < maxbits; s += (maxbits - s <= 5 ? 5 : 4)) {
-    __syncthreads();  // the previous pass (or the staging) is complete
-    fwht_pass<NT>(s_x, 0, nfull, maxbits, s, s0, tid);
-    int off = nfull * mb;
-    for (int bit = maxbits - 1; bit >= 0; --bit)  // uniform
-      if (rest & (1 << bit)) {
-        fwht_pass<NT>(s_x, off, 1, bit, s, s0, tid);
-        off += 1 << bit;
-      }
-  }
-}
-
 // B1: width of the residual stage (0: none, 8 or 16); RS: stage scales.
 template <int UPL, int B1, bool RS>
 __global__ __launch_bounds__(kL2Waves * 64) void k_gemv_l2(GemvArgs a, int xt, RhtIn rht) {

@@ -146,6 +146,20 @@ __device__ __forceinline__ void wait_vmem() {
 #endif
 }
 
+// Workgroup barrier for data in LDS: waits for this wave's LDS operations
+// (lgkmcnt 0), then meets the other waves; the memory clobber keeps the
+// compiler from moving memory accesses across it.  Unlike __syncthreads()
+// it does not wait for outstanding vector-memory loads (whose fence, with an
+// LDS-direct copy in flight, becomes a wait for every load of the wave): the
+// caller first waits (wait_vmem) for the LDS-direct copies that must have
+// landed, and loads issued after them, e.g. index rows from HBM, stay in
+// flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#endif
+}
+
 // Wait for every outstanding memory operation of the wave.
 __device__ __forceinline__ void wait_all_memory() {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -418,6 +432,37 @@ __device__ __forceinline__ void fwht_pass(float *s_x, int off, int count, int lb
       case 2: fwht_group<4>(s_x, base, s, sc); break;
       default: fwht_group<2>(s_x, base, s, sc); break;
     }
+  }
+}
+
+// The input transform: signs (null: none) and the largest block.
+struct RhtIn {
+  const int8_t *signs;
+  int mb;
+};
+
+// In-place orthonormal FWHT of every block of s_x[0, K): K / mb blocks of
+// mb, then one block per set bit of K % mb, largest first.  Passes of up to
+// four stages, one barrier each; the blocks of mb are one flat loop over
+// their groups, the few remainder blocks one loop each.
+// s0: the first in-block bit left to transform (4 when the staging has done
+// bits 0..3).
+template <int NT>
+__device__ __forceinline__ void fwht_lds(float *s_x, int K, int mb, int tid, int s0) {
+  const int nfull = K / mb, rest = K % mb;
+  int maxbits = 0;
+  for (int p = mb; p > 1; p >>= 1) ++maxbits;
+  // passes at s0, s0 + 4, ...: a block's last pass takes its remaining 1..5
+  // bits (the loop stops at maxbits - 1 so a 5-bit remainder is one pass)
+  for (int s = s0; s < maxbits; s += (maxbits - s <= 5 ? 5 : 4)) {
+    __syncthreads();  // the previous pass (or the staging) is complete
+    fwht_pass<NT>(s_x, 0, nfull, maxbits, s, s0, tid);
+    int off = nfull * mb;
+    for (int bit = maxbits - 1; bit >= 0; --bit)  // uniform
+      if (rest & (1 << bit)) {
+        fwht_pass<NT>(s_x, off, 1, bit, s, s0, tid);
+        off += 1 << bit;
+      }
   }
 }
 

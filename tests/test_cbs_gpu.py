@@ -117,3 +117,25 @@ def test_cbs_gemv_deterministic(vq):
     a = vq.vq_gemv(w, x).cpu().numpy()
     b = vq.vq_gemv(w, x).cpu().numpy()
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# (N, K, x dtype, largest transform block): the input transform inside the
+# sliced kernel (vq_gemv_rht): blocks of 8192 as in the 70B-MLP workload,
+# greedy blocks of a non-power-of-two K (28672 -> 8192 x 3 + 4096), small
+# blocks (16, below the 16-element register staging; 1: signs only)
+RHT_CASES = [(28672, 8192, "bf16", 8192), (8192, 28672, "bf16", 8192), (4096, 16384, "f32", 16384),
+             (8192, 8192, "bf16", 16), (4096, 8192, "f32", 1), (33000, 2048, "bf16", 512)]
+
+
+@pytest.mark.parametrize("n,k,xdt,mb", RHT_CASES)
+def test_cbs_gemv_rht(vq, n, k, xdt, mb):
+    import torch
+    print(f"cbs rht {n}x{k} {xdt} mb={mb}", flush=True)
+    sw = vqsynth.random_weight(n, k, 1, 16, None, seed=n + k + mb)
+    xs, x64 = vqsynth.make_x(2, k, xdt, np.random.SeedSequence(k + mb))
+    signs = vqsynth.make_signs(k, np.random.SeedSequence(mb + 3))
+    y = vq.vq_gemv_rht(device_weight(sw), x_to_device(xs, xdt), torch.from_numpy(signs).cuda(), mb)
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set(sample_rows(n, 48, mb).tolist()) | block_edges(n)))
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw, rows), oracle.rht_ref(x64, signs, mb))
+    assert_within(y.cpu().numpy()[:, rows], y_ref, bound, f"rht {n}x{k} {xdt} mb={mb}")
