@@ -3,6 +3,8 @@
 // k_gemm_ladder.hip: mixed-width ladders and stage scales).
 #pragma once
 
+#include <type_traits>
+
 #include "vqmm_device.h"
 #include "vqmm_internal.h"
 
@@ -24,6 +26,10 @@ struct GemmArgs {
   float rs[VQ_MAX_STAGES];   // stage scales
   int cboff[VQ_MAX_STAGES];  // first LDS codebook row of each stage (BITS = 0 kernels)
   int cbrows;                // codebook rows of all stages
+  // fp16 path of the 256-token tile kernels (null xh: the bf16 path):
+  const uint16_t *xh;  // x as fp16 in A-fragment order (k_x_f16), m_pad tokens
+  const float *xf;     // [m_pad] per-token factors undoing the rescale of xh
+  int m_pad;           // tokens rounded up to 16
 };
 
 // LDS codebook rows of the BITS = 0 (per-stage widths) kernels: 128 KiB.
@@ -172,6 +178,49 @@ __device__ __forceinline__ uint4 group_to_bf16_scaled(const uint4 (&v)[S], float
   pk.z = pack_bf16(sf * w[4], sf * w[5]);
   pk.w = pack_bf16(sf * w[6], sf * w[7]);
   return pk;
+}
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// 8 weights of one group as fp16 for the fp16 matrix-core path: c0 s with
+// one stage, (c0 + c1) s with two, in packed-half arithmetic (v_pk_add_f16,
+// v_pk_mul_f16), each operation rounded once to nearest even.  The sum is
+// rounded relative to itself and then the product, so |w16 - w| <= (2^-10 +
+// 2^-22) |w| for every weight (subnormal results aside: absolute error at
+// most 2^-25), where bf16 weights carry up to 2^-8 |w|.  sc16: fp16 bits of
+// the block scale.
+template <int S>
+__device__ __forceinline__ uint4 group_to_f16(const uint4 (&v)[S], uint32_t sc16) {
+  static_assert(S == 1 || S == 2, "one or two stages");
+  const half2_t s2 = as_h2(sc16 | (sc16 << 16));
+  auto pair = [&](uint32_t c0, uint32_t c1) -> uint32_t {
+    const half2_t w = S == 1 ? as_h2(c0) : as_h2(c0) + as_h2(c1);
+    return __builtin_bit_cast(uint32_t, w * s2);
+  };
+  return make_uint4(pair(v[0].x, v[S - 1].x), pair(v[0].y, v[S - 1].y), pair(v[0].z, v[S - 1].z),
+                    pair(v[0].w, v[S - 1].w));
+}
+
+// The same with stage scales: s sum_t r_t c_t in fp32 (summation from stage
+// 0), rounded once to fp16.
+template <int S>
+__device__ __forceinline__ uint4 group_to_f16_scaled(const uint4 (&v)[S], float sf, const float *rs) {
+  float w[8];
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    const uint32_t ht[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float c0 = h2f(ht[e] & 0xffffu) * rs[t], c1 = h2f(ht[e] >> 16) * rs[t];
+      w[2 * e] = t == 0 ? c0 : w[2 * e] + c0;
+      w[2 * e + 1] = t == 0 ? c1 : w[2 * e + 1] + c1;
+    }
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    o[e] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)(sf * w[2 * e]), (_Float16)(sf * w[2 * e + 1])});
+  return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // Everything one thread needs from global memory for one K step (4 groups,
@@ -501,6 +550,23 @@ struct XStep {
   uint32_t sc;
 };
 
+// fp16 path: multiply each accumulator by its token's factor (the inverse
+// of the power-of-two rescale of that token's x), acc[i][j][r] belonging to
+// token m0 + 64 wave + 16 i + 4 (lane / 16) + r.
+template <int NJ>
+__device__ __forceinline__ void token_factors(const GemmArgs &a, int m0, int wave, int lane, f32x4 (&acc)[4][NJ]) {
+  const buf_t bf = make_buf(a.xf, 4u * (uint32_t)a.m_pad);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t tok = (uint32_t)min(m0 + wave * 64 + 16 * i + 4 * (lane >> 4) + r, a.m_pad - 1);
+      const float f = __uint_as_float(buf_u32(bf, 4u * tok, 0));
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j][r] *= f;
+    }
+}
+
 // Tile 256 (tokens) x 128 (W rows), K step 32, 4 waves stacked along the
 // tokens, each owning 64 x 128 as 4 x 8 blocks of v_mfma_f32_16x16x32_bf16
 // (lane l of an A fragment holds 8 consecutive k of token l % 16, so each x
@@ -513,9 +579,10 @@ struct XStep {
 // iteration earlier) with the decode of step k+2, loads step k+4, then the
 // barrier.  The tile written in iteration k holds step k-1, whose fragments
 // were read in iteration k-2.
-template <class LD, bool RS>
+template <class LD, bool RS, bool F16 = false>
 __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
   constexpr int S = LD::S;
+  using frag_t = typename std::conditional<F16, f16x8_t, bf16x8_t>::type;
   __shared__ uint4 s_cb[LD::kRows];
   __shared__ __attribute__((aligned(16))) uint16_t s_w[3][kLN * kWP];
   const int tid = threadIdx.x;
@@ -550,17 +617,24 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
     bhi[t] = make_buf(LD::hi(t) ? a.hi[t] : a.lo[t], LD::hi(t) ? (ng + 1) / 2 : ng);
   }
   const buf_t bsc = make_buf(a.sc, 2u * a.n * a.nblk);
-  const buf_t bx = make_buf(a.x, 2u * a.m * a.k);
+  const buf_t bx = F16 ? make_buf(a.xh, 2u * (uint32_t)a.m_pad * (uint32_t)a.k) : make_buf(a.x, 2u * a.m * a.k);
   const uint32_t vlo = (uint32_t)wrow_c * a.G;  // + 16 per quad
   const uint32_t vhi = vlo >> 1;                // + 8 per quad (G is even)
   const uint32_t vsc = 2u * wrow_c * a.nblk;
   // x byte offsets of this lane's token (one per 16-token block) and k chunk;
   // tokens past m load token m-1 and feed rows that are never stored
+  // (fp16 path: the lane's 16 bytes of its token block's 1 KiB fragment
+  // per K step; blocks past m_pad load the last one)
   uint32_t va[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = min(m0 + wave * 64 + 16 * i + (lane & 15), a.m - 1);
-    va[i] = 2u * ((uint32_t)r * a.k + 8 * (lane >> 4));
+    if (F16) {
+      const uint32_t tb = (uint32_t)min(m0 + wave * 64 + 16 * i, a.m_pad - 16) / 16u;
+      va[i] = 16u * (tb * (uint32_t)(a.k / 32) * 64u + (uint32_t)lane);
+    } else {
+      const int r = min(m0 + wave * 64 + 16 * i + (lane & 15), a.m - 1);
+      va[i] = 2u * ((uint32_t)r * a.k + 8 * (lane >> 4));
+    }
   }
 
   f32x4 acc[4][8];
@@ -584,7 +658,7 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
   auto load_x = [&](int ks, XStep &X) {
     ks = min(ks, nks - 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) X.av[i] = buf_u128(bx, va[i], 64u * ks);
+    for (int i = 0; i < 4; ++i) X.av[i] = buf_u128(bx, va[i], (F16 ? 1024u : 64u) * ks);
     const uint32_t blk = (uint32_t)(((uint64_t)ks * a.smagic) >> 32);  // (32 ks) / scale_block
     X.sc = buf_u16(bsc, vsc, 2u * blk);
   };
@@ -608,26 +682,30 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
       for (int t = 0; t < S; ++t) v[u][t] = s_cb[LD::off(t) + idx_of(Q, s, u, t)];
   };
   auto decode = [&](int u, const uint4 (&v)[S], uint32_t sc, uint16_t *wt) {
-    const uint4 pk = RS ? group_to_bf16_scaled<S>(v, h2f(sc), a.rs) : group_to_bf16<S>(v, h2f(sc));
+    uint4 pk;
+    if constexpr (F16) pk = RS ? group_to_f16_scaled<S>(v, h2f(sc), a.rs) : group_to_f16<S>(v, sc);
+    else pk = RS ? group_to_bf16_scaled<S>(v, h2f(sc), a.rs) : group_to_bf16<S>(v, h2f(sc));
     *reinterpret_cast<uint4 *>(&wt[drow * kWP + 8 * (dg + u)]) = pk;
   };
-  auto read_b = [&](const uint16_t *wr, bf16x8_t (&bfr)[8]) {
+  auto read_b = [&](const uint16_t *wr, frag_t (&bfr)[8]) {
 #pragma unroll
     for (int jn = 0; jn < 8; ++jn)
-      bfr[jn] = *reinterpret_cast<const bf16x8_t *>(&wr[(16 * jn + (lane & 15)) * kWP + 8 * (lane >> 4)]);
+      bfr[jn] = *reinterpret_cast<const frag_t *>(&wr[(16 * jn + (lane & 15)) * kWP + 8 * (lane >> 4)]);
   };
-  auto mma8 = [&](const XStep &X, const bf16x8_t (&bfr)[8], int i) {
-    const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, X.av[i]);
+  auto mma8 = [&](const XStep &X, const frag_t (&bfr)[8], int i) {
+    const frag_t afr = __builtin_bit_cast(frag_t, X.av[i]);
 #pragma unroll
-    for (int jn = 0; jn < 8; ++jn)
-      acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[jn], acc[i][jn], 0, 0, 0);
+    for (int jn = 0; jn < 8; ++jn) {
+      if constexpr (F16) acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, bfr[jn], acc[i][jn], 0, 0, 0);
+      else acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[jn], acc[i][jn], 0, 0, 0);
+    }
   };
   // Iteration ks: B fragments of step ks+1 into Bn (tile (ks+1) % 3), MFMAs
   // of step ks (Xm, Bc), decode of step ks+2 (codebook vectors in v, gathered
   // one iteration earlier; scale in Xd) into tile (ks+2) % 3, gathers of step
   // ks+3 (quad Qg, step sg) into v, loads of step ks+4 into Xm (and, when
   // ks % 4 == 2, of quad (ks+6)/4 into Qn), barrier.
-  auto iter = [&](int ks, XStep &Xm, const XStep &Xd, const bf16x8_t (&Bc)[8], bf16x8_t (&Bn)[8],
+  auto iter = [&](int ks, XStep &Xm, const XStep &Xd, const frag_t (&Bc)[8], frag_t (&Bn)[8],
                   const Quad<S> &Qg, int sg, Quad<S> &Qn, bool quad_load, uint4 (&v)[2][S]) {
     uint16_t *ww = s_w[(ks + 2) % 3];
     read_b(s_w[(ks + 1) % 3], Bn);
@@ -671,7 +749,7 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
   decode(1, v[1], X1.sc, s_w[1]);
   gather(Q0, 2, v);  // step 2, decoded in iteration 0
   __syncthreads();
-  bf16x8_t B0[8], B1[8];
+  frag_t B0[8], B1[8];
   read_b(s_w[0], B0);
   // eight steps (two quads) per trip; the three W tiles rotate with ks % 3
   // (compile-time inside the trip only when 3 divides the trip length, so the
@@ -689,6 +767,7 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
     iter(ks + 6, X2, X0, B0, B1, Q0, 1, Q1, true, v);   // quad (ks+12)/4 -> Q1
     iter(ks + 7, X3, X1, B1, B0, Q0, 2, Q1, false, v);
   }
+  if constexpr (F16) token_factors(a, m0, wave, lane, acc);
   // tiles wholly inside y: descriptor stores as in the wide kernel
   if (m0 + kLM <= a.m && n0 + kLN <= a.n && (uint64_t)kLM * a.n * 4 < (1u << 31)) {
     const buf_t by = make_buf(a.y + (size_t)m0 * a.n + n0, (uint32_t)kLM * (uint32_t)a.n * 4u);
@@ -732,6 +811,13 @@ __device__ __forceinline__ void mfma_tied(f32x4 &acc, const bf16x8_t &a, const b
   (void)acc, (void)a, (void)b;
 #endif
 }
+__device__ __forceinline__ void mfma_tied(f32x4 &acc, const f16x8_t &a, const f16x8_t &b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+#else
+  (void)acc, (void)a, (void)b;
+#endif
+}
 
 // Tile 256 (tokens) x 256 (W rows), K step 32, 4 waves stacked along the
 // tokens, each owning 64 x 256 as 4 x 16 blocks of v_mfma_f32_16x16x32_bf16:
@@ -743,9 +829,10 @@ __device__ __forceinline__ void mfma_tied(f32x4 &acc, const bf16x8_t &a, const b
 // of tile k & 1 in two halves, issues the gathers of step k+1, interleaves
 // the 64 MFMAs of step k with the decode of step k+1 into the other tile,
 // loads step k+4, one barrier.
-template <class LD, bool RS>
+template <class LD, bool RS, bool F16 = false>
 __global__ __launch_bounds__(256) void k_gemm_wide(GemmArgs a) {
   constexpr int S = LD::S;
+  using frag_t = typename std::conditional<F16, f16x8_t, bf16x8_t>::type;
   __shared__ uint4 s_cb[LD::kRows];
   __shared__ __attribute__((aligned(16))) uint4 s_w[2][kWN * 4];
   const int tid = threadIdx.x;
@@ -778,15 +865,22 @@ __global__ __launch_bounds__(256) void k_gemm_wide(GemmArgs a) {
     bhi[t] = make_buf(LD::hi(t) ? a.hi[t] : a.lo[t], LD::hi(t) ? (ng + 1) / 2 : ng);
   }
   const buf_t bsc = make_buf(a.sc, 2u * a.n * a.nblk);
-  const buf_t bx = make_buf(a.x, 2u * a.m * a.k);
+  const buf_t bx = F16 ? make_buf(a.xh, 2u * (uint32_t)a.m_pad * (uint32_t)a.k) : make_buf(a.x, 2u * a.m * a.k);
   const uint32_t vlo = (uint32_t)wrow_c * a.G;
   const uint32_t vhi = vlo >> 1;
   const uint32_t vsc = 2u * wrow_c * a.nblk;
+  // (fp16 path: the lane's 16 bytes of its token block's 1 KiB fragment
+  // per K step; blocks past m_pad load the last one)
   uint32_t va[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = min(m0 + wave * 64 + 16 * i + (lane & 15), a.m - 1);
-    va[i] = 2u * ((uint32_t)r * a.k + 8 * (lane >> 4));
+    if (F16) {
+      const uint32_t tb = (uint32_t)min(m0 + wave * 64 + 16 * i, a.m_pad - 16) / 16u;
+      va[i] = 16u * (tb * (uint32_t)(a.k / 32) * 64u + (uint32_t)lane);
+    } else {
+      const int r = min(m0 + wave * 64 + 16 * i + (lane & 15), a.m - 1);
+      va[i] = 2u * ((uint32_t)r * a.k + 8 * (lane >> 4));
+    }
   }
   // swizzled chunk position of chunk c of tile row r
   auto wpos = [](int r, int c) { return 4 * r + (c ^ ((r >> 2) & 3)); };
@@ -810,7 +904,7 @@ __global__ __launch_bounds__(256) void k_gemm_wide(GemmArgs a) {
   auto load_x = [&](int ks, XStep &X) {
     ks = min(ks, nks - 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) X.av[i] = buf_u128(bx, va[i], 64u * ks);
+    for (int i = 0; i < 4; ++i) X.av[i] = buf_u128(bx, va[i], (F16 ? 1024u : 64u) * ks);
     const uint32_t blk = (uint32_t)(((uint64_t)ks * a.smagic) >> 32);
     X.sc = buf_u16(bsc, vsc, 2u * blk);
   };
@@ -837,19 +931,20 @@ __global__ __launch_bounds__(256) void k_gemm_wide(GemmArgs a) {
     for (int g = 0; g < 4; ++g) gather1(Q, s, g, v[g]);
   };
   auto decode = [&](int g, const uint4 (&v)[S], uint32_t sc, uint4 *wt) {
-    wt[wpos(tid, g)] = RS ? group_to_bf16_scaled<S>(v, h2f(sc), a.rs) : group_to_bf16<S>(v, h2f(sc));
+    if constexpr (F16) wt[wpos(tid, g)] = RS ? group_to_f16_scaled<S>(v, h2f(sc), a.rs) : group_to_f16<S>(v, sc);
+    else wt[wpos(tid, g)] = RS ? group_to_bf16_scaled<S>(v, h2f(sc), a.rs) : group_to_bf16<S>(v, h2f(sc));
   };
-  auto read_b2 = [&](const uint4 *wr, int half, int j0, bf16x8_t (&bfr)[8]) {
+  auto read_b2 = [&](const uint4 *wr, int half, int j0, frag_t (&bfr)[8]) {
 #pragma unroll
     for (int j = j0; j < j0 + 2; ++j)
-      bfr[j] = __builtin_bit_cast(bf16x8_t, wr[wpos(16 * (8 * half + j) + (lane & 15), lane >> 4)]);
+      bfr[j] = __builtin_bit_cast(frag_t, wr[wpos(16 * (8 * half + j) + (lane & 15), lane >> 4)]);
   };
-  auto read_b = [&](const uint4 *wr, int half, bf16x8_t (&bfr)[8]) {
+  auto read_b = [&](const uint4 *wr, int half, frag_t (&bfr)[8]) {
 #pragma unroll
     for (int j = 0; j < 8; j += 2) read_b2(wr, half, j, bfr);
   };
-  auto mma = [&](const XStep &X, const bf16x8_t (&bfr)[8], int half, int i) {
-    const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, X.av[i]);
+  auto mma = [&](const XStep &X, const frag_t (&bfr)[8], int half, int i) {
+    const frag_t afr = __builtin_bit_cast(frag_t, X.av[i]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) mfma_tied(acc[i][8 * half + j], afr, bfr[j]);
   };
@@ -868,7 +963,7 @@ __global__ __launch_bounds__(256) void k_gemm_wide(GemmArgs a) {
   // more LDS reads in flight than the 15 the counter tracks and the MFMAs
   // start at once.
   auto iter = [&](int ks, const XStep &Xm, const XStep &Xd, XStep &Xl, const Quad<S> &Qg, int sg, Quad<S> &Qn,
-                  bool quad_load, bf16x8_t (&BA)[8], bf16x8_t (&BB)[8], uint4 (&v)[4][S]) {
+                  bool quad_load, frag_t (&BA)[8], frag_t (&BB)[8], uint4 (&v)[4][S]) {
     const uint4 *wr = s_w[ks & 1];
     uint4 *ww = s_w[(ks + 1) & 1];
     read_b(wr, 1, BB);
@@ -914,7 +1009,7 @@ __global__ __launch_bounds__(256) void k_gemm_wide(GemmArgs a) {
   for (int g = 0; g < 4; ++g) decode(g, v[g], X0.sc, s_w[0]);
   gather(Q0, 1, v);
   __syncthreads();
-  bf16x8_t BA[8], BB[8];
+  frag_t BA[8], BB[8];
   read_b(s_w[0], 0, BA);
   // eight steps (two quads) per trip: iteration ks gathers step ks+2, so quad
   // Q0 (steps ks..ks+3) is last gathered in iteration ks+1 and refilled in
@@ -953,6 +1048,7 @@ __global__ __launch_bounds__(256) void k_gemm_wide(GemmArgs a) {
                    "+a"(acc[i][13]), "+a"(acc[i][14]), "+a"(acc[i][15]));
   }
 #endif
+  if constexpr (F16) token_factors(a, m0, wave, lane, acc);
   // Tiles lying wholly inside y (every row < m, every column < n) store
   // through a descriptor based at the tile's first element without per-store
   // tests: the lane's offset is fixed, rows step by a scalar offset, columns
@@ -1503,7 +1599,8 @@ static bool launch_few(const GemmArgs &a, hipStream_t s) {
 
 // The 256 x 256 (wide) or 256 x 128 (tile) kernel for many tokens when the
 // shape allows it (K % 256 == 0, scale blocks of whole K steps, K < 2^20);
-// false: nothing launched.  `a` has tiles_m / tiles_n / per_xcd of the
+// false: nothing launched.  With a.xh set (one or two stages) the fp16
+// variants run on x converted by k_x_f16.  `a` has tiles_m / tiles_n / per_xcd of the
 // 256 x 128 tiling.
 template <class LD, bool RS>
 static bool launch_tiles(const GemmArgs &a, hipStream_t s) {
@@ -1516,7 +1613,19 @@ static bool launch_tiles(const GemmArgs &a, hipStream_t s) {
       GemmArgs w = a;
       w.tiles_n = (a.n + kWN - 1) / kWN;
       w.per_xcd = (w.tiles_m * w.tiles_n + 7) / 8;
+      if constexpr (LD::S <= 2) {
+        if (w.xh) {
+          hipLaunchKernelGGL((k_gemm_wide<LD, RS, true>), dim3(8 * w.per_xcd), dim3(256), 0, s, w);
+          return true;
+        }
+      }
       hipLaunchKernelGGL((k_gemm_wide<LD, RS>), dim3(8 * w.per_xcd), dim3(256), 0, s, w);
+      return true;
+    }
+  }
+  if constexpr (LD::S <= 2) {
+    if (a.xh) {
+      hipLaunchKernelGGL((k_gemm_tile<LD, RS, true>), dim3(8 * a.per_xcd), dim3(256), 0, s, a);
       return true;
     }
   }

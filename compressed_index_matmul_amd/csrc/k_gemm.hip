@@ -115,16 +115,97 @@ static void launch_gemm_ladder(const WView &w, const GemmArgs &a, hipStream_t s)
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp16 path of the 256-token tile kernels
+// ---------------------------------------------------------------------------
+// x (bf16 [m][k]) -> fp16 after a power-of-two rescale per token that puts
+// the token's largest |x| in [2^14, 2^15) (every value within 2^28 of it is
+// then exact), written in the A-fragment order of the 16x16x32 kernels:
+// token block b (16 tokens), K step s (32 columns), lane l: 16 bytes at
+// ((b (k/32) + s) 64 + l) 16 holding token 16 b + l % 16, columns 32 s +
+// 8 (l / 16) .. + 8, so a wave's fragment is one contiguous 1 KiB.  Tokens
+// m .. m_pad - 1 are zero.  xf[token] = 2^-e undoes the rescale.  One wave
+// per token: the row's largest |x| (fixed-order wave reduction), then the
+// conversion (the row is read twice; the second read hits in L2).
+__global__ __launch_bounds__(256) void k_x_f16(const uint16_t *x, int m, int m_pad, int k, uint16_t *xh,
+                                               float *xf) {
+  const int lane = threadIdx.x & 63;
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);  // wave-uniform
+  if (tok >= m_pad) return;
+  const int chunks = k / 8;  // 8 columns per 16-byte chunk
+  const uint4 *row = reinterpret_cast<const uint4 *>(x + (size_t)min(tok, m - 1) * k);
+  float mx = 0.f;
+  if (tok < m) {
+    for (int c = lane; c < chunks; c += 64) {
+      const uint4 v = row[c];
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(fabsf(bf2f(w4[e] & 0xffffu)), fabsf(bf2f(w4[e] >> 16))));
+    }
+  }
+  // fixed-order maximum over the wave (maxima are exact in any order)
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const int e = (mx > 0.f && mx <= 3.0e38f) ? 14 - ilogbf(mx) : 0;
+  if (lane == 0) xf[tok] = ldexpf(1.f, -e);
+  const size_t steps = (size_t)k / 32;
+  const size_t blk = (size_t)(tok / 16) * steps * 64 + (tok % 16);
+  uint4 *out = reinterpret_cast<uint4 *>(xh);
+  for (int c = lane; c < chunks; c += 64) {
+    uint4 o = make_uint4(0u, 0u, 0u, 0u);
+    if (tok < m) {
+      const uint4 v = row[c];
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+      uint32_t h[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        h[q] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)ldexpf(bf2f(w4[q] & 0xffffu), e),
+                                                  (_Float16)ldexpf(bf2f(w4[q] >> 16), e)});
+      o = make_uint4(h[0], h[1], h[2], h[3]);
+    }
+    out[blk + ((size_t)(c / 4) * 64 + 16 * (c % 4))] = o;
+  }
+}
+
+namespace {
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Formats with a 256-token tile kernel of one or two stages (the fp16
+// variants exist for these): 8/12-bit one stage, 12+12, 8+8, 12+4, 8+4, with
+// or without stage scales.
+bool tile_f16_format(const WView &w) {
+  if (w.S == 1) return w.sb[0] == 8 || w.sb[0] == 12;
+  if (w.S != 2) return false;
+  const int b0 = w.sb[0], b1 = w.sb[1];
+  return (b0 == 12 && (b1 == 12 || b1 == 4)) || (b0 == 8 && (b1 == 8 || b1 == 4));
+}
+
+}  // namespace
+
+// The fp16 tile path: more tokens than the few-token kernel takes, a shape
+// the tile kernels take, a format with an fp16 variant.
+bool gemm_f16_takes(const WView &w, int m) {
+  return m > 64 && w.k % 256 == 0 && w.bs % 32 == 0 && w.k < (1 << 20) && tile_f16_format(w);
+}
+
 size_t gemm_workspace_bytes(const WView &w, int m) {
-  (void)w;
-  (void)m;
-  return 0;  // no kernel of the many-token product keeps scratch
+  if (!gemm_f16_takes(w, m)) return 0;
+  const size_t m_pad = ((size_t)m + 15) & ~(size_t)15;
+  return align256(m_pad * (size_t)w.k * 2) + align256(m_pad * 4);
 }
 
 hipError_t launch_gemm(const WView &w, const uint16_t *x, int m, float *y, void *ws, size_t ws_bytes, hipStream_t s) {
-  (void)ws;
-  (void)ws_bytes;
-  const GemmArgs a = make_gemm_args(w, x, m, y);
+  GemmArgs a = make_gemm_args(w, x, m, y);
+  if (gemm_f16_takes(w, m) && ws && ws_bytes >= gemm_workspace_bytes(w, m)) {
+    const int m_pad = (m + 15) & ~15;
+    uint16_t *xh = static_cast<uint16_t *>(ws);
+    float *xf = reinterpret_cast<float *>(static_cast<char *>(ws) + align256((size_t)m_pad * w.k * 2));
+    hipLaunchKernelGGL(k_x_f16, dim3(m_pad / 4), dim3(256), 0, s, x, m, m_pad, w.k, xh, xf);
+    a.xh = xh;
+    a.xf = xf;
+    a.m_pad = m_pad;
+  }
   if (!plain_format(w)) {
     if (launch_gemm_ladder_lds(w, a, s)) return hipGetLastError();
     bool fits = a.cbrows <= kLadderCbRows;

@@ -184,8 +184,19 @@ int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, f
 
 /*
  * Many-token product y = x dequant(W)^T (GLQ page, "Inference kernels":
- * tensor-core path for batched inputs).  Decoded weight tiles are rounded to
- * bf16 on chip and multiplied on bf16 matrix cores with fp32 accumulation.
+ * tensor-core path for batched inputs).  Decoded weight tiles are rounded on
+ * chip to a 16-bit type and multiplied on matrix cores with fp32
+ * accumulation.  Two paths:
+ *  - fp16 (more than 64 tokens, k_in % 256 == 0, block_size % 32 == 0, one
+ *    stage of 8 or 12 bits or two stages 12+12, 12+4, 8+8, 8+4): x is first
+ *    converted into the workspace to fp16 after a power-of-two rescale per
+ *    token (exact for every value within 2^28 of the token's largest |x|,
+ *    smaller ones off by at most 2^-39 of it), each weight is rounded to
+ *    fp16 (relative error <= 2^-10 + 2^-22), and the bound is |y - y_exact|
+ *    <= (2^-10 + 2^-22 + k_in 2^-24) sum_k |w x| + 1e-6, inside
+ *    2e-3 * sum_k |w x| + 1e-6 for any x when k_in <= 16384;
+ *  - bf16 (every other call, including all calls with 64 tokens or fewer):
+ *    see the bound below.
  *   x         : bf16 bits [m][k_in];  m >= 1
  *   y         : float [m][n_out]
  *   workspace : device scratch of ws_bytes bytes owned by the caller, 16-byte
@@ -197,6 +208,7 @@ int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, f
  *               keeps split-K partials in such a scratch buffer so that the
  *               reduction order stays fixed); two calls in flight at the same
  *               time need two workspaces.
+ * On the bf16 path x is used as given and the workspace is not touched.
  * bf16 keeps 8 significant bits, so each weight carries a relative error of
  * up to 2^-8: the guaranteed bound is |y - y_exact| <= (2^-8 + 2^-23 +
  * k_in 2^-24) sum_k |w x| + 1e-6.  For dense activations the rounding errors
