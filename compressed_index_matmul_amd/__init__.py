@@ -10,7 +10,8 @@ Entry points (same names as the C ABI):
 * :func:`vq_unpack_dequant` -- unpacked indices and/or the fp16 dense weight
 * :func:`vq_gemv`           -- y = x dequant(W)^T for 1..16 tokens
 * :func:`vq_gemm`           -- the same for many bf16 tokens on matrix cores
-  (with :func:`vq_gemm_workspace_size` for its caller-owned scratch)
+  (with :func:`vq_gemm_workspace_size` for its caller-owned scratch;
+  :func:`vq_gemm_noalloc` uses the library's static scratch instead)
 * :func:`rht_apply`         -- randomized Hadamard transform of activations
 * :func:`vq_gemv_rht`       -- vq_gemv with the input transform inside the kernel
 * :func:`vq_compressed_bytes`, :func:`vq_validate`, :func:`vq_version`
@@ -32,15 +33,16 @@ import numpy as np
 
 __all__ = [
     "VQError", "VQWeight", "lib", "LIB_PATH", "vq_version", "vq_validate", "vq_compressed_bytes",
-    "vq_unpack_dequant", "vq_gemv", "vq_gemm", "vq_gemm_workspace_size", "rht_apply", "vq_gemv_rht", "VQ_F32",
-    "VQ_BF16", "VQ_STAGE_SCALES", "EXPORTS",
+    "vq_unpack_dequant", "vq_gemv", "vq_gemm", "vq_gemm_workspace_size", "vq_gemm_noalloc", "rht_apply",
+    "vq_gemv_rht", "VQ_F32", "VQ_BF16", "VQ_STAGE_SCALES", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvqmm.so")
 VQ_F32, VQ_BF16 = 0, 1
 MAX_STAGES = 4
 EXPORTS = ("vq_version", "vq_status_string", "vq_validate", "vq_compressed_bytes",
-           "vq_unpack_dequant", "vq_gemv", "vq_gemm", "vq_gemm_workspace_size", "rht_apply", "vq_gemv_rht")
+           "vq_unpack_dequant", "vq_gemv", "vq_gemm", "vq_gemm_workspace_size", "vq_gemm_noalloc", "rht_apply",
+           "vq_gemv_rht")
 
 _ptr4 = ctypes.c_void_p * MAX_STAGES
 _int4 = ctypes.c_int32 * MAX_STAGES
@@ -101,6 +103,7 @@ def lib() -> ctypes.CDLL:
         L.vq_gemm.argtypes, L.vq_gemm.restype = [D, P, ctypes.c_int32, P, P, ctypes.c_size_t, P], ctypes.c_int
         L.vq_gemm_workspace_size.argtypes = [D, ctypes.c_int32]
         L.vq_gemm_workspace_size.restype = ctypes.c_size_t
+        L.vq_gemm_noalloc.argtypes, L.vq_gemm_noalloc.restype = [D, P, ctypes.c_int32, P, P], ctypes.c_int
         L.rht_apply.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P, P]
         L.rht_apply.restype = ctypes.c_int
         L.vq_gemv_rht.argtypes = [D, P, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P, P]
@@ -390,6 +393,25 @@ def vq_gemm(w: VQWeight, x, y=None, workspace=None, stream=None):
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().vq_gemm(w.ref(), x.data_ptr(), m, y.data_ptr(), ws_ptr, ws_bytes, _stream_handle(stream)),
            "vq_gemm")
+    return y
+
+
+def vq_gemm_noalloc(w: VQWeight, x, y, stream=None):
+    """vq_gemm without a workspace: the library's static scratch serves the
+    call (at most VQ_GEMM_NOALLOC_SCRATCH bytes; VQError otherwise).  x:
+    bfloat16 [M, K], y: float32 [M, N], both on the weight's GPU -- the
+    caller provides y, nothing is allocated."""
+    import torch
+    dev = _weight_device(w)
+    x = _tokens(x, w.k_in)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("vq_gemm_noalloc takes bfloat16 activations")
+    _on_gpu(x, dev, "x")
+    m = x.shape[0]
+    if y is None:
+        raise ValueError("vq_gemm_noalloc allocates nothing: pass y")
+    y = _out(y, (m, w.n_out), dev)
+    _check(lib().vq_gemm_noalloc(w.ref(), x.data_ptr(), m, y.data_ptr(), _stream_handle(stream)), "vq_gemm_noalloc")
     return y
 
 

@@ -25,6 +25,8 @@
 // (every stage of one width, no stage scales) and the general path of
 // residual ladders; ladders with tuned instantiations are dispatched from
 // k_gemm_ladder.hip first.
+#include <mutex>
+
 #include "gemm_kernels.h"
 
 namespace vqmm {
@@ -193,6 +195,39 @@ size_t gemm_workspace_bytes(const WView &w, int m) {
   if (!gemm_f16_takes(w, m)) return 0;
   const size_t m_pad = ((size_t)m + 15) & ~(size_t)15;
   return align256(m_pad * (size_t)w.k * 2) + align256(m_pad * 4);
+}
+
+// ---------------------------------------------------------------------------
+// The product without caller workspace (vq_gemm_noalloc): the scratch the
+// fp16 path needs lives in a static device array, one per GPU, held until
+// the process ends.  Host code never passes the array's name to a kernel
+// (in host code it stands for a host-side shadow, not a device address): its
+// device address is looked up once per device with hipGetSymbolAddress and
+// that pointer is what the kernels get.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kGemmScratchBytes];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::once_flag g_scratch_once[kScratchDevices];
+void *g_scratch_ptr[kScratchDevices];
+hipError_t g_scratch_err[kScratchDevices];
+
+}  // namespace
+
+hipError_t gemm_scratch(void **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void *p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *ptr = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
 }
 
 hipError_t launch_gemm(const WView &w, const uint16_t *x, int m, float *y, void *ws, size_t ws_bytes, hipStream_t s) {

@@ -195,6 +195,24 @@ int vq_gemm(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float *y, voi
   return map_hip(launch_sparse_add(v, x_bf16, VQ_BF16, m, y, s));
 }
 
+int vq_gemm_noalloc(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float *y, void *stream) {
+  WView v;
+  int st = check_weight(w, &v);
+  if (st != VQ_OK) return st;
+  if (!x_bf16 || !y) return VQ_ERR_NULL;
+  if (m < 1) return VQ_ERR_SHAPE;
+  if ((int64_t)m * v.k >= ((int64_t)1 << 31) || (int64_t)m * v.n >= ((int64_t)1 << 31)) return VQ_ERR_SHAPE;
+  if (!aligned16(x_bf16) || !aligned16(y)) return VQ_ERR_ALIGN;
+  const size_t need = gemm_workspace_bytes(v, m);
+  if (need > kGemmScratchBytes) return VQ_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if (need > 0 && gemm_scratch(&ws) != hipSuccess) return VQ_ERR_HIP;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = map_hip(launch_gemm(v, x_bf16, m, y, ws, need > 0 ? kGemmScratchBytes : 0, s));
+  if (st != VQ_OK) return st;
+  return map_hip(launch_sparse_add(v, x_bf16, VQ_BF16, m, y, s));
+}
+
 size_t vq_gemm_workspace_size(const vq_weight *w, int32_t m) {
   WView v;
   if (check_weight(w, &v) != VQ_OK || m < 1) return 0;

@@ -62,6 +62,10 @@ bool launch_gemv_tokens(const WView &w, const void *x, int batch, float *y, hipS
 hipError_t launch_gemm(const WView &w, const uint16_t *x, int m, float *y, void *ws, size_t ws_bytes, hipStream_t s);
 // Workspace bytes the many-token product of m tokens needs (0: none).
 size_t gemm_workspace_bytes(const WView &w, int m);
+// The library's own scratch for vq_gemm_noalloc: kGemmScratchBytes of device
+// memory per GPU (a static device array), its address on the current device.
+constexpr size_t kGemmScratchBytes = (size_t)33 << 20;
+hipError_t gemm_scratch(void **ptr);
 // y[b][r] += sum_j val_j x[b][col_j] over the sparse correction's row r, for
 // m tokens of x (VQ_F32 / VQ_BF16); after the main product on the same
 // stream.  No-op without a correction.

@@ -27,7 +27,9 @@
  *    A failed launch returns VQ_ERR_HIP.  No C++ exception crosses the ABI.
  *  - The library allocates no device memory and holds no per-call state;
  *    calls on different streams may run concurrently.  Scratch memory, where
- *    a kernel needs any, is the caller's workspace (vq_gemm).
+ *    a kernel needs any, is the caller's workspace (vq_gemm), except for
+ *    vq_gemm_noalloc, which uses a static device array of the library and
+ *    must not overlap with another vq_gemm_noalloc call on the same GPU.
  *  - Results are deterministic: fixed reduction order, no atomics.
  */
 #ifndef VQMM_H
@@ -224,6 +226,26 @@ int vq_gemm(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float *y, voi
  * Returns 0 for an invalid descriptor or m < 1 (vq_gemm then reports the
  * error itself).  Host only; touches no device. */
 size_t vq_gemm_workspace_size(const vq_weight *w, int32_t m);
+
+/*
+ * vq_gemm for callers that cannot allocate device memory or pass a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same product and results, with the scratch taken from
+ * the library's own static device buffer of VQ_GEMM_NOALLOC_SCRATCH bytes
+ * per GPU (held until the process ends; its device address is looked up on
+ * the first call on each device).  The caller still passes x and y.
+ * Returns VQ_ERR_WORKSPACE, before any HIP call, when the call would need
+ * more scratch than that (vq_gemm_workspace_size(w, m) >
+ * VQ_GEMM_NOALLOC_SCRATCH: 33 MiB holds fp16 x for 4096 tokens of k_in =
+ * 4096 or 2048 tokens of k_in = 8192).
+ * Allocates nothing (no hipMalloc or hipFree).  Every call on one GPU shares
+ * that GPU's buffer and leaves its contents behind; each call overwrites
+ * all of the scratch it reads, so nothing has to be cleared, but calls that
+ * overlap in time on one GPU (different streams, different threads) race on
+ * it: serialize them.
+ */
+#define VQ_GEMM_NOALLOC_SCRATCH ((size_t)33 << 20)
+int vq_gemm_noalloc(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float *y, void *stream);
 
 /*
  * Randomized Hadamard transform of each row of x (GLQ page, "How it works":

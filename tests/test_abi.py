@@ -168,6 +168,28 @@ def test_gemm_workspace_contract(L, n, k, bits, stages, m):
         assert L.vq_gemm(d, FAKE, m, FAKE, None, 0, None) == VQ_ERR_WORKSPACE
 
 
+def test_gemm_noalloc_checks(L):
+    """The no-allocation entry point validates like vq_gemm and refuses,
+    before any HIP call, a call that needs more than its static scratch."""
+    d = ctypes.byref(fake_desc(n=4096, k=4096, bits=12, stages=2, bs=128))
+    assert L.vq_gemm_noalloc(d, None, 2048, FAKE, None) == VQ_ERR_NULL
+    assert L.vq_gemm_noalloc(d, FAKE, 0, FAKE, None) == VQ_ERR_SHAPE
+    assert L.vq_gemm_noalloc(d, FAKE + 2, 2048, FAKE, None) == VQ_ERR_ALIGN
+    limit = 33 << 20
+    m_big = 8192  # 8192 tokens x 4096 columns of fp16 x: 64 MiB of scratch
+    assert L.vq_gemm_workspace_size(d, m_big) > limit
+    assert L.vq_gemm_noalloc(d, FAKE, m_big, FAKE, None) == VQ_ERR_WORKSPACE
+    assert L.vq_gemm_workspace_size(d, 4096) <= limit
+    bad = fake_desc()
+    bad.n_out = 0
+    assert L.vq_gemm_noalloc(ctypes.byref(bad), FAKE, 64, FAKE, None) == VQ_ERR_SHAPE
+
+
+def test_header_states_noalloc_limit():
+    m = re.search(r"#define VQ_GEMM_NOALLOC_SCRATCH \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == 33 << 20
+
+
 def test_gemm_workspace_size_invalid(L):
     assert L.vq_gemm_workspace_size(None, 16) == 0
     d = fake_desc()
