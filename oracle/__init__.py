@@ -358,6 +358,57 @@ def rht_ref(x: np.ndarray, signs: np.ndarray, max_block: int) -> np.ndarray:
     return out
 
 
+def rht_inverse_ref(y: np.ndarray, signs: np.ndarray, max_block: int) -> np.ndarray:
+    """Output-side transform of each row of ``y`` [B, n], float64: the inverse
+    of :func:`rht_ref`.
+
+    GLQ "How it works": the weights are rotated and the inverse transform runs
+    inside the inference kernels; "Inference kernels" (the fused linear: input
+    RHT, decode, scale, output RHT).  Reading: a weight stored rotated on its
+    output side as W' = (H D) W, with D = diag(signs) and H the block-diagonal
+    orthonormal Hadamard of :func:`rht_blocks`, gives W x = (H D)^T W' x, and
+    (H D)^T = D H because H is symmetric: the blocks' Hadamard first, then the
+    sign flips.
+    """
+    y64 = np.asarray(y, dtype=np.float64)
+    if y64.ndim == 1:
+        y64 = y64[None, :]
+    sg = np.asarray(signs, dtype=np.float64)
+    n = y64.shape[1]
+    out = np.empty_like(y64)
+    for b in range(y64.shape[0]):
+        off = 0
+        for blk in rht_blocks(n, max_block):
+            out[b, off:off + blk] = fwht(y64[b, off:off + blk])
+            off += blk
+        out[b] *= sg
+    return out
+
+
+def rht_shards_ref(x: np.ndarray, shard_lens: Sequence[int], signs: np.ndarray, max_block: int,
+                   inverse: bool = False) -> np.ndarray:
+    """Shard-batched transform (GLQ "Inference kernels", shard-batched output
+    RHT: the per-shard output transforms of a fused QKV or gate-up layer in
+    one launch).  Each row of ``x`` [B, sum(shard_lens)] is cut into
+    consecutive shards; every shard is transformed on its own, exactly as
+    :func:`rht_ref` (or :func:`rht_inverse_ref` with ``inverse``) transforms
+    a row of that length, with the signs of its own columns.  Reading: the
+    block decomposition restarts at every shard boundary, because each shard
+    is a separate linear whose rotation was chosen for its own size."""
+    x64 = np.asarray(x, dtype=np.float64)
+    if x64.ndim == 1:
+        x64 = x64[None, :]
+    if sum(shard_lens) != x64.shape[1] or any(n <= 0 for n in shard_lens):
+        raise ValueError("shard lengths must be positive and cover the row")
+    fn = rht_inverse_ref if inverse else rht_ref
+    out = np.empty_like(x64)
+    off = 0
+    for n in shard_lens:
+        out[:, off:off + n] = fn(x64[:, off:off + n], signs[off:off + n], max_block)
+        off += n
+    return out
+
+
 # --------------------------------------------------------------------------
 # c-5  storage cost
 # --------------------------------------------------------------------------

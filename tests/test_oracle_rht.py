@@ -99,3 +99,64 @@ def test_rht_preserves_norm_per_block():
     for b in oracle.rht_blocks(n, 8192):
         assert abs(np.linalg.norm(got[off:off + b]) - np.linalg.norm(x[off:off + b])) <= 1e-10
         off += b
+
+
+def test_inverse_is_dense_transpose():
+    """The output transform is (H D)^T = D H, built densely with scipy: the
+    transpose of the input transform's matrix."""
+    rng = np.random.default_rng(10)
+    n = 2688
+    signs = rng.integers(0, 2, n) * 2 - 1
+    y = rng.standard_normal((2, n))
+    blocks = oracle.rht_blocks(n, 1024)
+    fwd = scipy.linalg.block_diag(*[scipy.linalg.hadamard(b) / math.sqrt(b) for b in blocks]) @ np.diag(signs)
+    got = oracle.rht_inverse_ref(y, signs, 1024)
+    want = (fwd.T @ y.T).T
+    assert np.allclose(got, want, rtol=0, atol=1e-12 * np.abs(y).sum())
+
+
+def test_inverse_signs_last():
+    """Signs act after the transform: with y = e_0 and sigma_0 = -1 only the
+    first output is negative (a sign-first reading would negate them all)."""
+    n = 64
+    signs = np.ones(n)
+    signs[0] = -1
+    y = np.zeros(n)
+    y[0] = 1.0
+    got = oracle.rht_inverse_ref(y, signs, 64)[0]
+    want = np.ones(n) / 8.0
+    want[0] = -1 / 8.0
+    assert np.allclose(got, want, atol=1e-15)
+
+
+@pytest.mark.parametrize("n,mb", [(28672, 8192), (2688, 8192), (576, 64), (1, 1)])
+def test_inverse_round_trip(n, mb):
+    rng = np.random.default_rng(n)
+    signs = rng.integers(0, 2, n) * 2 - 1
+    x = rng.standard_normal((2, n))
+    back = oracle.rht_inverse_ref(oracle.rht_ref(x, signs, mb), signs, mb)
+    assert np.allclose(back, x, rtol=0, atol=1e-12 * np.sqrt(n))
+
+
+def test_shards_dense():
+    """Shards 12 | 8 with blocks of at most 8: blockdiag(H8, H4 | H8), each
+    shard's decomposition restarting at its own boundary (one decomposition
+    of the whole row of 20 would give H16, H4 instead)."""
+    rng = np.random.default_rng(11)
+    signs = rng.integers(0, 2, 20) * 2 - 1
+    x = rng.standard_normal((3, 20))
+    h = [scipy.linalg.hadamard(b) / math.sqrt(b) for b in (8, 4, 8)]
+    dense = scipy.linalg.block_diag(*h)
+    got = oracle.rht_shards_ref(x, [12, 8], signs, 8)
+    assert np.allclose(got, (dense @ (x * signs).T).T, rtol=0, atol=1e-13)
+    got_inv = oracle.rht_shards_ref(x, [12, 8], signs, 8, inverse=True)
+    assert np.allclose(got_inv, ((dense @ x.T).T) * signs, rtol=0, atol=1e-13)
+    whole = oracle.rht_ref(x, signs, 16)
+    assert not np.allclose(oracle.rht_shards_ref(x, [12, 8], signs, 16), whole)
+
+
+def test_shards_reject_bad_lengths():
+    with pytest.raises(ValueError):
+        oracle.rht_shards_ref(np.zeros((1, 8)), [4, 3], np.ones(8), 8)
+    with pytest.raises(ValueError):
+        oracle.rht_shards_ref(np.zeros((1, 8)), [8, 0], np.ones(8), 8)

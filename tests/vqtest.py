@@ -94,3 +94,16 @@ def assert_within(y, y_ref, bound, what=""):
         raise AssertionError(f"{what}: {int((~ok).sum())} outputs outside the bound "
                              f"(worst ratio {worst:.3g}); first {bad.tolist()}")
     return worst
+
+
+def assert_all_rows(y, sw: vqsynth.SynthWeight, x64, what="", chunk=4096):
+    """Every output of y [B, n_out] against the oracle's exact product, the
+    float64 weight built a block of rows at a time to bound host memory."""
+    idx = oracle_indices(sw)
+    worst = 0.0
+    for r0 in range(0, sw.n_out, chunk):
+        rows = np.arange(r0, min(r0 + chunk, sw.n_out))
+        w64 = oracle_w64(sw, rows, idx)
+        y_ref, bound = oracle.matmul_ref(w64, x64)
+        worst = max(worst, assert_within(y[:, rows], y_ref, bound, f"{what} rows {r0}.."))
+    return worst
