@@ -13,6 +13,8 @@ Entry points (same names as the C ABI):
   (with :func:`vq_gemm_workspace_size` for its caller-owned scratch;
   :func:`vq_gemm_noalloc` uses the library's static scratch instead)
 * :func:`rht_apply`         -- randomized Hadamard transform of activations
+* :func:`rht_apply_shards`  -- the same per shard of a fused layer's rows, forward
+  (input side) or inverse (output side), in one launch
 * :func:`vq_gemv_rht`       -- vq_gemv with the input transform inside the kernel
 * :func:`vq_compressed_bytes`, :func:`vq_validate`, :func:`vq_version`
 
@@ -34,7 +36,7 @@ import numpy as np
 __all__ = [
     "VQError", "VQWeight", "lib", "LIB_PATH", "vq_version", "vq_validate", "vq_compressed_bytes",
     "vq_unpack_dequant", "vq_gemv", "vq_gemm", "vq_gemm_workspace_size", "vq_gemm_noalloc", "rht_apply",
-    "vq_gemv_rht", "VQ_F32", "VQ_BF16", "VQ_STAGE_SCALES", "EXPORTS",
+    "rht_apply_shards", "vq_gemv_rht", "VQ_F32", "VQ_BF16", "VQ_STAGE_SCALES", "VQ_RHT_MAX_SHARDS", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvqmm.so")
@@ -42,7 +44,8 @@ VQ_F32, VQ_BF16 = 0, 1
 MAX_STAGES = 4
 EXPORTS = ("vq_version", "vq_status_string", "vq_validate", "vq_compressed_bytes",
            "vq_unpack_dequant", "vq_gemv", "vq_gemm", "vq_gemm_workspace_size", "vq_gemm_noalloc", "rht_apply",
-           "vq_gemv_rht")
+           "rht_apply_shards", "vq_gemv_rht")
+VQ_RHT_MAX_SHARDS = 16
 
 _ptr4 = ctypes.c_void_p * MAX_STAGES
 _int4 = ctypes.c_int32 * MAX_STAGES
@@ -106,6 +109,9 @@ def lib() -> ctypes.CDLL:
         L.vq_gemm_noalloc.argtypes, L.vq_gemm_noalloc.restype = [D, P, ctypes.c_int32, P, P], ctypes.c_int
         L.rht_apply.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P, P]
         L.rht_apply.restype = ctypes.c_int
+        L.rht_apply_shards.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P,
+                                       ctypes.c_int32, ctypes.c_int32, P, P]
+        L.rht_apply_shards.restype = ctypes.c_int
         L.vq_gemv_rht.argtypes = [D, P, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P, P]
         L.vq_gemv_rht.restype = ctypes.c_int
         _LIB = L
@@ -429,6 +435,31 @@ def rht_apply(x, signs, max_block: int, out=None, stream=None):
     out = _out(out, (b, n), dev, "out")
     _check(lib().rht_apply(x.data_ptr(), xt, b, n, signs.data_ptr(), max_block, out.data_ptr(),
                            _stream_handle(stream)), "rht_apply")
+    return out
+
+
+def rht_apply_shards(x, signs, max_block: int, shard_lens, inverse: bool = False, out=None, stream=None):
+    """The transform of every shard of each row on its own, in one launch:
+    x [B, n] float32/bfloat16 with n = sum(shard_lens), signs int8 [n] on the
+    device -> float32 [B, n].  inverse=False: signs, then Hadamard (the input
+    transform); inverse=True: Hadamard, then signs (the output transform)."""
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    if x.dim() != 2:
+        raise ValueError(f"x has shape {tuple(x.shape)}; expected [tokens, n]")
+    xt = _xtype(x)
+    dev = x.device
+    _on_gpu(x, dev, "x")
+    b, n = x.shape
+    lens = [int(v) for v in shard_lens]
+    if not 1 <= len(lens) <= VQ_RHT_MAX_SHARDS or min(lens) < 1 or sum(lens) != n:
+        raise ValueError(f"shard lengths {lens} must be 1..{VQ_RHT_MAX_SHARDS} positive lengths summing to {n}")
+    _signs(signs, n, dev)
+    out = _out(out, (b, n), dev, "out")
+    arr = (ctypes.c_int32 * len(lens))(*lens)
+    _check(lib().rht_apply_shards(x.data_ptr(), xt, b, n, len(lens), ctypes.cast(arr, ctypes.c_void_p),
+                                  signs.data_ptr(), max_block, 1 if inverse else 0, out.data_ptr(),
+                                  _stream_handle(stream)), "rht_apply_shards")
     return out
 
 

@@ -1,10 +1,17 @@
-// Randomized Hadamard transform of the input (GLQ page, "How it works":
-// random sign flips, then a fast Walsh-Hadamard transform; "Bit widths":
-// block-diagonal over power-of-two blocks).
+// Randomized Hadamard transform (GLQ page, "How it works": random sign
+// flips, then a fast Walsh-Hadamard transform, its inverse inside the
+// inference kernels; "Bit widths": block-diagonal over power-of-two blocks;
+// "Inference kernels": the per-shard output transforms of a fused layer
+// batched into one launch).
 //
-// One workgroup per (token, block).  The block (<= 16384 fp32 = 64 KiB) lives
-// in LDS.  Blocks of at least 256 elements (k_rht_vec): the first four
-// butterfly stages run in registers as the block is staged, the rest in
+// Forward (the input side): signs, then the blocks' Hadamard.  Inverse (the
+// output side): the blocks' Hadamard, then signs.  A row may be cut into up
+// to kRhtMaxShards shards, each decomposed into blocks on its own; the grid
+// is (token x block, shard).
+//
+// One workgroup per (token, block, shard).  The block (<= 16384 fp32 = 64
+// KiB) lives in LDS.  Blocks of at least 256 elements (k_rht_vec): the first
+// four butterfly stages run in registers as the block is staged, the rest in
 // passes of four (the last of up to five) through LDS.  Smaller blocks
 // (k_rht): the first log2(R) stages in registers (R = elements per thread),
 // the rest as radix-2 passes through LDS.  Natural (Sylvester) order,
@@ -21,51 +28,57 @@ struct RhtArgs {
   const void *x;
   const int8_t *signs;
   float *out;
-  int n;          // row length
-  int xt;         // VQ_F32 / VQ_BF16
-  int nblocks;    // blocks per row
-  int mb;         // max_block
-  int nfull;      // n / max_block full blocks, then the set bits of the rest
-  int rest;       // n % max_block
+  int n;        // row length (all shards)
+  int xt;       // VQ_F32 / VQ_BF16
+  int mb;       // max_block
+  int nbx;      // grid.x per token: the most blocks of any shard
+  int sh_off[kRhtMaxShards + 1];  // shard s is columns sh_off[s] .. sh_off[s + 1]
 };
 
-// Offset and length of block `b` of the greedy largest-first decomposition:
-// nfull blocks of max_block, then one block per set bit of the remainder,
-// largest first.
-__device__ __forceinline__ void rht_block(const RhtArgs &a, int b, int &off, int &len) {
-  if (b < a.nfull) {
-    off = b * a.mb;
+// Token, column offset and length of this workgroup's block (false: no
+// block, the shard has fewer than nbx).  Within a shard of length L the
+// greedy largest-first decomposition is L / mb blocks of mb, then one block
+// per set bit of L % mb, largest first.
+__device__ __forceinline__ bool rht_locate(const RhtArgs &a, int &row, int &off, int &len) {
+  const int sh = blockIdx.y;
+  const int s0 = a.sh_off[sh];
+  const int slen = a.sh_off[sh + 1] - s0;
+  const int nfull = slen / a.mb, rest = slen % a.mb;
+  row = blockIdx.x / a.nbx;
+  const int b = blockIdx.x % a.nbx;
+  if (b >= nfull + __builtin_popcount((unsigned)rest)) return false;
+  if (b < nfull) {
+    off = s0 + b * a.mb;
     len = a.mb;
-    return;
+    return true;
   }
-  off = a.nfull * a.mb;
-  int j = b - a.nfull;
+  off = s0 + nfull * a.mb;
+  int j = b - nfull;
   for (int bit = 30; bit >= 0; --bit) {
-    if (a.rest & (1 << bit)) {
+    if (rest & (1 << bit)) {
       if (j == 0) {
         len = 1 << bit;
-        return;
+        return true;
       }
       off += 1 << bit;
       --j;
     }
   }
-  len = 0;  // unreachable for b < nblocks
+  return false;  // unreachable: b indexes a set bit
 }
 
 // Blocks of at least 256 elements with every block of every row 16-byte
 // aligned in x, signs and out.  A thread stages 16 consecutive elements
-// times their signs and runs the first four butterfly stages on them in
-// registers; the remaining stages run in passes of four through LDS (groups
-// of 16 elements in registers, one barrier per pass), the last pass taking
-// up to five and applying the orthonormal scale; then one coalesced store.
-template <bool BF16>
+// (times their signs when forward) and runs the first four butterfly stages
+// on them in registers; the remaining stages run in passes of four through
+// LDS (groups of 16 elements in registers, one barrier per pass), the last
+// pass taking up to five and applying the orthonormal scale; then one
+// coalesced store (times the signs when inverse).
+template <bool BF16, bool INV>
 __global__ __launch_bounds__(kRhtThreads) void k_rht_vec(RhtArgs a) {
   __shared__ __attribute__((aligned(16))) float buf[kRhtMaxBlock];
-  const int blk = blockIdx.x % a.nblocks;
-  const int row = blockIdx.x / a.nblocks;
-  int off, nb;
-  rht_block(a, blk, off, nb);
+  int row, off, nb;
+  if (!rht_locate(a, row, off, nb)) return;  // whole workgroup
   int lb = 0;
   while ((1 << lb) < nb) ++lb;  // nb is a power of two >= 256
   const int tid = threadIdx.x;
@@ -74,7 +87,7 @@ __global__ __launch_bounds__(kRhtThreads) void k_rht_vec(RhtArgs a) {
     float v[16];
     const void *xr = BF16 ? (const void *)(reinterpret_cast<const uint16_t *>(a.x) + base)
                           : (const void *)(reinterpret_cast<const float *>(a.x) + base);
-    rht_load16(xr, !BF16, a.signs + off, 16 * g, v);
+    rht_load16<!INV>(xr, !BF16, a.signs + off, 16 * g, v);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       *reinterpret_cast<float4 *>(&buf[16 * g + 4 * q]) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
@@ -85,16 +98,24 @@ __global__ __launch_bounds__(kRhtThreads) void k_rht_vec(RhtArgs a) {
   }
   __syncthreads();
   float4 *po = reinterpret_cast<float4 *>(a.out + base);
-  for (int i = tid; i < nb / 4; i += kRhtThreads) po[i] = reinterpret_cast<const float4 *>(buf)[i];
+  for (int i = tid; i < nb / 4; i += kRhtThreads) {
+    float4 v = reinterpret_cast<const float4 *>(buf)[i];
+    if (INV) {
+      const uint32_t sg = *reinterpret_cast<const uint32_t *>(a.signs + off + 4 * i);
+      v.x *= (float)(int8_t)(sg & 0xffu);
+      v.y *= (float)(int8_t)((sg >> 8) & 0xffu);
+      v.z *= (float)(int8_t)((sg >> 16) & 0xffu);
+      v.w *= (float)(int8_t)(sg >> 24);
+    }
+    po[i] = v;
+  }
 }
 
-template <int R>
+template <int R, bool INV>
 __global__ __launch_bounds__(kRhtThreads) void k_rht(RhtArgs a) {
   __shared__ float buf[kRhtMaxBlock];
-  const int blk = blockIdx.x % a.nblocks;
-  const int row = blockIdx.x / a.nblocks;
-  int off, nb;
-  rht_block(a, blk, off, nb);
+  int row, off, nb;
+  if (!rht_locate(a, row, off, nb)) return;  // whole workgroup
   const int tid = threadIdx.x;
   const int64_t base = (int64_t)row * a.n + off;
   // Contiguous layout: thread t owns elements R*t .. R*t+R-1 (when R*t < nb).
@@ -106,9 +127,9 @@ __global__ __launch_bounds__(kRhtThreads) void k_rht(RhtArgs a) {
     for (int q = 0; q < R; ++q) {
       if (q < r_eff) {
         const int64_t gi = base + i0 + q;
-        float xv = (a.xt == VQ_F32) ? reinterpret_cast<const float *>(a.x)[gi]
-                                    : bf2f(reinterpret_cast<const uint16_t *>(a.x)[gi]);
-        v[q] = xv * (float)a.signs[off + i0 + q];
+        const float xv = (a.xt == VQ_F32) ? reinterpret_cast<const float *>(a.x)[gi]
+                                          : bf2f(reinterpret_cast<const uint16_t *>(a.x)[gi]);
+        v[q] = INV ? xv : xv * (float)a.signs[off + i0 + q];
       }
     }
     // in-register stages h = 1 .. r_eff/2
@@ -141,11 +162,43 @@ __global__ __launch_bounds__(kRhtThreads) void k_rht(RhtArgs a) {
   }
   __syncthreads();
   const float sc = (float)(1.0 / __builtin_sqrt((double)nb));
-  for (int i = tid; i < nb; i += kRhtThreads) a.out[base + i] = buf[i] * sc;
+  for (int i = tid; i < nb; i += kRhtThreads) {
+    const float o = buf[i] * sc;
+    a.out[base + i] = INV ? o * (float)a.signs[off + i] : o;
+  }
 }
 
-hipError_t launch_rht(const void *x, int xt, int batch, int n, const int8_t *signs, int max_block,
-                      float *out, hipStream_t s) {
+template <bool INV>
+static void launch_rht_dir(const RhtArgs &a, dim3 grid, bool vec, int xt, int r, hipStream_t s) {
+  if (vec) {
+    if (xt == VQ_BF16) hipLaunchKernelGGL((k_rht_vec<true, INV>), grid, dim3(kRhtThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_rht_vec<false, INV>), grid, dim3(kRhtThreads), 0, s, a);
+  } else if (r <= 1) {
+    hipLaunchKernelGGL((k_rht<1, INV>), grid, dim3(kRhtThreads), 0, s, a);
+  } else if (r == 2) {
+    hipLaunchKernelGGL((k_rht<2, INV>), grid, dim3(kRhtThreads), 0, s, a);
+  } else if (r == 4) {
+    hipLaunchKernelGGL((k_rht<4, INV>), grid, dim3(kRhtThreads), 0, s, a);
+  } else if (r == 8) {
+    hipLaunchKernelGGL((k_rht<8, INV>), grid, dim3(kRhtThreads), 0, s, a);
+  } else if (r == 16) {
+    hipLaunchKernelGGL((k_rht<16, INV>), grid, dim3(kRhtThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((k_rht<32, INV>), grid, dim3(kRhtThreads), 0, s, a);
+  }
+}
+
+int rht_grid_blocks(int nsh, const int32_t *shard_len, int max_block) {
+  int nbx = 0;
+  for (int i = 0; i < nsh; ++i) {
+    const int nb = shard_len[i] / max_block + __builtin_popcount((unsigned)(shard_len[i] % max_block));
+    nbx = nb > nbx ? nb : nbx;
+  }
+  return nbx;
+}
+
+hipError_t launch_rht(const void *x, int xt, int batch, int n, int nsh, const int32_t *shard_len,
+                      const int8_t *signs, int max_block, bool inverse, float *out, hipStream_t s) {
   RhtArgs a{};
   a.x = x;
   a.signs = signs;
@@ -153,39 +206,29 @@ hipError_t launch_rht(const void *x, int xt, int batch, int n, const int8_t *sig
   a.n = n;
   a.xt = xt;
   a.mb = max_block;
-  a.nfull = n / max_block;
-  a.rest = n % max_block;
-  a.nblocks = a.nfull + __builtin_popcount((unsigned)a.rest);
-  int maxlen = a.nfull ? max_block : 1;
-  while (maxlen * 2 <= a.rest) maxlen *= 2;
-  const dim3 grid((unsigned)((int64_t)batch * a.nblocks));
+  a.nbx = rht_grid_blocks(nsh, shard_len, max_block);
+  // vector path: every block of every shard is at least 256 elements long
+  // (so every shard and block offset is a multiple of 256), and x, signs,
+  // out and the row pitch keep 16-byte alignment
+  bool big_blocks = true;
+  int maxlen = 1;
+  for (int i = 0; i < nsh; ++i) {
+    a.sh_off[i + 1] = a.sh_off[i] + shard_len[i];
+    const int nfull = shard_len[i] / max_block, rest = shard_len[i] % max_block;
+    big_blocks = big_blocks && (nfull == 0 || max_block >= 256) && rest % 256 == 0;
+    int ml = nfull ? max_block : 1;
+    while (ml * 2 <= rest) ml *= 2;
+    maxlen = ml > maxlen ? ml : maxlen;
+  }
+  const dim3 grid((unsigned)((int64_t)batch * a.nbx), (unsigned)nsh);
   // Elements per thread for the register stages: the largest block spread
   // over the workgroup (at least 1, at most 32 for a 16384 block).
-  int r = maxlen / kRhtThreads;
-  // vector path: every block is at least 256 elements long (so every block
-  // offset is a multiple of 256), and x, signs, out and the row pitch keep
-  // 16-byte alignment
+  const int r = maxlen / kRhtThreads;
   const int xb = xt == VQ_F32 ? 4 : 2;
-  const bool big_blocks = (a.nfull == 0 || max_block >= 256) && a.rest % 256 == 0;
   const bool aligned = ((uintptr_t)x % 16 == 0) && ((uintptr_t)signs % 16 == 0) && ((uintptr_t)out % 16 == 0) &&
                        ((int64_t)n * xb % 16 == 0);
-  if (big_blocks && aligned) {
-    if (xt == VQ_BF16) hipLaunchKernelGGL((k_rht_vec<true>), grid, dim3(kRhtThreads), 0, s, a);
-    else hipLaunchKernelGGL((k_rht_vec<false>), grid, dim3(kRhtThreads), 0, s, a);
-    return hipGetLastError();
-  }
-  if (r <= 1)
-    hipLaunchKernelGGL(k_rht<1>, grid, dim3(kRhtThreads), 0, s, a);
-  else if (r == 2)
-    hipLaunchKernelGGL(k_rht<2>, grid, dim3(kRhtThreads), 0, s, a);
-  else if (r == 4)
-    hipLaunchKernelGGL(k_rht<4>, grid, dim3(kRhtThreads), 0, s, a);
-  else if (r == 8)
-    hipLaunchKernelGGL(k_rht<8>, grid, dim3(kRhtThreads), 0, s, a);
-  else if (r == 16)
-    hipLaunchKernelGGL(k_rht<16>, grid, dim3(kRhtThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_rht<32>, grid, dim3(kRhtThreads), 0, s, a);
+  if (inverse) launch_rht_dir<true>(a, grid, big_blocks && aligned, xt, r, s);
+  else launch_rht_dir<false>(a, grid, big_blocks && aligned, xt, r, s);
   return hipGetLastError();
 }
 

@@ -241,17 +241,32 @@ int vq_gemv_rht(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batc
   return VQ_OK;
 }
 
+static_assert(VQ_RHT_MAX_SHARDS == kRhtMaxShards, "shard limit of the header and the kernels");
+
 int rht_apply(const void *x, int32_t x_dtype, int32_t batch, int32_t n, const int8_t *signs,
               int32_t max_block, float *out, void *stream) {
-  if (!x || !signs || !out) return VQ_ERR_NULL;
+  return rht_apply_shards(x, x_dtype, batch, n, 1, &n, signs, max_block, VQ_RHT_FORWARD, out, stream);
+}
+
+int rht_apply_shards(const void *x, int32_t x_dtype, int32_t batch, int32_t n, int32_t n_shards,
+                     const int32_t *shard_len, const int8_t *signs, int32_t max_block, int32_t direction,
+                     float *out, void *stream) {
+  if (!x || !signs || !out || !shard_len) return VQ_ERR_NULL;
   if (x_dtype != VQ_F32 && x_dtype != VQ_BF16) return VQ_ERR_DTYPE;
-  if (batch < 1 || n < 1) return VQ_ERR_SHAPE;
+  if (direction != VQ_RHT_FORWARD && direction != VQ_RHT_INVERSE) return VQ_ERR_VALUE;
+  if (batch < 1 || n < 1 || n_shards < 1 || n_shards > VQ_RHT_MAX_SHARDS) return VQ_ERR_SHAPE;
   if (max_block < 1 || max_block > 16384 || (max_block & (max_block - 1)) != 0) return VQ_ERR_SHAPE;
+  int64_t total = 0;
+  for (int i = 0; i < n_shards; ++i) {
+    if (shard_len[i] < 1) return VQ_ERR_SHAPE;
+    total += shard_len[i];
+  }
+  if (total != n) return VQ_ERR_SHAPE;
   if ((int64_t)batch * n >= ((int64_t)1 << 31)) return VQ_ERR_SHAPE;
-  const int64_t nblocks = n / max_block + __builtin_popcount((unsigned)(n % max_block));
-  if (nblocks * batch >= ((int64_t)1 << 31)) return VQ_ERR_SHAPE;
+  if ((int64_t)rht_grid_blocks(n_shards, shard_len, max_block) * batch >= ((int64_t)1 << 31)) return VQ_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(out)) return VQ_ERR_ALIGN;
-  return map_hip(launch_rht(x, x_dtype, batch, n, signs, max_block, out, reinterpret_cast<hipStream_t>(stream)));
+  return map_hip(launch_rht(x, x_dtype, batch, n, n_shards, shard_len, signs, max_block,
+                            direction == VQ_RHT_INVERSE, out, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -333,8 +333,10 @@ __device__ __forceinline__ void stage_ladder_lds(const uint16_t *const *cb, uint
 // ---------------------------------------------------------------------------
 
 // Elements i .. i + 15 of x (fp32 or bf16, 16-byte aligned) times their
-// signs (int8, 16-byte aligned), then butterfly stages 1, 2, 4, 8 (the low
-// four bits of the index) in registers, Sylvester order.
+// signs (int8, 16-byte aligned; not read without SIGNS), then butterfly
+// stages 1, 2, 4, 8 (the low four bits of the index) in registers,
+// Sylvester order.
+template <bool SIGNS = true>
 __device__ __forceinline__ void rht_load16(const void *x, bool f32, const int8_t *signs, size_t i, float (&v)[16]) {
   if (f32) {
 #pragma unroll
@@ -354,10 +356,12 @@ __device__ __forceinline__ void rht_load16(const void *x, bool f32, const int8_t
       }
     }
   }
-  const uint4 sg = *reinterpret_cast<const uint4 *>(signs + i);
-  const uint32_t s4[4] = {sg.x, sg.y, sg.z, sg.w};
+  if (SIGNS) {
+    const uint4 sg = *reinterpret_cast<const uint4 *>(signs + i);
+    const uint32_t s4[4] = {sg.x, sg.y, sg.z, sg.w};
 #pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] *= (float)(int8_t)((s4[j >> 2] >> (8 * (j & 3))) & 0xffu);
+    for (int j = 0; j < 16; ++j) v[j] *= (float)(int8_t)((s4[j >> 2] >> (8 * (j & 3))) & 0xffu);
+  }
 #pragma unroll
   for (int h = 1; h < 16; h <<= 1)
 #pragma unroll

@@ -42,8 +42,15 @@ inline bool plain_format(const WView &w) { return w.uniform && !w.scaled && w.bi
 int device_cu_count();
 
 hipError_t launch_unpack_dequant(const WView &w, uint16_t *idx_out, uint16_t *w_out, hipStream_t s);
-hipError_t launch_rht(const void *x, int xt, int batch, int n, const int8_t *signs, int max_block,
-                      float *out, hipStream_t s);
+// Shards per row of one transform launch.
+constexpr int kRhtMaxShards = 16;
+// grid.x workgroups per token of a transform launch: the most blocks of any
+// shard.
+int rht_grid_blocks(int nsh, const int32_t *shard_len, int max_block);
+// The transform of batch rows of n = sum(shard_len) columns, each shard on
+// its own; forward = signs then Hadamard, inverse = Hadamard then signs.
+hipError_t launch_rht(const void *x, int xt, int batch, int n, int nsh, const int32_t *shard_len,
+                      const int8_t *signs, int max_block, bool inverse, float *out, hipStream_t s);
 // One token of x (fp32 or bf16, VQ_F32 / VQ_BF16) against W: y[n].
 // *sp_done: the launched kernel also added the sparse correction.
 hipError_t launch_gemv_token(const WView &w, const void *x, int xt, float *y, hipStream_t s, bool *sp_done);

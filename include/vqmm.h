@@ -266,6 +266,38 @@ int rht_apply(const void *x, int32_t x_dtype, int32_t batch, int32_t n, const in
               int32_t max_block, float *out, void *stream);
 
 /*
+ * The transform of rows cut into shards, in one launch (GLQ page,
+ * "Inference kernels": the per-shard output transforms of a fused QKV or
+ * gate-up layer batched into a single launch; "How it works": the weights
+ * are rotated and the inverse transform runs in the inference kernels).
+ * Row b of x is n = shard_len[0] + ... + shard_len[n_shards - 1] columns;
+ * each shard is transformed on its own, exactly as rht_apply transforms a
+ * row of that length (its own greedy block decomposition, the signs of its
+ * own columns):
+ *   direction VQ_RHT_FORWARD: signs, then the blocks' Hadamard (the input
+ *     transform; one shard gives rht_apply);
+ *   direction VQ_RHT_INVERSE: the blocks' Hadamard, then signs -- the
+ *     inverse (transpose) of the forward transform, the output-side step
+ *     y = D H y' for a weight stored rotated on its output side.
+ *   x          : [batch][n], VQ_F32 or VQ_BF16, 16-byte aligned
+ *   n_shards   : 1..VQ_RHT_MAX_SHARDS
+ *   shard_len  : HOST array [n_shards], each >= 1, summing to n; read during
+ *                the call only
+ *   signs      : int8 [n], each +1 or -1 (device)
+ *   max_block  : power of two, 1..16384
+ *   out        : float [batch][n], 16-byte aligned; must not alias x
+ * Errors (before any HIP call): VQ_ERR_NULL, VQ_ERR_DTYPE, VQ_ERR_VALUE for
+ * an unknown direction, VQ_ERR_SHAPE for shard lengths that are not
+ * positive or do not sum to n.  Same error bound as rht_apply, per block.
+ */
+#define VQ_RHT_FORWARD 0
+#define VQ_RHT_INVERSE 1
+#define VQ_RHT_MAX_SHARDS 16
+int rht_apply_shards(const void *x, int32_t x_dtype, int32_t batch, int32_t n, int32_t n_shards,
+                     const int32_t *shard_len, const int8_t *signs, int32_t max_block, int32_t direction,
+                     float *out, void *stream);
+
+/*
  * The decode-style product with the input transform applied inside the
  * decode kernel (GLQ page, "Advanced", "Trellis codebook": its decode
  * kernels run the input Hadamard transform in every decode block instead of

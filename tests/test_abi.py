@@ -246,6 +246,39 @@ def test_rht_argument_checks(L):
     assert L.rht_apply(FAKE + 4, 0, 1, 64, FAKE, 64, FAKE, None) == VQ_ERR_ALIGN
 
 
+def _lens(*v):
+    arr = (ctypes.c_int32 * len(v))(*v)
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+def test_rht_shards_argument_checks(L):
+    """Shard lists are checked on the host: positive lengths that sum to n,
+    1..16 shards, a known direction; nothing is launched on an error."""
+    ok, _k1 = _lens(48, 16)
+    assert L.rht_apply_shards(FAKE, 0, 1, 64, 2, None, FAKE, 64, 0, FAKE, None) == VQ_ERR_NULL
+    assert L.rht_apply_shards(None, 0, 1, 64, 2, ok, FAKE, 64, 0, FAKE, None) == VQ_ERR_NULL
+    assert L.rht_apply_shards(FAKE, 0, 1, 64, 2, ok, None, 64, 0, FAKE, None) == VQ_ERR_NULL
+    assert L.rht_apply_shards(FAKE, 3, 1, 64, 2, ok, FAKE, 64, 0, FAKE, None) == VQ_ERR_DTYPE
+    assert L.rht_apply_shards(FAKE, 0, 1, 64, 2, ok, FAKE, 64, 2, FAKE, None) == VQ_ERR_VALUE
+    assert L.rht_apply_shards(FAKE, 0, 1, 64, 0, ok, FAKE, 64, 0, FAKE, None) == VQ_ERR_SHAPE
+    assert L.rht_apply_shards(FAKE, 0, 1, 64, 17, ok, FAKE, 64, 0, FAKE, None) == VQ_ERR_SHAPE
+    short, _k2 = _lens(48, 8)
+    assert L.rht_apply_shards(FAKE, 0, 1, 64, 2, short, FAKE, 64, 1, FAKE, None) == VQ_ERR_SHAPE
+    neg, _k3 = _lens(80, -16)
+    assert L.rht_apply_shards(FAKE, 0, 1, 64, 2, neg, FAKE, 64, 1, FAKE, None) == VQ_ERR_SHAPE
+    zero, _k4 = _lens(64, 0)
+    assert L.rht_apply_shards(FAKE, 0, 1, 64, 2, zero, FAKE, 64, 1, FAKE, None) == VQ_ERR_SHAPE
+    assert L.rht_apply_shards(FAKE, 0, 1, 64, 2, ok, FAKE, 96, 1, FAKE, None) == VQ_ERR_SHAPE
+    assert L.rht_apply_shards(FAKE + 4, 0, 1, 64, 2, ok, FAKE, 64, 1, FAKE, None) == VQ_ERR_ALIGN
+
+
+def test_header_rht_constants():
+    src = open(HEADER).read()
+    import compressed_index_matmul_amd as vq
+    assert re.search(r"#define VQ_RHT_FORWARD 0\b", src) and re.search(r"#define VQ_RHT_INVERSE 1\b", src)
+    assert int(re.search(r"#define VQ_RHT_MAX_SHARDS (\d+)", src).group(1)) == vq.VQ_RHT_MAX_SHARDS
+
+
 @pytest.mark.parametrize("wl", [w for w in vqsynth.WORKLOADS if isinstance(vqsynth.WORKLOADS[w]["bits"], int)])
 def test_compressed_bytes_match_oracle(L, wl):
     """The library's byte count equals the oracle's closed form for every
