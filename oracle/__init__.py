@@ -19,7 +19,8 @@ from the two source pages:
   which passes an inverse residual scale.
 * orka README, quick start: the ``rvq-12-4`` quant mode (a 12-bit primary
   stage and a 4-bit residual stage, about 2 bits per weight); "How it works"
-  and the ``correct`` command: the decode may add a sparse correction.
+  and the ``correct`` command of its CLI: the decode may add a sparse
+  correction, and ``correct`` adds a low-rank or sparse correction.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
 leg may import this package.  It shares no code with the HIP library and
@@ -47,6 +48,8 @@ __all__ = [
     "dequant_exact",
     "dequant_fp16",
     "sparse_dense",
+    "lowrank_dense",
+    "lowrank_bound",
     "matmul_ref",
     "within_tolerance",
     "rht_blocks",
@@ -153,7 +156,7 @@ def n_scale_blocks(k_in: int, scale_block: int) -> int:
 def dequant_exact(n_out: int, k_in: int, indices: Sequence[np.ndarray],
                   codebooks: Sequence[np.ndarray], scales: np.ndarray,
                   scale_block: int, stage_scales: Optional[Sequence[float]] = None,
-                  sparse=None) -> np.ndarray:
+                  sparse=None, lowrank=None) -> np.ndarray:
     """Dequantized weight, float64, shape ``[n_out, k_in]``.
 
     orka README, "How it works": a group decodes to the scale times the sum of
@@ -182,6 +185,18 @@ def dequant_exact(n_out: int, k_in: int, indices: Sequence[np.ndarray],
     stage order starting from stage 0's product, each addition rounded to
     float64, then one float64 multiplication by the block scale.  With every
     r_t = 1 this is the exact value above, bit for bit.
+
+    ``sparse`` (CSR ``(rowptr, col, val)``, fp16 values) is the sparse
+    correction of orka's decode ("How it works"): each entry is added to its
+    weight after the block scale, a row's entries in storage order.
+
+    ``lowrank`` (``(U, V)``: fp16 ``U [n_out, r]`` and ``V [r, k_in]``) is
+    the low-rank correction of orka's ``correct`` command (CLI), whose form
+    the pages do not give.  Reading: the correction is the product U V added
+    to the decoded weight (after the sparse entries), w += sum_j U[:, j]
+    V[j, :], each product exact in float64 (11 + 11 significant bits) and the
+    rank-one terms added in order j = 0, 1, ..., each addition rounded to
+    float64.
     """
     if k_in % GROUP:
         raise ValueError("k_in must be a multiple of 8")
@@ -214,6 +229,10 @@ def dequant_exact(n_out: int, k_in: int, indices: Sequence[np.ndarray],
         for r in range(n_out):
             for j in range(rowptr[r], rowptr[r + 1]):
                 w[r, col[j]] = w[r, col[j]] + val[j]
+    if lowrank is not None:
+        u, v = _check_lowrank(n_out, k_in, lowrank)
+        for j in range(u.shape[1]):
+            w = w + np.outer(u[:, j], v[j])  # exact products, one rounding per addition
     return w
 
 
@@ -243,20 +262,60 @@ def sparse_dense(n_out: int, k_in: int, sparse) -> np.ndarray:
     return d
 
 
+def _check_lowrank(n_out: int, k_in: int, lowrank):
+    u, v = lowrank
+    u = np.asarray(u, dtype=np.float16).astype(np.float64)
+    v = np.asarray(v, dtype=np.float16).astype(np.float64)
+    if u.ndim != 2 or v.ndim != 2 or u.shape[0] != n_out or v.shape[1] != k_in or u.shape[1] != v.shape[0]:
+        raise ValueError("low-rank factors must be U [n_out, r] and V [r, k_in]")
+    if u.shape[1] < 1:
+        raise ValueError("rank must be at least 1")
+    return u, v
+
+
+def lowrank_dense(n_out: int, k_in: int, lowrank) -> np.ndarray:
+    """The low-rank correction alone, U V, as a float64 [n_out, k_in]
+    matrix (rank-one terms added in order j = 0, 1, ...)."""
+    u, v = _check_lowrank(n_out, k_in, lowrank)
+    d = np.zeros((n_out, k_in), dtype=np.float64)
+    for j in range(u.shape[1]):
+        d = d + np.outer(u[:, j], v[j])
+    return d
+
+
+def lowrank_bound(x: np.ndarray, lowrank) -> np.ndarray:
+    """Error scale of applying the low-rank correction through its factors,
+    y += (x V^T) U^T: ``bound[b, r] = sum_j |U[r, j]| sum_k |V[j, k] x[b, k]|``.
+
+    Reading: the pages fix no precision for the correction; a product that
+    never forms U V carries rounding relative to this scale, not to
+    sum_k |(U V)[r, k] x[b, k]| (which cancellation in U V can make much
+    smaller), so the matmul acceptance bound of a weight with a low-rank
+    correction adds this term to :func:`matmul_ref`'s."""
+    x64 = np.asarray(x, dtype=np.float64)
+    if x64.ndim == 1:
+        x64 = x64[None, :]
+    u, v = lowrank
+    u = np.asarray(u, dtype=np.float16).astype(np.float64)
+    v = np.asarray(v, dtype=np.float16).astype(np.float64)
+    return (np.abs(x64) @ np.abs(v).T) @ np.abs(u).T
+
+
 def dequant_fp16(n_out, k_in, indices, codebooks, scales, scale_block,
-                 stage_scales=None, sparse=None) -> np.ndarray:
+                 stage_scales=None, sparse=None, lowrank=None) -> np.ndarray:
     """fp16 dequantized weight: the float64 value rounded once to nearest-even.
 
     Reading: the pages fix no rounding; the result is the float64 value of
     :func:`dequant_exact` (exact without stage scales, the stated evaluation
-    order with them, plus the sparse correction if any) converted once to
+    order with them, plus the sparse and low-rank corrections if any)
+    converted once to
     IEEE binary16 with
     round-to-nearest-even (numpy's float64 -> float16 cast rounds once; the
     tests check it against Python's own half-float packing).  Subnormals are
     kept, overflow gives +/-inf, a zero result keeps the sign IEEE gives it.
     """
     return dequant_exact(n_out, k_in, indices, codebooks, scales, scale_block,
-                         stage_scales, sparse).astype(np.float16)
+                         stage_scales, sparse, lowrank).astype(np.float16)
 
 
 # --------------------------------------------------------------------------
@@ -427,7 +486,8 @@ def _stage_widths(n_stages: int, bits) -> list:
 
 
 def compressed_bytes(n_out: int, k_in: int, n_stages: int, bits: Union[int, Sequence[int]],
-                     scale_block: int, include_codebooks: bool = True, sparse_nnz: int = 0) -> int:
+                     scale_block: int, include_codebooks: bool = True, sparse_nnz: int = 0,
+                     lowrank_rank: int = 0) -> int:
     """Bytes of the stored weight: index planes, fp16 scales and (optionally)
     the fp16 codebooks, each counted once.
 
@@ -437,7 +497,8 @@ def compressed_bytes(n_out: int, k_in: int, n_stages: int, bits: Union[int, Sequ
     group, 12-bit = one byte per group plus one byte per two groups (ceil),
     8-bit = one byte per group, 4-bit = one byte per two groups (ceil).
     A sparse correction of ``sparse_nnz`` entries adds its CSR arrays: int32
-    row pointers (n_out + 1), int32 columns and fp16 values.
+    row pointers (n_out + 1), int32 columns and fp16 values.  A low-rank
+    correction of rank r adds its fp16 factors: 2 r (n_out + k_in) bytes.
     """
     groups = n_out * (k_in // GROUP)
     per_width = {4: (groups + 1) // 2, 8: groups, 12: groups + (groups + 1) // 2, 16: 2 * groups}
@@ -447,6 +508,8 @@ def compressed_bytes(n_out: int, k_in: int, n_stages: int, bits: Union[int, Sequ
         total += sum((1 << b) * GROUP * 2 for b in widths)
     if sparse_nnz:
         total += 4 * (n_out + 1) + (4 + 2) * sparse_nnz
+    if lowrank_rank:
+        total += 2 * lowrank_rank * (n_out + k_in)
     return total
 
 
