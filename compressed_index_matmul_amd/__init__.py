@@ -51,6 +51,7 @@ _ptr4 = ctypes.c_void_p * MAX_STAGES
 _int4 = ctypes.c_int32 * MAX_STAGES
 _flt4 = ctypes.c_float * MAX_STAGES
 VQ_STAGE_SCALES = 1
+VQ_MAX_LR_RANK = 256
 
 
 class VQWeightDesc(ctypes.Structure):
@@ -74,6 +75,10 @@ class VQWeightDesc(ctypes.Structure):
         ("sp_rowptr", ctypes.c_void_p),
         ("sp_col", ctypes.c_void_p),
         ("sp_val", ctypes.c_void_p),
+        ("lr_rank", ctypes.c_int32),
+        ("lr_reserved", ctypes.c_int32),
+        ("lr_u", ctypes.c_void_p),
+        ("lr_v", ctypes.c_void_p),
     ]
 
 
@@ -162,13 +167,15 @@ class VQWeight:
     raw device addresses.  ``stage_bits`` (optional) gives each stage its own
     index width (4, 8, 12 or 16); ``stage_scales`` (optional) one float
     residual scale per stage; ``sparse`` (optional) a CSR correction
-    ``(rowptr, col, val)`` added to the decoded weight.
+    ``(rowptr, col, val)`` added to the decoded weight; ``lowrank``
+    (optional) fp16 factors ``(U [n_out, r], V [r, k_in])`` whose product is
+    added to it.
     """
 
     def __init__(self, n_out: int, k_in: int, n_stages: int, idx_bits: int, scale_block: int,
                  codebooks: Sequence, scales, lo: Sequence = (), hi: Sequence = (),
                  idx16: Sequence = (), device="cuda", stage_bits: Optional[Sequence[int]] = None,
-                 stage_scales: Optional[Sequence[float]] = None, sparse=None):
+                 stage_scales: Optional[Sequence[float]] = None, sparse=None, lowrank=None):
         import torch
         self.n_out, self.k_in, self.n_stages, self.idx_bits = n_out, k_in, n_stages, idx_bits
         self.scale_block = scale_block
@@ -187,6 +194,10 @@ class VQWeight:
             self.sparse = (_as_device(np.asarray(rp, np.int32), self.device, torch.int32),
                            _as_device(np.asarray(cl, np.int32), self.device, torch.int32),
                            _as_device(np.asarray(vl, np.float16), self.device, torch.float16))
+        self.lowrank = None
+        if lowrank is not None:
+            u, v = lowrank
+            self.lowrank = (_as_device(u, self.device, torch.float16), _as_device(v, self.device, torch.float16))
         self._check_arrays()
         self.desc = VQWeightDesc()
         self._fill_desc()
@@ -239,6 +250,16 @@ class VQWeight:
                 raise ValueError("sparse columns and values differ in length")
             for name, t in (("sparse col", cl), ("sparse val", vl)):
                 need(t, "entries", name, cl.numel())
+        if self.lowrank is not None:
+            u, v = self.lowrank
+            if u.dim() != 2 or v.dim() != 2 or u.shape[0] != n or v.shape[1] != k or u.shape[1] != v.shape[0]:
+                raise ValueError(f"low-rank factors must be U [{n}, r] and V [r, {k}], got "
+                                 f"{tuple(u.shape)} and {tuple(v.shape)}")
+            r = u.shape[1]
+            if not 1 <= r <= VQ_MAX_LR_RANK:
+                raise ValueError(f"low-rank rank {r} is outside 1..{VQ_MAX_LR_RANK}")
+            need(u, "fp16 values", "lowrank U", n * r)
+            need(v, "fp16 values", "lowrank V", r * k)
 
     def _fill_desc(self):
         d = self.desc
@@ -260,6 +281,10 @@ class VQWeight:
         d.sp_rowptr = self.sparse[0].data_ptr() if nnz else None
         d.sp_col = self.sparse[1].data_ptr() if nnz else None
         d.sp_val = self.sparse[2].data_ptr() if nnz else None
+        d.lr_rank = 0 if self.lowrank is None else int(self.lowrank[0].shape[1])
+        d.lr_reserved = 0
+        d.lr_u = self.lowrank[0].data_ptr() if self.lowrank is not None else None
+        d.lr_v = self.lowrank[1].data_ptr() if self.lowrank is not None else None
 
     def clone(self) -> "VQWeight":
         """Another copy of the same weight at distinct device addresses."""
@@ -271,13 +296,14 @@ class VQWeight:
         w.hi = [None if v is None else v.clone() for v in self.hi]
         w.idx16 = [None if v is None else v.clone() for v in self.idx16]
         w.sparse = None if self.sparse is None else tuple(t.clone() for t in self.sparse)
+        w.lowrank = None if self.lowrank is None else tuple(t.clone() for t in self.lowrank)
         w.desc = VQWeightDesc()
         w._fill_desc()
         return w
 
     def nbytes_device(self) -> int:
         ts = [*self.codebooks, self.scales, *[v for v in self.lo + self.hi + self.idx16 if v is not None],
-              *(self.sparse or ())]
+              *(self.sparse or ()), *(self.lowrank or ())]
         return sum(t.numel() * t.element_size() for t in ts)
 
     def ref(self):

@@ -24,7 +24,7 @@ ARCH = "gfx950"
 
 SOURCES = ["vqmm_api.cpp", "k_dequant.hip", "k_rht.hip", "k_gemv.hip", "k_gemv_ladder.hip", "k_gemm.hip",
            "k_gemm_ladder.hip", "k_sparse.hip",
-           "k_gemv_sparse.hip", "k_gemv_l2.hip", "k_gemv_cbs.hip"]
+           "k_gemv_sparse.hip", "k_gemv_l2.hip", "k_gemv_cbs.hip", "k_lowrank.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

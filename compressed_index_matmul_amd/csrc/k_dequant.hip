@@ -9,7 +9,8 @@
 // so the result is the correctly rounded value whatever the summation order.  Write-bandwidth bound.  A
 // sparse correction (orka README, "How it works": the decode plus a sparse
 // correction) is added to the float64 value entry by entry, in storage
-// order, before the one rounding.
+// order, then a low-rank correction's terms U[r][j] V[j][c] in order of j
+// (orka README, CLI: the correct command), before the one rounding.
 //
 // Residual ladders (per-stage widths) and stage scales (GLQ page, "Inference
 // kernels": the inverse residual scale of the two-stage call) take the
@@ -48,7 +49,24 @@ struct DequantArgs {
   const int32_t *sp_rowptr;
   const int32_t *sp_col;
   const uint16_t *sp_val;
+  int lr_rank;              // low-rank correction U V, 0 = none
+  const uint16_t *lr_u;     // fp16 [N][lr_rank]
+  const uint16_t *lr_v;     // fp16 [lr_rank][K]
 };
+
+// The low-rank terms of group g of row r added to its float64 values: for
+// j = 0, 1, ... in order, wv[q] += U[r][j] V[j][8g + q] (the fp16 product
+// is exact in float64, so a fused multiply-add rounds the same).
+__device__ __forceinline__ void add_lowrank(const DequantArgs &a, int64_t r, int g, double (&wv)[8]) {
+  const uint16_t *ur = a.lr_u + r * a.lr_rank;
+  for (int j = 0; j < a.lr_rank; ++j) {
+    const double u = (double)h2f(ur[j]);
+    const uint4 h = *reinterpret_cast<const uint4 *>(a.lr_v + (int64_t)j * a.k + 8 * g);
+    const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) wv[q] = wv[q] + u * (double)h2f((hw[q >> 1] >> (16 * (q & 1))) & 0xffffu);
+  }
+}
 
 // The eight fp16 results of a group, two per word: one test for the group,
 // the hardware rounding when all eight are finite and below 65504, else the
@@ -118,6 +136,7 @@ __global__ __launch_bounds__(256) void k_unpack_dequant(DequantArgs a) {
         if (q == c) wv[q] = wv[q] + v;
     }
   }
+  if (a.lr_rank > 0) add_lowrank(a, r, g, wv);
   reinterpret_cast<uint4 *>(a.w_out + r * (int64_t)a.k)[g] = round_group_f16(wv);
 }
 
@@ -162,6 +181,7 @@ __device__ __forceinline__ void dequant_group(const DequantArgs &a, const uint4 
         if (q == c) wv[q] = wv[q] + sv;
     }
   }
+  if (a.lr_rank > 0) add_lowrank(a, r, g, wv);
   reinterpret_cast<uint4 *>(a.w_out + r * (int64_t)a.k)[g] = round_group_f16(wv);
 }
 
@@ -298,6 +318,9 @@ hipError_t launch_unpack_dequant(const WView &w, uint16_t *idx_out, uint16_t *w_
   a.sp_rowptr = w.sp_rowptr;
   a.sp_col = w.sp_col;
   a.sp_val = w.sp_val;
+  a.lr_rank = w.lr_rank;
+  a.lr_u = w.lr_u;
+  a.lr_v = w.lr_v;
   if (launch_dequant_lds(w, a, s)) return hipGetLastError();
   const unsigned blocks = (unsigned)((a.total + 255) / 256);
   if (!plain_format(w))

@@ -120,7 +120,9 @@ hipError_t launch_gemv_token(const WView &w, const void *x, int xt, float *y, hi
   return hipGetLastError();
 }
 
-bool gemv_rht_takes(const WView &w) { return w.sp_nnz == 0 && (gemv_cbs_rht_takes(w) || gemv_l2_takes(w)); }
+bool gemv_rht_takes(const WView &w) {
+  return w.sp_nnz == 0 && w.lr_rank == 0 && (gemv_cbs_rht_takes(w) || gemv_l2_takes(w));
+}
 
 hipError_t launch_gemv_rht_token(const WView &w, const void *x, int xt, const int8_t *signs, int max_block, float *y,
                                  hipStream_t s) {

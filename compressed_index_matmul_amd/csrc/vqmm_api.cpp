@@ -52,6 +52,13 @@ int check_weight(const vq_weight *w, WView *v) {
     if (!w->sp_rowptr || !w->sp_col || !w->sp_val) return VQ_ERR_NULL;
     if (!aligned16(w->sp_rowptr) || !aligned16(w->sp_col) || !aligned16(w->sp_val)) return VQ_ERR_ALIGN;
   }
+  if (w->lr_rank < 0 || w->lr_rank > VQ_MAX_LR_RANK || w->lr_reserved != 0) return VQ_ERR_SHAPE;
+  if (w->lr_rank > 0) {
+    if (!w->lr_u || !w->lr_v) return VQ_ERR_NULL;
+    if (!aligned16(w->lr_u) || !aligned16(w->lr_v)) return VQ_ERR_ALIGN;
+    if ((int64_t)w->lr_rank * w->n_out >= ((int64_t)1 << 31) || (int64_t)w->lr_rank * w->k_in >= ((int64_t)1 << 31))
+      return VQ_ERR_SHAPE;
+  }
   if (v) {
     *v = WView{};
     v->n = w->n_out;
@@ -83,11 +90,34 @@ int check_weight(const vq_weight *w, WView *v) {
     v->sp_rowptr = w->sp_nnz > 0 ? w->sp_rowptr : nullptr;
     v->sp_col = w->sp_nnz > 0 ? w->sp_col : nullptr;
     v->sp_val = w->sp_nnz > 0 ? w->sp_val : nullptr;
+    v->lr_rank = w->lr_rank;
+    v->lr_u = w->lr_rank > 0 ? w->lr_u : nullptr;
+    v->lr_v = w->lr_rank > 0 ? w->lr_v : nullptr;
   }
   return VQ_OK;
 }
 
 int map_hip(hipError_t e) { return e == hipSuccess ? VQ_OK : VQ_ERR_HIP; }
+
+// Workspace of the many-token product: the main product's part, then the
+// low-rank correction's t (both 256-byte multiples).
+size_t total_workspace_bytes(const WView &v, int m) { return gemm_workspace_bytes(v, m) + lowrank_workspace_bytes(v, m); }
+
+// Grid limit of the low-rank kernels for many tokens (64-token tiles in
+// grid.y).
+bool lowrank_rows_fit(const WView &v, int m) { return v.lr_rank == 0 || (m + 63) / 64 <= 65535; }
+
+// The many-token product with its corrections; ws holds at least
+// total_workspace_bytes(v, m) bytes (null when that is 0).
+int run_gemm(const WView &v, const uint16_t *x, int m, float *y, void *ws, hipStream_t s) {
+  const size_t main_bytes = gemm_workspace_bytes(v, m);
+  int st = map_hip(launch_gemm(v, x, m, y, main_bytes > 0 ? ws : nullptr, main_bytes, s));
+  if (st != VQ_OK) return st;
+  st = map_hip(launch_sparse_add(v, x, VQ_BF16, m, y, s));
+  if (st != VQ_OK || v.lr_rank == 0) return st;
+  float *t = reinterpret_cast<float *>(static_cast<char *>(ws) + main_bytes);
+  return map_hip(launch_lowrank_gemm(v, x, m, y, t, s));
+}
 
 }  // namespace
 
@@ -139,6 +169,7 @@ int64_t vq_compressed_bytes(const vq_weight *w) {
     total += ((int64_t)1 << b) * 16;
   }
   if (v.sp_nnz > 0) total += 4 * ((int64_t)v.n + 1) + 6 * (int64_t)v.sp_nnz;
+  if (v.lr_rank > 0) total += 2 * (int64_t)v.lr_rank * ((int64_t)v.n + v.k);
   return total;
 }
 
@@ -174,8 +205,11 @@ int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, f
       if (st != VQ_OK) return st;
     }
   }
-  if (sp_done) return VQ_OK;
-  return map_hip(launch_sparse_add(v, x, x_dtype, batch, y, s));
+  if (!sp_done) {
+    st = map_hip(launch_sparse_add(v, x, x_dtype, batch, y, s));
+    if (st != VQ_OK) return st;
+  }
+  return map_hip(launch_lowrank_tokens(v, x, x_dtype, batch, y, s));
 }
 
 int vq_gemm(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float *y, void *workspace, size_t ws_bytes,
@@ -188,11 +222,9 @@ int vq_gemm(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float *y, voi
   if ((int64_t)m * v.k >= ((int64_t)1 << 31) || (int64_t)m * v.n >= ((int64_t)1 << 31)) return VQ_ERR_SHAPE;
   if (ws_bytes > 0 && !workspace) return VQ_ERR_NULL;
   if (!aligned16(x_bf16) || !aligned16(y) || !aligned16(workspace)) return VQ_ERR_ALIGN;
-  if (ws_bytes < gemm_workspace_bytes(v, m)) return VQ_ERR_WORKSPACE;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  st = map_hip(launch_gemm(v, x_bf16, m, y, workspace, ws_bytes, s));
-  if (st != VQ_OK) return st;
-  return map_hip(launch_sparse_add(v, x_bf16, VQ_BF16, m, y, s));
+  if (!lowrank_rows_fit(v, m)) return VQ_ERR_UNSUPPORTED;
+  if (ws_bytes < total_workspace_bytes(v, m)) return VQ_ERR_WORKSPACE;
+  return run_gemm(v, x_bf16, m, y, workspace, reinterpret_cast<hipStream_t>(stream));
 }
 
 int vq_gemm_noalloc(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float *y, void *stream) {
@@ -203,21 +235,19 @@ int vq_gemm_noalloc(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float
   if (m < 1) return VQ_ERR_SHAPE;
   if ((int64_t)m * v.k >= ((int64_t)1 << 31) || (int64_t)m * v.n >= ((int64_t)1 << 31)) return VQ_ERR_SHAPE;
   if (!aligned16(x_bf16) || !aligned16(y)) return VQ_ERR_ALIGN;
-  const size_t need = gemm_workspace_bytes(v, m);
+  if (!lowrank_rows_fit(v, m)) return VQ_ERR_UNSUPPORTED;
+  const size_t need = total_workspace_bytes(v, m);
   if (need > kGemmScratchBytes) return VQ_ERR_WORKSPACE;
   void *ws = nullptr;
   if (need > 0 && gemm_scratch(&ws) != hipSuccess) return VQ_ERR_HIP;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  st = map_hip(launch_gemm(v, x_bf16, m, y, ws, need > 0 ? kGemmScratchBytes : 0, s));
-  if (st != VQ_OK) return st;
-  return map_hip(launch_sparse_add(v, x_bf16, VQ_BF16, m, y, s));
+  return run_gemm(v, x_bf16, m, y, ws, reinterpret_cast<hipStream_t>(stream));
 }
 
 size_t vq_gemm_workspace_size(const vq_weight *w, int32_t m) {
   WView v;
   if (check_weight(w, &v) != VQ_OK || m < 1) return 0;
   if ((int64_t)m * v.k >= ((int64_t)1 << 31) || (int64_t)m * v.n >= ((int64_t)1 << 31)) return 0;
-  return gemm_workspace_bytes(v, m);
+  return total_workspace_bytes(v, m);
 }
 
 int vq_gemv_rht(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, const int8_t *signs,

@@ -32,6 +32,9 @@ struct WView {
   const int32_t *sp_rowptr;
   const int32_t *sp_col;
   const uint16_t *sp_val;
+  int lr_rank;             // low-rank correction rank (0: none)
+  const uint16_t *lr_u;    // fp16 [n][lr_rank]
+  const uint16_t *lr_v;    // fp16 [lr_rank][k]
 };
 
 // The plain formats the specialised kernels take: every stage of one width
@@ -55,8 +58,9 @@ hipError_t launch_rht(const void *x, int xt, int batch, int n, int nsh, const in
 // *sp_done: the launched kernel also added the sparse correction.
 hipError_t launch_gemv_token(const WView &w, const void *x, int xt, float *y, hipStream_t s, bool *sp_done);
 // The product with the input transform applied inside the decode kernel:
-// whether the weight has such a kernel (16-bit first stage the L2 decode
-// kernel takes, no sparse correction), and one token's launch.
+// whether the weight has such a kernel (a 16-bit weight the sliced or the
+// L2 decode kernel takes, no sparse or low-rank correction), and one token's
+// launch.
 bool gemv_rht_takes(const WView &w);
 hipError_t launch_gemv_rht_token(const WView &w, const void *x, int xt, const int8_t *signs, int max_block, float *y,
                                  hipStream_t s);
@@ -77,6 +81,13 @@ hipError_t gemm_scratch(void **ptr);
 // m tokens of x (VQ_F32 / VQ_BF16); after the main product on the same
 // stream.  No-op without a correction.
 hipError_t launch_sparse_add(const WView &w, const void *x, int xt, int m, float *y, hipStream_t s);
+// The low-rank correction's term y += (x V^T) U^T, after the main product on
+// the same stream; no-op without one.  Tokens (1..16, VQ_F32 / VQ_BF16):
+// one launch, no scratch.  Many bf16 tokens: t [m][lr_rank] in the caller's
+// workspace (lowrank_workspace_bytes), two launches.
+hipError_t launch_lowrank_tokens(const WView &w, const void *x, int xt, int batch, float *y, hipStream_t s);
+size_t lowrank_workspace_bytes(const WView &w, int m);
+hipError_t launch_lowrank_gemm(const WView &w, const uint16_t *x, int m, float *y, float *t, hipStream_t s);
 
 
 }  // namespace vqmm

@@ -42,11 +42,13 @@
 extern "C" {
 #endif
 
-#define VQMM_VERSION 4
+#define VQMM_VERSION 5
 #define VQ_MAX_STAGES 4
 
 /* vq_weight.flags: stage_scale[] holds one residual scale per stage. */
 #define VQ_STAGE_SCALES 1
+/* Largest rank of a low-rank correction (vq_weight.lr_rank). */
+#define VQ_MAX_LR_RANK 256
 
 /* Status codes returned by every entry point. */
 typedef enum vq_status {
@@ -103,6 +105,16 @@ typedef enum vq_dtype { VQ_F32 = 0, VQ_BF16 = 1 } vq_dtype;
  *               < k_in.  Kernels clamp row ranges to [0, sp_nnz] and skip
  *               columns >= k_in, so inconsistent data gives wrong values,
  *               never an access outside these arrays.
+ * lr_*        : optional low-rank correction added to the decoded weight
+ *               (orka README, CLI: the correct command adds a low-rank or
+ *               sparse correction; the pages give no form, this is the
+ *               library's reading): fp16 factors U = lr_u [n_out][lr_rank]
+ *               and V = lr_v [lr_rank][k_in], both row-major,
+ *                 w[r, c] += sum_j U[r][j] V[j][c],
+ *               after the sparse entries.  The products never form U V:
+ *               they compute t = x V^T, then y += t U^T, in fp32 with a
+ *               fixed order, so the error of this term is bounded relative
+ *               to sum_j |U[r][j]| sum_c |V[j][c] x[c]| (see vq_gemv).
  * Unused pointer slots and unused stage_bits / stage_scale entries are
  * ignored.  A zero-initialised descriptor with the first block filled in
  * describes a uniform ladder without stage scales or correction.
@@ -126,6 +138,10 @@ typedef struct vq_weight {
   const int32_t *sp_rowptr;          /* [n_out + 1] (when sp_nnz > 0) */
   const int32_t *sp_col;             /* [sp_nnz] */
   const uint16_t *sp_val;            /* fp16 bits [sp_nnz] */
+  int32_t lr_rank;                   /* rank of the low-rank correction, 0 = none, 1..VQ_MAX_LR_RANK */
+  int32_t lr_reserved;               /* set to 0 */
+  const uint16_t *lr_u;              /* fp16 bits [n_out][lr_rank] (when lr_rank > 0) */
+  const uint16_t *lr_v;              /* fp16 bits [lr_rank][k_in] */
 } vq_weight;
 
 /* Library version (VQMM_VERSION).  Host only. */
@@ -141,8 +157,9 @@ int vq_validate(const vq_weight *w);
 /* Stored bytes of the weight: index planes + fp16 scales + fp16 codebooks,
  * each counted once (per group and stage: 16-bit 2 bytes, 12-bit 1.5, 8-bit
  * 1, 4-bit 0.5, nibble planes rounded up), plus a sparse correction's
- * 4 (n_out + 1) + 6 sp_nnz bytes.  Negative vq_status on an invalid
- * descriptor.  Host only. */
+ * 4 (n_out + 1) + 6 sp_nnz bytes and a low-rank correction's 2 lr_rank
+ * (n_out + k_in) bytes.  Negative vq_status on an invalid descriptor.  Host
+ * only. */
 int64_t vq_compressed_bytes(const vq_weight *w);
 
 /*
@@ -158,7 +175,9 @@ int64_t vq_compressed_bytes(const vq_weight *w);
  *             (exact), summed from stage 0 up with float64 rounding, times
  *             the block scale in float64, then rounded once to fp16.  A
  *             sparse correction is added to that float64 value, entry by
- *             entry in storage order, before the one rounding.
+ *             entry in storage order, then a low-rank correction's terms
+ *             U[r][j] V[j][c] (exact products) for j = 0, 1, ... in order,
+ *             each addition rounded to float64, before the one rounding.
  * At least one output must be non-NULL.  Bit-exact.
  */
 int vq_unpack_dequant(const vq_weight *w, uint16_t *idx_out, uint16_t *w_out, void *stream);
@@ -179,7 +198,10 @@ int vq_unpack_dequant(const vq_weight *w, uint16_t *idx_out, uint16_t *w_out, vo
  * products, one launch for all tokens.  Other 2..16 bf16 tokens run on bf16
  * matrix cores as vq_gemm does, with the same error behaviour.  A sparse
  * correction adds x S^T (fp16 values times x, fp32 sums) in a second launch
- * on the same stream.
+ * on the same stream.  A low-rank correction adds (x V^T) U^T in one more
+ * launch with no scratch: every workgroup forms t = x V^T for all tokens
+ * itself (fp32, fixed order), then adds t U^T to its rows of y; its term
+ * is within 2e-3 * sum_j |U[r][j]| sum_c |V[j][c] x[c]| (k_in <= 16384).
  */
 int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, float *y,
             void *stream);
@@ -217,7 +239,10 @@ int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, f
  * average out and outputs stay well inside 2e-3 * sum_k |w x| + 1e-6 (about
  * 0.07 of it at k_in = 4096 for N(0,1) inputs); a one-hot or very short x
  * can exceed that tighter bound.  A sparse correction adds x S^T exactly as
- * vq_gemv does (fp32, not rounded to bf16).
+ * vq_gemv does (fp32, not rounded to bf16).  A low-rank correction takes
+ * two more launches: t = x V^T into the workspace (m * lr_rank floats after
+ * the fp16 path's part, 256-byte aligned), then y += t U^T, both fp32 with
+ * a fixed order, within the same bound as vq_gemv's low-rank term.
  */
 int vq_gemm(const vq_weight *w, const uint16_t *x_bf16, int32_t m, float *y, void *workspace, size_t ws_bytes,
             void *stream);
@@ -305,12 +330,20 @@ int rht_apply_shards(const void *x, int32_t x_dtype, int32_t batch, int32_t n, i
  *   y[b] = dequant(W) . RHT(x[b]),  RHT as rht_apply with signs, max_block,
  * for 1..16 tokens, with no buffer for the transformed x: every workgroup
  * transforms its own copy in LDS.  Taken for the weights the 16-bit decode
- * kernel serves: a 16-bit first stage, at most one 8- or 16-bit residual
- * stage, stage scales allowed, K % 2048 == 0 with K <= 32768 (26624 with a
- * 16-bit and 28672 with an 8-bit residual), scale blocks of 32-column units
- * that divide 2048 or cover the row, and no sparse correction; any other
- * weight returns VQ_ERR_UNSUPPORTED with nothing launched (use rht_apply,
- * then vq_gemv).
+ * kernels serve, without a sparse or low-rank correction:
+ *  - one 16-bit stage with one scale per row, n_out * k_in >= 2^25, k_in a
+ *    multiple of 1024 up to 37632 whose 1024-column count is 1, 2, 4 or 8
+ *    times one of 1, 2, 4, 7, 8 (the codebook-sliced kernel), or
+ *  - a 16-bit first stage, at most one 8- or 16-bit residual stage, stage
+ *    scales allowed, K % 2048 == 0 with K <= 32768 (26624 with a 16-bit and
+ *    28672 with an 8-bit residual), scale blocks of 32-column units that
+ *    divide 2048 or cover the row (the codebook-gather kernel).
+ * Any other weight returns VQ_ERR_UNSUPPORTED with nothing launched (use
+ * rht_apply, then vq_gemv).  The 8- and 12-bit decode kernel keeps up to
+ * 128 KiB of codebooks in LDS; a transform inside it would also need the
+ * row of fp32 x there (4 bytes a column), which fits beside two 12-bit
+ * codebooks only for rows of up to about 6000 columns.  It is not built:
+ * those weights take the separate launch.
  *   x         : [batch][k_in], VQ_F32 or VQ_BF16, 16-byte aligned
  *   signs     : int8 [k_in], each +1 or -1, 16-byte aligned
  *   max_block : power of two, 1..16384 (VQ_ERR_SHAPE otherwise)

@@ -400,3 +400,66 @@ def test_sparse_bytes_by_hand():
     # 3 rows, 2 entries: 4 int32 row pointers + 2 int32 columns + 2 fp16 values
     base = oracle.compressed_bytes(3, 16, 1, 8, 16)
     assert oracle.compressed_bytes(3, 16, 1, 8, 16, sparse_nnz=2) == base + 16 + 8 + 4
+
+
+def lowrank_desc(rank=16, n=64, k=64):
+    d = fake_desc(n=n, k=k)
+    d.lr_rank, d.lr_u, d.lr_v = rank, FAKE, FAKE
+    return d
+
+
+def test_valid_lowrank(L):
+    for rank in (1, 7, 256):
+        assert L.vq_validate(ctypes.byref(lowrank_desc(rank))) == VQ_OK
+    d = fake_desc()
+    d.lr_u = FAKE + 3  # rank 0: the pointers are ignored
+    assert L.vq_validate(ctypes.byref(d)) == VQ_OK
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda d: setattr(d, "lr_rank", -1), VQ_ERR_SHAPE),
+    (lambda d: setattr(d, "lr_rank", 257), VQ_ERR_SHAPE),
+    (lambda d: setattr(d, "lr_reserved", 1), VQ_ERR_SHAPE),
+    (lambda d: setattr(d, "lr_u", None), VQ_ERR_NULL),
+    (lambda d: setattr(d, "lr_v", None), VQ_ERR_NULL),
+    (lambda d: setattr(d, "lr_u", FAKE + 2), VQ_ERR_ALIGN),
+    (lambda d: setattr(d, "lr_v", FAKE + 8), VQ_ERR_ALIGN),
+])
+def test_invalid_lowrank(L, mutate, code):
+    d = lowrank_desc()
+    mutate(d)
+    assert L.vq_validate(ctypes.byref(d)) == code
+    assert L.vq_gemv(ctypes.byref(d), FAKE, 1, 1, FAKE, None) == code
+    assert L.vq_gemm(ctypes.byref(d), FAKE, 64, FAKE, None, 0, None) == code
+    assert L.vq_gemm_noalloc(ctypes.byref(d), FAKE, 64, FAKE, None) == code
+    assert L.vq_unpack_dequant(ctypes.byref(d), FAKE, FAKE, None) == code
+
+
+@pytest.mark.parametrize("rank", [1, 32, 256])
+def test_lowrank_bytes_match_oracle(L, rank):
+    d = lowrank_desc(rank, n=4096, k=14336)
+    d.scale_block = 128
+    assert L.vq_compressed_bytes(ctypes.byref(d)) == oracle.compressed_bytes(4096, 14336, 1, 12, 128,
+                                                                             lowrank_rank=rank)
+
+
+def test_lowrank_workspace(L):
+    """The many-token product keeps t = x V^T (m x rank floats) in the
+    workspace after the main product's part, so even the bf16 path (64
+    tokens or fewer) needs one; too little is refused before any HIP call."""
+    d = lowrank_desc(32, n=4096, k=4096)
+    d.n_stages, d.scale_block = 2, 128
+    for t in range(2):
+        d.codebook[t], d.idx_lo[t], d.idx_hi[t] = FAKE, FAKE, FAKE
+    plain = fake_desc(n=4096, k=4096, stages=2, bits=12, bs=128)
+    for m in (1, 40, 300, 2048):
+        extra = (m * 32 * 4 + 255) // 256 * 256
+        assert L.vq_gemm_workspace_size(ctypes.byref(d), m) == L.vq_gemm_workspace_size(ctypes.byref(plain), m) + extra
+        need = L.vq_gemm_workspace_size(ctypes.byref(d), m)
+        assert L.vq_gemm(ctypes.byref(d), FAKE, m, FAKE, FAKE, need - 256, None) == VQ_ERR_WORKSPACE
+
+
+def test_gemv_rht_refuses_lowrank(L):
+    d = fake_desc(n=8192, k=4096, bits=16, bs=4096)
+    d.lr_rank, d.lr_u, d.lr_v = 8, FAKE, FAKE
+    assert L.vq_gemv_rht(ctypes.byref(d), FAKE, 1, 1, FAKE, 4096, FAKE, None) == VQ_ERR_UNSUPPORTED

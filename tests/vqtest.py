@@ -26,7 +26,7 @@ def device_weight(sw: vqsynth.SynthWeight, device="cuda"):
     return VQWeight(sw.n_out, sw.k_in, sw.n_stages, sw.idx_bits, sw.scale_block,
                     codebooks=sw.codebooks, scales=sw.scales, lo=sw.lo, hi=sw.hi,
                     idx16=sw.idx16, device=device, stage_bits=sw.stage_bits,
-                    stage_scales=sw.stage_scales, sparse=sw.sparse)
+                    stage_scales=sw.stage_scales, sparse=sw.sparse, lowrank=sw.lowrank)
 
 
 def sparse_rows(sw: vqsynth.SynthWeight, rows):
@@ -43,6 +43,25 @@ def sparse_rows(sw: vqsynth.SynthWeight, rows):
             np.concatenate(parts_v) if parts_v else np.zeros(0, np.float16))
 
 
+def lowrank_rows(sw: vqsynth.SynthWeight, rows):
+    """The low-rank factors restricted to `rows` of U (None: all)."""
+    if sw.lowrank is None or rows is None:
+        return sw.lowrank
+    u, v = sw.lowrank
+    return u[np.asarray(rows)], v
+
+
+def product_ref(sw: vqsynth.SynthWeight, x64, rows=None, idx=None):
+    """(y_ref, bound) of x against the selected rows: the oracle's exact
+    product and its acceptance scale, with the low-rank correction's
+    factor-wise scale added when the weight has one."""
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw, rows, idx), x64)
+    lr = lowrank_rows(sw, rows)
+    if lr is not None:
+        bound = bound + oracle.lowrank_bound(x64, lr)
+    return y_ref, bound
+
+
 def oracle_indices(sw: vqsynth.SynthWeight):
     return [oracle.unpack_indices(b, sw.n_groups, lo=sw.lo[t], hi=sw.hi[t], idx16=sw.idx16[t])
             for t, b in enumerate(sw.widths)]
@@ -54,11 +73,11 @@ def oracle_w64(sw: vqsynth.SynthWeight, rows=None, idx=None):
     g = sw.k_in // 8
     if rows is None:
         return oracle.dequant_exact(sw.n_out, sw.k_in, idx, sw.codebooks, sw.scales, sw.scale_block,
-                                    sw.stage_scales, sw.sparse)
+                                    sw.stage_scales, sw.sparse, sw.lowrank)
     rows = np.asarray(rows)
     sub = [i.reshape(sw.n_out, g)[rows].reshape(-1) for i in idx]
     return oracle.dequant_exact(len(rows), sw.k_in, sub, sw.codebooks, sw.scales[rows], sw.scale_block,
-                                sw.stage_scales, sparse_rows(sw, rows))
+                                sw.stage_scales, sparse_rows(sw, rows), lowrank_rows(sw, rows))
 
 
 def oracle_w16(sw: vqsynth.SynthWeight, rows=None, idx=None):
@@ -66,11 +85,11 @@ def oracle_w16(sw: vqsynth.SynthWeight, rows=None, idx=None):
     g = sw.k_in // 8
     if rows is None:
         return oracle.dequant_fp16(sw.n_out, sw.k_in, idx, sw.codebooks, sw.scales, sw.scale_block,
-                                   sw.stage_scales, sw.sparse)
+                                   sw.stage_scales, sw.sparse, sw.lowrank)
     rows = np.asarray(rows)
     sub = [i.reshape(sw.n_out, g)[rows].reshape(-1) for i in idx]
     return oracle.dequant_fp16(len(rows), sw.k_in, sub, sw.codebooks, sw.scales[rows], sw.scale_block,
-                               sw.stage_scales, sparse_rows(sw, rows))
+                               sw.stage_scales, sparse_rows(sw, rows), lowrank_rows(sw, rows))
 
 
 def sample_rows(n: int, count: int, seed: int):
@@ -103,7 +122,6 @@ def assert_all_rows(y, sw: vqsynth.SynthWeight, x64, what="", chunk=4096):
     worst = 0.0
     for r0 in range(0, sw.n_out, chunk):
         rows = np.arange(r0, min(r0 + chunk, sw.n_out))
-        w64 = oracle_w64(sw, rows, idx)
-        y_ref, bound = oracle.matmul_ref(w64, x64)
+        y_ref, bound = product_ref(sw, x64, rows, idx)
         worst = max(worst, assert_within(y[:, rows], y_ref, bound, f"{what} rows {r0}.."))
     return worst
