@@ -39,7 +39,9 @@ __all__ = [
     "rht_apply_shards", "vq_gemv_rht", "VQ_F32", "VQ_BF16", "VQ_STAGE_SCALES", "VQ_RHT_MAX_SHARDS", "EXPORTS",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvqmm.so")
+# VQMM_LIBRARY names another build of the same library (the host-sanitized
+# one the CPU tests load); by default the in-tree libvqmm.so.
+LIB_PATH = os.environ.get("VQMM_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvqmm.so")
 VQ_F32, VQ_BF16 = 0, 1
 MAX_STAGES = 4
 EXPORTS = ("vq_version", "vq_status_string", "vq_validate", "vq_compressed_bytes",
