@@ -192,7 +192,12 @@ int vq_unpack_dequant(const vq_weight *w, uint16_t *idx_out, uint16_t *w_out, vo
  * One token, or fp32 tokens: exact fp16 codebook products accumulated in fp32
  * (bf16 x is held in fp16 after a power-of-two rescale per 32 columns, exact
  * for every value within 2^28 of the largest |x| of its 32), so every output
- * satisfies |y - y_exact| <= 2e-3 * sum_k |w x| + 1e-6.
+ * satisfies |y - y_exact| <= 2e-3 * sum_k |w x| + 1e-6.  One exception: on
+ * a single 16-bit stage with one scale per row and n_out * k_in >= 2^25
+ * (the codebook-sliced kernel), fp32 x is held in fp16 after a power-of-two
+ * rescale per 16 U columns, i.e. rounded to 11 significant bits, so the
+ * bound there is (2^-11 + k_in 2^-24) sum_k |w x| + 1e-6 (inside 2e-3 for
+ * k_in <= 16384); bf16 x stays exact on that kernel.
  * 2..4 bf16 tokens whose rows are short enough (k_in <= 6144, and the
  * codebooks plus every token's x fit on chip) use the same exact fp16
  * products, one launch for all tokens.  Other 2..16 bf16 tokens run on bf16
