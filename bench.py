@@ -337,7 +337,7 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(rows=2048, reps=3):
+def cpu_baseline(rows=8192, reps=3):
     """The float64 oracle as it stands on a bounded sample of the headline
     workload: `rows` rows of each 70B-MLP linear (every column), with the
     input transform of a fresh x.  Unpack, dequant, transform and matmul are
