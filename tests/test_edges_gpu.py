@@ -252,6 +252,25 @@ def test_gemm_wide_row_tiles(vq, m, n, k, st, bits, bs):
     assert_bf16_path(y.cpu().numpy()[:, rows], y_ref, bound, k, f"gemm {m}x{n}x{k} bs {bs}")
 
 
+@pytest.mark.parametrize("m,n,k,st,bits,bs", [(2048, 8212, 256, 3, 8, 128), (1950, 8192, 512, 4, 8, 256)])
+def test_gemm_wide_bf16_every_output(vq, m, n, k, st, bits, bs):
+    """The bf16 256 x 256 wide kernel (three and four 8-bit stages, which have
+    no fp16 variant) on every output: every one of a wave's 64 accumulator
+    blocks in full tiles, a ragged last row tile and (second case) a ragged
+    token panel, so a missing wait after the asm MFMAs shows up in any
+    block."""
+    import torch
+    print(f"wide bf16 {m}x{n}x{k} stages {st}", flush=True)
+    sw = vqsynth.random_weight(n, k, st, bits, bs, seed=m + n + st)
+    xs, x64 = _x(m, k, "bf16", m * 7 + n)
+    w = device_weight(sw)
+    assert vq.vq_gemm_workspace_size(w, m) == 0, "three or more stages: the bf16 path"
+    y = vq.vq_gemm(w, x_to_device(xs, "bf16"))
+    torch.cuda.synchronize()
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
+    assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"wide bf16 {m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("m,n,k,st,bits,bs", [(17, 4096, 512, 2, 12, 128), (40, 8200, 1024, 1, 8, 1024),
                                              (64, 4100, 256, 2, 12, 256), (33, 2500, 768, 2, 12, 384),
                                              (16, 4096, 512, 1, 12, 128), (2, 2049, 512, 2, 12, 512)])
