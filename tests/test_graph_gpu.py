@@ -5,7 +5,9 @@ work (another call, torch ops, a synchronisation) runs between replays.  The
 shapes route to the main kernels: the LDS and L2 decode GEMVs (the latter
 also with the input transform inside), the fused and
 the multi-token sparse correction, the few-token, wide and tile GEMMs, the RHT
-and the LDS dequant."""
+and the LDS dequant, the codebook-sliced 16-bit GEMV (with and without the
+transform inside), the shard-batched transform in both directions, the
+no-allocation GEMM and the low-rank correction."""
 import numpy as np
 import pytest
 
@@ -115,3 +117,45 @@ def test_graph_replay_dequant(vq):
         assert st == 0
 
     replay_matches(call, wt, lambda: torch.zeros(10, device="cuda").add_(1))
+
+
+def test_graph_replay_gemv_cbs(vq):
+    """The codebook-sliced 16-bit kernel (one stage, one scale per row), plain
+    and with the input transform inside."""
+    import torch
+    sw = vqsynth.random_weight(8192, 4096, 1, 16, 4096, seed=12)
+    w = device_weight(sw)
+    x = _x(1, 4096, "bf16", 13)
+    x2 = _x(1, 4096, "bf16", 14)
+    signs = torch.from_numpy(vqsynth.make_signs(4096, np.random.SeedSequence(15))).cuda()
+    y = torch.empty((1, 8192), dtype=torch.float32, device="cuda")
+    y2 = torch.empty_like(y)
+    replay_matches(lambda: vq.vq_gemv(w, x, y=y), y, lambda: vq.vq_gemv(w, x2, y=y2))
+    replay_matches(lambda: vq.vq_gemv_rht(w, x, signs, 4096, y=y), y, lambda: vq.vq_gemv(w, x2, y=y2))
+
+
+def test_graph_replay_rht_shards(vq):
+    import torch
+    n = 8192 + 2048 + 576
+    x = _x(3, n, "f32", 16)
+    signs = torch.from_numpy(vqsynth.make_signs(n, np.random.SeedSequence(17))).cuda()
+    out = torch.empty((3, n), dtype=torch.float32, device="cuda")
+    for inverse in (False, True):
+        replay_matches(lambda: vq.rht_apply_shards(x, signs, 4096, [8192, 2048, 576], inverse=inverse, out=out), out,
+                       lambda: torch.ones(10, device="cuda").cumsum(0))
+
+
+def test_graph_replay_noalloc_and_lowrank(vq):
+    """vq_gemm_noalloc (static scratch) and a weight with a low-rank
+    correction through vq_gemv (one launch more) and vq_gemm (t in the
+    workspace)."""
+    import torch
+    sw = vqsynth.random_weight(4096, 1024, 2, [12, 12], 128, seed=18, lowrank_rank=16)
+    w = device_weight(sw)
+    for m, f in ((300, lambda x, y: vq.vq_gemm_noalloc(w, x, y)), (300, lambda x, y: vq.vq_gemm(w, x, y=y)),
+                 (1, lambda x, y: vq.vq_gemv(w, x, y=y)), (16, lambda x, y: vq.vq_gemv(w, x, y=y))):
+        x = _x(m, 1024, "bf16", 19 + m)
+        x2 = _x(m, 1024, "bf16", 20 + m)
+        y = torch.empty((m, 4096), dtype=torch.float32, device="cuda")
+        y2 = torch.empty_like(y)
+        replay_matches(lambda: f(x, y), y, lambda: f(x2, y2))
