@@ -66,8 +66,8 @@ SOURCES = {
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="headline and rooflines only (no other legs, no cpu)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu baseline")
     ap.add_argument("--only", default="", help="comma list of detail legs to run")
