@@ -216,7 +216,7 @@ int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, f
  * tensor-core path for batched inputs).  Decoded weight tiles are rounded on
  * chip to a 16-bit type and multiplied on matrix cores with fp32
  * accumulation.  Two paths:
- *  - fp16 (more than 64 tokens, k_in % 256 == 0, block_size % 32 == 0, one
+ *  - fp16 (more than 64 tokens, k_in % 256 == 0, scale_block % 32 == 0, one
  *    stage of 8 or 12 bits or two stages 12+12, 12+4, 8+8, 8+4): x is first
  *    converted into the workspace to fp16 after a power-of-two rescale per
  *    token (exact for every value within 2^28 of the token's largest |x|,
@@ -226,18 +226,23 @@ int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, f
  *    2e-3 * sum_k |w x| + 1e-6 for any x when k_in <= 16384;
  *  - bf16 (every other call, including all calls with 64 tokens or fewer):
  *    see the bound below.
- *   x         : bf16 bits [m][k_in];  m >= 1
+ *   x         : bf16 bits [m][k_in];  m >= 1, m * k_in and m * n_out below
+ *               2^31 (VQ_ERR_SHAPE otherwise); with a low-rank correction
+ *               at most 65535 * 64 tokens (VQ_ERR_UNSUPPORTED otherwise)
  *   y         : float [m][n_out]
  *   workspace : device scratch of ws_bytes bytes owned by the caller, 16-byte
  *               aligned, or NULL when ws_bytes == 0.  It must hold at least
  *               vq_gemm_workspace_size(w, m) bytes (VQ_ERR_WORKSPACE
  *               otherwise, before any HIP call); its contents on entry are
  *               ignored and on return unspecified.  Kernels of the same call
- *               use it in stream order (the GLQ page, "Inference kernels",
- *               keeps split-K partials in such a scratch buffer so that the
- *               reduction order stays fixed); two calls in flight at the same
- *               time need two workspaces.
- * On the bf16 path x is used as given and the workspace is not touched.
+ *               use it in stream order; two calls in flight at the same time
+ *               need two workspaces.  (The GLQ page, "Inference kernels",
+ *               keeps split-K partials in such a scratch buffer for a fixed
+ *               reduction order; here split-K sums meet in LDS in a fixed
+ *               order, and the workspace holds the fp16 x and a low-rank
+ *               correction's t.)
+ * On the bf16 path x is used as given and the workspace holds only a
+ * low-rank correction's t.
  * bf16 keeps 8 significant bits, so each weight carries a relative error of
  * up to 2^-8: the guaranteed bound is |y - y_exact| <= (2^-8 + 2^-23 +
  * k_in 2^-24) sum_k |w x| + 1e-6.  For dense activations the rounding errors
