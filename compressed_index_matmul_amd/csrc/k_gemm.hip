@@ -186,9 +186,12 @@ bool tile_f16_format(const WView &w) {
 }  // namespace
 
 // The fp16 tile path: more tokens than the few-token kernel takes, a shape
-// the tile kernels take, a format with an fp16 variant.
+// the tile kernels take, a format with an fp16 variant, and a padded x whose
+// bytes (2 m_pad k) a 32-bit buffer range and offset still cover.
 bool gemm_f16_takes(const WView &w, int m) {
-  return m > 64 && w.k % 256 == 0 && w.bs % 32 == 0 && w.k < (1 << 20) && tile_f16_format(w);
+  const int64_t m_pad = ((int64_t)m + 15) & ~(int64_t)15;
+  return m > 64 && w.k % 256 == 0 && w.bs % 32 == 0 && w.k < (1 << 20) && m_pad * w.k < ((int64_t)1 << 31) &&
+         tile_f16_format(w);
 }
 
 size_t gemm_workspace_bytes(const WView &w, int m) {

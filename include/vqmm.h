@@ -216,8 +216,9 @@ int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, f
  * tensor-core path for batched inputs).  Decoded weight tiles are rounded on
  * chip to a 16-bit type and multiplied on matrix cores with fp32
  * accumulation.  Two paths:
- *  - fp16 (more than 64 tokens, k_in % 256 == 0, scale_block % 32 == 0, one
- *    stage of 8 or 12 bits or two stages 12+12, 12+4, 8+8, 8+4): x is first
+ *  - fp16 (more than 64 tokens, k_in % 256 == 0, scale_block % 32 == 0,
+ *    m rounded up to 16 times k_in below 2^31, one stage of 8 or 12 bits
+ *    or two stages 12+12, 12+4, 8+8, 8+4): x is first
  *    converted into the workspace to fp16 after a power-of-two rescale per
  *    token (exact for every value within 2^28 of the token's largest |x|,
  *    smaller ones off by at most 2^-39 of it), each weight is rounded to
