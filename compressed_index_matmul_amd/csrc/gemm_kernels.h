@@ -59,13 +59,12 @@ __device__ __forceinline__ int scale_blk(const GemmArgs &a, int g) {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Decode group g of W row `row` to 8 bf16 (packed in a uint4).  Stage sum and
-// scale in fp32 (summation starts from stage 0).  BITS = 0: per-stage widths
-// (a.sb), each entry times its stage scale.
+// Decode group g of W row `row` to 8 fp32 weights: stage sum and scale in
+// fp32 (summation starts from stage 0).  BITS = 0: per-stage widths (a.sb),
+// each entry times its stage scale.
 template <int S, int BITS, bool CB_LDS>
-__device__ __forceinline__ uint4 decode_group_bf16(const GemmArgs &a, const uint4 *s_cb, int row, int g) {
+__device__ __forceinline__ void decode_group_f32(const GemmArgs &a, const uint4 *s_cb, int row, int g, float (&w)[8]) {
   const size_t f = (size_t)row * a.G + g;
-  float w[8];
 #pragma unroll
   for (int t = 0; t < S; ++t) {
     const uint32_t idx = load_index(BITS ? BITS : a.sb[t], a.lo[t], a.hi[t], a.i16[t], f);
@@ -84,9 +83,18 @@ __device__ __forceinline__ uint4 decode_group_bf16(const GemmArgs &a, const uint
     }
   }
   const float s = h2f(a.sc[(size_t)row * a.nblk + (8 * g) / a.bs]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) w[e] *= s;
+}
+
+// The same group as 8 bf16 (packed in a uint4).
+template <int S, int BITS, bool CB_LDS>
+__device__ __forceinline__ uint4 decode_group_bf16(const GemmArgs &a, const uint4 *s_cb, int row, int g) {
+  float w[8];
+  decode_group_f32<S, BITS, CB_LDS>(a, s_cb, row, g, w);
   uint32_t o[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = f2bf(s * w[2 * e]) | (f2bf(s * w[2 * e + 1]) << 16);
+  for (int e = 0; e < 4; ++e) o[e] = f2bf(w[2 * e]) | (f2bf(w[2 * e + 1]) << 16);
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
@@ -120,12 +128,27 @@ __device__ __forceinline__ float add_f16(uint32_t a, uint32_t b) {
   return d;
 }
 
-// 8 weights of one group as bf16: sum of the stage vectors (fp32, each
-// partial sum rounded once), times the scale (fp32), rounded to bf16.
+// 8 fp32 weights as two bf16 parts for the few-token products: hi = w
+// rounded to bf16, lo = (w - hi) rounded to bf16.  w - hi is exact in fp32
+// (at most 16 significant bits), so |w - (hi + lo)| <= 2^-18 |w|, where hi
+// alone is off by up to 2^-9 |w|; two bf16 MFMAs (x hi, then x lo) then
+// give every output the accuracy of exact fp16 products.
+__device__ __forceinline__ void split_bf16(const float (&w)[8], uint4 &hi, uint4 &lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = pack_bf16(w[2 * e], w[2 * e + 1]);
+    l[e] = pack_bf16(w[2 * e] - __uint_as_float(h[e] << 16), w[2 * e + 1] - __uint_as_float(h[e] & 0xffff0000u));
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// 8 weights of one group in fp32: sum of the stage vectors (each partial sum
+// rounded once), times the scale.
 template <int S>
-__device__ __forceinline__ uint4 group_to_bf16(const uint4 (&v)[S], float sf) {
+__device__ __forceinline__ void group_to_f32(const uint4 (&v)[S], float sf, float (&w)[8]) {
   const uint32_t h0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
-  float w[8];
   if (S == 1) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -149,19 +172,22 @@ __device__ __forceinline__ uint4 group_to_bf16(const uint4 (&v)[S], float sf) {
       }
     }
   }
-  uint4 pk;
-  pk.x = pack_bf16(sf * w[0], sf * w[1]);
-  pk.y = pack_bf16(sf * w[2], sf * w[3]);
-  pk.z = pack_bf16(sf * w[4], sf * w[5]);
-  pk.w = pack_bf16(sf * w[6], sf * w[7]);
-  return pk;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) w[e] *= sf;
 }
 
-// 8 weights of one group as bf16 with stage scales: sum of each stage vector
-// times its scale (fp32, from stage 0), times the block scale, rounded to bf16.
+// The same rounded to bf16.
 template <int S>
-__device__ __forceinline__ uint4 group_to_bf16_scaled(const uint4 (&v)[S], float sf, const float *rs) {
+__device__ __forceinline__ uint4 group_to_bf16(const uint4 (&v)[S], float sf) {
   float w[8];
+  group_to_f32<S>(v, sf, w);
+  return make_uint4(pack_bf16(w[0], w[1]), pack_bf16(w[2], w[3]), pack_bf16(w[4], w[5]), pack_bf16(w[6], w[7]));
+}
+
+// 8 weights of one group in fp32 with stage scales: sum of each stage vector
+// times its scale (from stage 0), times the block scale.
+template <int S>
+__device__ __forceinline__ void group_to_f32_scaled(const uint4 (&v)[S], float sf, const float *rs, float (&w)[8]) {
 #pragma unroll
   for (int t = 0; t < S; ++t) {
     const uint32_t ht[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
@@ -172,12 +198,16 @@ __device__ __forceinline__ uint4 group_to_bf16_scaled(const uint4 (&v)[S], float
       w[2 * e + 1] = t == 0 ? c1 : w[2 * e + 1] + c1;
     }
   }
-  uint4 pk;
-  pk.x = pack_bf16(sf * w[0], sf * w[1]);
-  pk.y = pack_bf16(sf * w[2], sf * w[3]);
-  pk.z = pack_bf16(sf * w[4], sf * w[5]);
-  pk.w = pack_bf16(sf * w[6], sf * w[7]);
-  return pk;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) w[e] *= sf;
+}
+
+// The same rounded to bf16.
+template <int S>
+__device__ __forceinline__ uint4 group_to_bf16_scaled(const uint4 (&v)[S], float sf, const float *rs) {
+  float w[8];
+  group_to_f32_scaled<S>(v, sf, rs, w);
+  return make_uint4(pack_bf16(w[0], w[1]), pack_bf16(w[2], w[3]), pack_bf16(w[4], w[5]), pack_bf16(w[6], w[7]));
 }
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -1149,7 +1179,8 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_small(GemmArgs a) {
   const int nJ = a.G / 16;
   const int nslabs = (a.n + 15) / 16;
 
-  auto decode = [&](const SmallRegs<S> &R, int r) -> bf16x8_t {
+  // the group's weights as bf16 hi + lo parts (split_bf16)
+  auto decode = [&](const SmallRegs<S> &R, int r, uint4 &hi, uint4 &lo) {
     float w[8];
 #pragma unroll
     for (int t = 0; t < S; ++t) {
@@ -1169,12 +1200,9 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_small(GemmArgs a) {
       }
     }
     const float sf = h2f(R.sc);
-    uint4 pk;
-    pk.x = pack_bf16(sf * w[0], sf * w[1]);
-    pk.y = pack_bf16(sf * w[2], sf * w[3]);
-    pk.z = pack_bf16(sf * w[4], sf * w[5]);
-    pk.w = pack_bf16(sf * w[6], sf * w[7]);
-    return __builtin_bit_cast(bf16x8_t, pk);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] *= sf;
+    split_bf16(w, hi, lo);
   };
 
   for (int slab = blockIdx.x; slab < nslabs; slab += gridDim.x) {
@@ -1195,8 +1223,11 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_small(GemmArgs a) {
     auto run = [&](const SmallRegs<S> &R) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bf16x8_t bfr = decode(R, r);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, R.av[r]), bfr, acc, 0, 0, 0);
+        uint4 hi, lo;
+        decode(R, r, hi, lo);
+        const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, R.av[r]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(bf16x8_t, hi), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(bf16x8_t, lo), acc, 0, 0, 0);
       }
     };
     if (nmine > 0) {  // wave-uniform; every wave still reaches both barriers below
@@ -1398,11 +1429,23 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_few(GemmArgs a, int units
       v[t] = s_cb[LD::off(t) + idx];
     }
     const float sf = h2f(Q.sc);
-    const bf16x8_t bfr =
-        __builtin_bit_cast(bf16x8_t, RS ? group_to_bf16_scaled<S>(v, sf, a.rs) : group_to_bf16<S>(v, sf));
+    if constexpr (TB == 1) {
+      // up to 16 tokens: the weights as bf16 hi + lo, two MFMAs
+      float w[8];
+      if constexpr (RS) group_to_f32_scaled<S>(v, sf, a.rs, w);
+      else group_to_f32<S>(v, sf, w);
+      uint4 hi, lo;
+      split_bf16(w, hi, lo);
+      const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, X.av[0]);
+      acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(bf16x8_t, hi), acc[0], 0, 0, 0);
+      acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(bf16x8_t, lo), acc[0], 0, 0, 0);
+    } else {
+      const bf16x8_t bfr =
+          __builtin_bit_cast(bf16x8_t, RS ? group_to_bf16_scaled<S>(v, sf, a.rs) : group_to_bf16<S>(v, sf));
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-      acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, X.av[tb]), bfr, acc[tb], 0, 0, 0);
+      for (int tb = 0; tb < TB; ++tb)
+        acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, X.av[tb]), bfr, acc[tb], 0, 0, 0);
+    }
   };
 
   FewQuad<S> Q0, Q1;
@@ -1515,13 +1558,18 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_small_gen(GemmArgs a) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int ks = wave; ks < nks; ks += kSWaves) {
       const int g = ks * 4 + q;
-      uint4 av = make_uint4(0, 0, 0, 0), bv = make_uint4(0, 0, 0, 0);
+      uint4 av = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0), lo = make_uint4(0, 0, 0, 0);
       if (g < a.G) {
         if (tok < a.m) av = *reinterpret_cast<const uint4 *>(a.x + (size_t)tok * a.k + 8 * g);
-        if (wrow < a.n) bv = decode_group_bf16<S, BITS, CB_LDS>(a, s_cb, wrow, g);
+        if (wrow < a.n) {
+          float w[8];
+          decode_group_f32<S, BITS, CB_LDS>(a, s_cb, wrow, g, w);
+          split_bf16(w, hi, lo);
+        }
       }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                    __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
+      const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, av);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(bf16x8_t, hi), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(bf16x8_t, lo), acc, 0, 0, 0);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) s_red[wave][4 * (lane >> 4) + r][lane & 15] = acc[r];

@@ -50,9 +50,14 @@ def bf16_worst_case_bound(bound, k):
     return (2.0 ** -8 + 2.0 ** -23 + k * 2.0 ** -24) * bound + 1e-6
 
 
-def assert_bf16_path(y, y_ref, bound, k, what):
+def assert_bf16_path(y, y_ref, bound, k, what, m=None):
     """bf16 paths: the worst-case bound always; the 2e-3 bound once K is
-    large enough for the per-weight rounding errors to average (K >= 256)."""
+    large enough for the per-weight rounding errors to average (K >= 256).
+    With at most 16 tokens (m given) the weights enter as bf16 hi + lo parts
+    and the 2e-3 bound holds for any K."""
+    if m is not None and m <= 16:
+        assert_within(y, y_ref, bound, what)
+        return
     err = np.abs(np.asarray(y, np.float64) - y_ref)
     assert np.all(err <= bf16_worst_case_bound(bound, k)), f"{what}: beyond the bf16 worst-case bound"
     if k >= 256:
@@ -74,7 +79,7 @@ def test_gemv_ragged(vq, shape, dtype, batch):
     got = y.cpu().numpy()
     got = got if rows is None else got[:, rows]
     if batch > 1 and dtype == "bf16":   # 2..16 bf16 tokens run on bf16 matrix cores
-        assert_bf16_path(got, y_ref, bound, k, f"{shape} {dtype} B={batch}")
+        assert_bf16_path(got, y_ref, bound, k, f"{shape} {dtype} B={batch}", m=batch)
     else:                               # fp32 decode: the 2e-3 bound for any input
         assert_within(got, y_ref, bound, f"{shape} {dtype} B={batch}")
 
@@ -93,9 +98,7 @@ def test_gemv_tokens_lds(vq, n, k, st, bits, bs, batch):
     y = vq.vq_gemv(device_weight(sw), x_to_device(xs, "bf16"))
     torch.cuda.synchronize()
     y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
-    assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"{n}x{k} B={batch}")
-    if (k // 32 + 63) // 64 * batch <= 6 and not (st == 2 and bits == 12 and batch == 4 and k > 2048):
-        assert_within(y.cpu().numpy(), y_ref, bound, f"{n}x{k} B={batch} (exact fp16 products)")
+    assert_within(y.cpu().numpy(), y_ref, bound, f"{n}x{k} B={batch}")
 
 
 def test_gemv_tokens_lds_one_hot(vq):
@@ -215,7 +218,7 @@ def test_gemm_ragged(vq, m, n, k, st, bits):
     y = vq.vq_gemm(device_weight(sw), x_to_device(xs, "bf16"))
     torch.cuda.synchronize()
     y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
-    assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"gemm {m}x{n}x{k}")
+    assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"gemm {m}x{n}x{k}", m=m)
 
 
 @pytest.mark.parametrize("m,n,k,st,bits,bs", [(257, 131, 512, 2, 12, 128), (40, 64, 768, 2, 8, 768),
@@ -232,7 +235,7 @@ def test_gemm_tile_ragged(vq, m, n, k, st, bits, bs):
     y = vq.vq_gemm(device_weight(sw), x_to_device(xs, "bf16"))
     torch.cuda.synchronize()
     y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
-    assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"gemm {m}x{n}x{k} bs {bs}")
+    assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"gemm {m}x{n}x{k} bs {bs}", m=m)
 
 
 @pytest.mark.parametrize("m,n,k,st,bits,bs", [(1900, 14300, 512, 2, 12, 128), (2048, 14336, 256, 2, 12, 128),
@@ -285,7 +288,7 @@ def test_gemm_token_blocks(vq, m, n, k, st, bits, bs):
     y = vq.vq_gemm(device_weight(sw), x_to_device(xs, "bf16"))
     torch.cuda.synchronize()
     y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
-    assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"gemm {m}x{n}x{k} bs {bs}")
+    assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"gemm {m}x{n}x{k} bs {bs}", m=m)
 
 
 @pytest.mark.parametrize("m,n,k,st,bits,bs", [(5, 8200, 512, 2, 12, 128), (16, 8192, 1024, 1, 8, 1024),
@@ -300,7 +303,50 @@ def test_gemm_few_tokens_wide(vq, m, n, k, st, bits, bs):
     y = vq.vq_gemm(device_weight(sw), x_to_device(xs, "bf16"))
     torch.cuda.synchronize()
     y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
-    assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"gemm {m}x{n}x{k} bs {bs}")
+    assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"gemm {m}x{n}x{k} bs {bs}", m=m)
+
+
+# (n, k, stages, widths, scale block, stage scales): the unit kernel (12+12,
+# 8-bit), the slab kernel (16-bit), the general slab kernel (K % 128 != 0),
+# a 12+4 ladder with stage scales, three 8-bit stages
+ONE_HOT_SHAPES = [(2048, 1024, 2, 12, 128, None), (2304, 2048, 1, 8, 2048, None), (300, 1024, 1, 16, 1024, None),
+                  (200, 520, 2, 12, 40, None), (1024, 768, 2, [12, 4], 128, (0.5, 1.5)),
+                  (600, 512, 3, 8, 128, None)]
+
+
+@pytest.mark.parametrize("shape", ONE_HOT_SHAPES, ids=lambda s: "x".join(str(v) for v in s[:4]))
+@pytest.mark.parametrize("batch", [5, 8, 16])
+def test_gemv_tokens_any_x(vq, shape, batch):
+    """5-16 bf16 tokens on the matrix-core kernels meet the 2e-3 bound for
+    any x: one-hot tokens, a token with one large and many tiny entries,
+    sparse and dense tokens in one batch, every output against the oracle
+    (bf16 weights alone would miss it on the one-hot tokens)."""
+    import torch
+    n, k, st, bits, bs, ssr = shape
+    sw = vqsynth.random_weight(n, k, st, bits, bs, seed=n + k + batch, stage_scale_range=ssr)
+    rng = np.random.default_rng(batch * 7 + k)
+    x = np.zeros((batch, k), np.float32)
+    for b in range(batch):
+        kind = b % 4
+        if kind == 0:
+            x[b, rng.integers(k)] = 1.0
+        elif kind == 1:
+            x[b, :] = rng.standard_normal(k) * 2.0 ** -20
+            x[b, rng.integers(k)] = 3.0
+        elif kind == 2:
+            cols = rng.choice(k, 5, replace=False)
+            x[b, cols] = rng.standard_normal(5)
+        else:
+            x[b, :] = rng.standard_normal(k)
+    xs = vqsynth.f32_to_bf16_bits(x)
+    x64 = vqsynth.bf16_bits_to_f32(xs).astype(np.float64)
+    w = device_weight(sw)
+    y = vq.vq_gemv(w, x_to_device(xs, "bf16"))
+    y2 = vq.vq_gemm(w, x_to_device(xs, "bf16"))
+    torch.cuda.synchronize()
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
+    assert_within(y.cpu().numpy(), y_ref, bound, f"gemv {n}x{k} B={batch}")
+    assert_within(y2.cpu().numpy(), y_ref, bound, f"gemm {n}x{k} m={batch}")
 
 
 def test_gemv_one_hot_columns(vq):
