@@ -402,3 +402,38 @@ def test_deterministic_and_stream_independent(vq):
         s.synchronize()
         torch.cuda.synchronize()
         assert torch.equal(y1, y2) and torch.equal(y1, y3), op
+
+
+def test_concurrent_streams(vq):
+    """Different products enqueued alternately on two streams with no
+    synchronisation between them (each vq_gemm with its own workspace) give
+    bit for bit the results of the same calls run one after another: the
+    library keeps no state between calls except vq_gemm_noalloc's scratch."""
+    import torch
+    ws = [device_weight(vqsynth.random_weight(4096, 4096, 2, 12, 128, seed=11)),
+          device_weight(vqsynth.random_weight(2048, 8192, 1, 16, 8192, seed=12)),
+          device_weight(vqsynth.random_weight(4096, 1024, 2, [12, 4], 128, seed=13, stage_scale_range=(0.2, 0.4)))]
+    xs = [x_to_device(_x(m, w.k_in, "bf16", 20 + i)[0], "bf16") for i, (w, m) in enumerate(zip(ws, (1, 1, 300)))]
+    signs = torch.from_numpy(vqsynth.make_signs(8192, np.random.SeedSequence(21))).cuda()
+
+    def calls(stream, wsp):
+        return [lambda: vq.vq_gemv(ws[0], xs[0], stream=stream),
+                lambda: vq.vq_gemv(ws[1], vq.rht_apply(xs[1], signs, 2048, stream=stream), stream=stream),
+                lambda: vq.vq_gemm(ws[2], xs[2], workspace=wsp, stream=stream)]
+
+    need = vq.vq_gemm_workspace_size(ws[2], 300)
+    wsp = [torch.empty(need, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    serial = [f() for f in calls(None, wsp[0])]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for rep in range(4):
+        for s, wp in ((s1, wsp[0]), (s2, wsp[1])):
+            with torch.cuda.stream(s):
+                outs.append([f() for f in calls(s, wp)])
+    torch.cuda.synchronize()
+    for got in outs:
+        for a, b in zip(serial, got):
+            assert torch.equal(a, b)
