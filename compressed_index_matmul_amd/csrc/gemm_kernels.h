@@ -130,9 +130,12 @@ __device__ __forceinline__ float add_f16(uint32_t a, uint32_t b) {
 
 // 8 fp32 weights as two bf16 parts for the few-token products: hi = w
 // rounded to bf16, lo = (w - hi) rounded to bf16.  w - hi is exact in fp32
-// (at most 16 significant bits), so |w - (hi + lo)| <= 2^-18 |w|, where hi
-// alone is off by up to 2^-9 |w|; two bf16 MFMAs (x hi, then x lo) then
-// give every output the accuracy of exact fp16 products.
+// (at most 16 significant bits).  For w in [2^e, 2^(e+1)), |w - hi| <=
+// 2^(e-8), and below that bound its bf16 rounding is off by at most
+// 2^(e-17) (at the bound it is a power of two, exact), so |w - (hi + lo)| <=
+// 2^-17 |w|, where hi alone is off by up to 2^-8 |w|; two bf16 MFMAs (x hi,
+// then x lo) then give every output about the accuracy of exact fp16
+// products.
 __device__ __forceinline__ void split_bf16(const float (&w)[8], uint4 &hi, uint4 &lo) {
   uint32_t h[4], l[4];
 #pragma unroll
@@ -1429,22 +1432,17 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_few(GemmArgs a, int units
       v[t] = s_cb[LD::off(t) + idx];
     }
     const float sf = h2f(Q.sc);
-    if constexpr (TB == 1) {
-      // up to 16 tokens: the weights as bf16 hi + lo, two MFMAs
-      float w[8];
-      if constexpr (RS) group_to_f32_scaled<S>(v, sf, a.rs, w);
-      else group_to_f32<S>(v, sf, w);
-      uint4 hi, lo;
-      split_bf16(w, hi, lo);
-      const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, X.av[0]);
-      acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(bf16x8_t, hi), acc[0], 0, 0, 0);
-      acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(bf16x8_t, lo), acc[0], 0, 0, 0);
-    } else {
-      const bf16x8_t bfr =
-          __builtin_bit_cast(bf16x8_t, RS ? group_to_bf16_scaled<S>(v, sf, a.rs) : group_to_bf16<S>(v, sf));
+    // the weights as bf16 hi + lo, two MFMAs per token block
+    float w[8];
+    if constexpr (RS) group_to_f32_scaled<S>(v, sf, a.rs, w);
+    else group_to_f32<S>(v, sf, w);
+    uint4 hi, lo;
+    split_bf16(w, hi, lo);
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
-        acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, X.av[tb]), bfr, acc[tb], 0, 0, 0);
+    for (int tb = 0; tb < TB; ++tb) {
+      const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, X.av[tb]);
+      acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(bf16x8_t, hi), acc[tb], 0, 0, 0);
+      acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(bf16x8_t, lo), acc[tb], 0, 0, 0);
     }
   };
 

@@ -203,10 +203,10 @@ int vq_unpack_dequant(const vq_weight *w, uint16_t *idx_out, uint16_t *w_out, vo
  * products, one launch for all tokens.  Other 2..16 bf16 tokens run on bf16
  * matrix cores as vq_gemm does with 16 tokens or fewer: each decoded weight
  * w enters as two bf16 parts, hi = bf16(w) and lo = bf16(w - hi) (|w - hi -
- * lo| <= 2^-18 |w|), multiplied in two MFMAs with exact products and fp32
- * sums, so every output satisfies |y - y_exact| <= (2^-18 + 2^-22 + k_in
- * 2^-24) sum_k |w x| + 1e-6, inside 2e-3 * sum_k |w x| + 1e-6 for any x
- * when k_in <= 16384.  A sparse
+ * lo| <= 2^-17 |w|), multiplied in two MFMAs with exact products and fp32
+ * sums of 2 k_in terms, so every output satisfies |y - y_exact| <= (2^-17 +
+ * 2^-20 + 2 k_in 2^-24) sum_k |w x| + 1e-6, inside 2e-3 * sum_k |w x| + 1e-6
+ * for any x when k_in <= 16384.  A sparse
  * correction adds x S^T (fp16 values times x, fp32 sums) in a second launch
  * on the same stream.  A low-rank correction adds (x V^T) U^T in one more
  * launch with no scratch: every workgroup forms t = x V^T for all tokens
@@ -231,9 +231,13 @@ int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, f
  *    <= (2^-10 + 2^-22 + k_in 2^-24) sum_k |w x| + 1e-6, inside
  *    2e-3 * sum_k |w x| + 1e-6 for any x when k_in <= 16384;
  *  - bf16 (every other call, including all calls with 64 tokens or fewer):
- *    see the bound below; with 16 tokens or fewer the weights enter as bf16
- *    hi + lo parts and the bound is vq_gemv's (inside 2e-3 * sum_k |w x| +
- *    1e-6 for any x when k_in <= 16384).
+ *    see the bound below.  With 16 tokens or fewer, and with 17..64 tokens
+ *    on the few-token unit kernel (stages of 8 bits, up to four, or of 12
+ *    bits, up to two, or the ladders 12+4 and 8+4; k_in % 256 == 0,
+ *    scale_block % 128 == 0, n_out from 8 to 128 times the CU count, i.e.
+ *    2048 to 32768 rows on 256 CUs), the weights enter as bf16 hi + lo parts
+ *    and the bound is vq_gemv's (inside 2e-3 * sum_k |w x| + 1e-6 for any x
+ *    when k_in <= 16384).
  *   x         : bf16 bits [m][k_in];  m >= 1, m * k_in and m * n_out below
  *               2^31 (VQ_ERR_SHAPE otherwise); with a low-rank correction
  *               at most 65535 * 64 tokens (VQ_ERR_UNSUPPORTED otherwise)
@@ -250,13 +254,14 @@ int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, f
  *               order, and the workspace holds the fp16 x and a low-rank
  *               correction's t.)
  * On the bf16 path x is used as given and the workspace holds only a
- * low-rank correction's t.
- * With more than 16 tokens on this path bf16 keeps 8 significant bits, so
- * each weight carries a relative error of up to 2^-8: the guaranteed bound
- * is |y - y_exact| <= (2^-8 + 2^-23 + k_in 2^-24) sum_k |w x| + 1e-6.  For
- * dense activations the rounding errors average out and outputs stay well
- * inside 2e-3 * sum_k |w x| + 1e-6 (about 0.07 of it at k_in = 4096 for
- * N(0,1) inputs); a one-hot or very short x can exceed that tighter bound.  A sparse correction adds x S^T exactly as
+ * low-rank correction's t.  Where the weights do not enter as hi + lo
+ * parts (more than 16 tokens off the few-token unit kernel), bf16 keeps 8
+ * significant bits, so each weight carries a relative error of up to 2^-8:
+ * the guaranteed bound is |y - y_exact| <= (2^-8 + 2^-23 + k_in 2^-24)
+ * sum_k |w x| + 1e-6.  For dense activations the rounding errors average
+ * out and outputs stay well inside 2e-3 * sum_k |w x| + 1e-6 (about 0.07
+ * of it at k_in = 4096 for N(0,1) inputs); a one-hot or very short x can
+ * exceed that tighter bound.  A sparse correction adds x S^T exactly as
  * vq_gemv does (fp32, not rounded to bf16).  A low-rank correction takes
  * two more launches: t = x V^T into the workspace (m * lr_rank floats after
  * the fp16 path's part, 256-byte aligned), then y += t U^T, both fp32 with

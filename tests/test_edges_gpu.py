@@ -50,12 +50,13 @@ def bf16_worst_case_bound(bound, k):
     return (2.0 ** -8 + 2.0 ** -23 + k * 2.0 ** -24) * bound + 1e-6
 
 
-def assert_bf16_path(y, y_ref, bound, k, what, m=None):
+def assert_bf16_path(y, y_ref, bound, k, what, m=None, few=False):
     """bf16 paths: the worst-case bound always; the 2e-3 bound once K is
     large enough for the per-weight rounding errors to average (K >= 256).
-    With at most 16 tokens (m given) the weights enter as bf16 hi + lo parts
-    and the 2e-3 bound holds for any K."""
-    if m is not None and m <= 16:
+    With at most 16 tokens (m given), or up to 64 on the few-token unit
+    kernel (few), the weights enter as bf16 hi + lo parts and the 2e-3 bound
+    holds for any K."""
+    if m is not None and (m <= 16 or (few and m <= 64)):
         assert_within(y, y_ref, bound, what)
         return
     err = np.abs(np.asarray(y, np.float64) - y_ref)
@@ -288,7 +289,7 @@ def test_gemm_token_blocks(vq, m, n, k, st, bits, bs):
     y = vq.vq_gemm(device_weight(sw), x_to_device(xs, "bf16"))
     torch.cuda.synchronize()
     y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
-    assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"gemm {m}x{n}x{k} bs {bs}", m=m)
+    assert_bf16_path(y.cpu().numpy(), y_ref, bound, k, f"gemm {m}x{n}x{k} bs {bs}", m=m, few=True)
 
 
 @pytest.mark.parametrize("m,n,k,st,bits,bs", [(5, 8200, 512, 2, 12, 128), (16, 8192, 1024, 1, 8, 1024),
@@ -324,9 +325,22 @@ def test_gemv_tokens_any_x(vq, shape, batch):
     import torch
     n, k, st, bits, bs, ssr = shape
     sw = vqsynth.random_weight(n, k, st, bits, bs, seed=n + k + batch, stage_scale_range=ssr)
-    rng = np.random.default_rng(batch * 7 + k)
-    x = np.zeros((batch, k), np.float32)
-    for b in range(batch):
+    xs, x64 = _mixed_tokens(batch, k, batch * 7 + k)
+    w = device_weight(sw)
+    y = vq.vq_gemv(w, x_to_device(xs, "bf16"))
+    y2 = vq.vq_gemm(w, x_to_device(xs, "bf16"))
+    torch.cuda.synchronize()
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
+    assert_within(y.cpu().numpy(), y_ref, bound, f"gemv {n}x{k} B={batch}")
+    assert_within(y2.cpu().numpy(), y_ref, bound, f"gemm {n}x{k} m={batch}")
+
+
+def _mixed_tokens(m, k, seed):
+    """bf16 tokens of four kinds in turn: one-hot, one large entry over tiny
+    ones, five nonzero columns, dense N(0,1)."""
+    rng = np.random.default_rng(seed)
+    x = np.zeros((m, k), np.float32)
+    for b in range(m):
         kind = b % 4
         if kind == 0:
             x[b, rng.integers(k)] = 1.0
@@ -339,14 +353,31 @@ def test_gemv_tokens_any_x(vq, shape, batch):
         else:
             x[b, :] = rng.standard_normal(k)
     xs = vqsynth.f32_to_bf16_bits(x)
-    x64 = vqsynth.bf16_bits_to_f32(xs).astype(np.float64)
-    w = device_weight(sw)
-    y = vq.vq_gemv(w, x_to_device(xs, "bf16"))
-    y2 = vq.vq_gemm(w, x_to_device(xs, "bf16"))
+    return xs, vqsynth.bf16_bits_to_f32(xs).astype(np.float64)
+
+
+# (n, k, stages, widths, scale block, stage scales) on the few-token unit
+# kernel (at least 128 units of 16 rows, K % 256 == 0, scale blocks of 128
+# columns or more): 12+12, one 8-bit stage, a 12+4 ladder with stage scales,
+# three 8-bit stages
+FEW_SHAPES = [(2048, 1024, 2, 12, 128, None), (2304, 2048, 1, 8, 2048, None), (2064, 768, 2, [12, 4], 128, (0.5, 1.5)),
+              (2176, 512, 3, 8, 128, None)]
+
+
+@pytest.mark.parametrize("shape", FEW_SHAPES, ids=lambda s: "x".join(str(v) for v in s[:4]))
+@pytest.mark.parametrize("m", [17, 40, 64])
+def test_gemm_tokens_any_x(vq, shape, m):
+    """17-64 bf16 tokens on the few-token unit kernel (two to four token
+    blocks) meet the 2e-3 bound for any x: one-hot, wide-range, sparse and
+    dense tokens, every output against the oracle."""
+    import torch
+    n, k, st, bits, bs, ssr = shape
+    sw = vqsynth.random_weight(n, k, st, bits, bs, seed=n + k + m, stage_scale_range=ssr)
+    xs, x64 = _mixed_tokens(m, k, m * 11 + k)
+    y = vq.vq_gemm(device_weight(sw), x_to_device(xs, "bf16"))
     torch.cuda.synchronize()
     y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
-    assert_within(y.cpu().numpy(), y_ref, bound, f"gemv {n}x{k} B={batch}")
-    assert_within(y2.cpu().numpy(), y_ref, bound, f"gemm {n}x{k} m={batch}")
+    assert_within(y.cpu().numpy(), y_ref, bound, f"gemm {n}x{k} m={m}")
 
 
 def test_gemv_one_hot_columns(vq):
