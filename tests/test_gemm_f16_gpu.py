@@ -113,3 +113,23 @@ def test_gemm_workspace_required(vq):
     with pytest.raises(vq.VQError) as e:
         vq.vq_gemm(w, x, workspace=torch.empty(need - 256, dtype=torch.uint8, device="cuda"))
     assert e.value.status == -8
+
+
+@pytest.mark.parametrize("m", [63, 64, 65, 80])
+def test_gemm_token_count_boundary(vq, m):
+    """Either side of the switch from the few-token unit kernel (bf16 hi + lo
+    weights, no workspace) to the fp16 tile path (more than 64 tokens, a
+    workspace): the same 12+12 weight and one-hot, wide-range, sparse and
+    dense tokens meet the 2e-3 bound on every output on both sides."""
+    import torch
+    from test_edges_gpu import _mixed_tokens
+    sw = vqsynth.random_weight(2048, 1024, 2, 12, 128, seed=64)
+    w = device_weight(sw)
+    need = vq.vq_gemm_workspace_size(w, m)
+    assert (need > 0) == (m > 64), need
+    xs, x64 = _mixed_tokens(m, sw.k_in, m)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    y = vq.vq_gemm(w, x_to_device(xs, "bf16"), workspace=ws if need else None)
+    torch.cuda.synchronize()
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw), x64)
+    assert_within(y.cpu().numpy(), y_ref, bound, f"2048x1024 m={m}")
