@@ -1618,14 +1618,17 @@ static GemmArgs make_gemm_args(const WView &w, const uint16_t *x, int m, float *
   return a;
 }
 
-// The few-token unit kernel with TB token blocks; false when the shape
-// leaves it fewer units than half the CUs (the slab and tile kernels spread
-// such shapes better).
+// The few-token unit kernel with TB token blocks; false with 16 tokens or
+// fewer when the shape leaves it fewer units than half the CUs (the slab
+// kernels, whose weights also enter as bf16 hi + lo parts, spread such
+// shapes better).  With 17..64 tokens it takes every row count up to eight
+// units per CU: the tile kernels it would leave them to round the weights
+// to bf16 alone.
 template <class LD, bool RS>
 static bool launch_few(const GemmArgs &a, hipStream_t s) {
   const int cus = device_cu_count();
   const int units = (a.n + 15) / 16;
-  if (2 * units < cus) return false;
+  if (a.m <= 16 && 2 * units < cus) return false;
   const int grid = units < cus ? units : cus;
   const int upw = (units + grid - 1) / grid;
   const int nks = a.k / 32;

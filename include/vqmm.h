@@ -234,8 +234,8 @@ int vq_gemv(const vq_weight *w, const void *x, int32_t x_dtype, int32_t batch, f
  *    see the bound below.  With 16 tokens or fewer, and with 17..64 tokens
  *    on the few-token unit kernel (stages of 8 bits, up to four, or of 12
  *    bits, up to two, or the ladders 12+4 and 8+4; k_in % 256 == 0,
- *    scale_block % 128 == 0, n_out from 8 to 128 times the CU count, i.e.
- *    2048 to 32768 rows on 256 CUs), the weights enter as bf16 hi + lo parts
+ *    scale_block % 128 == 0, n_out up to 128 times the CU count, i.e.
+ *    32768 rows on 256 CUs), the weights enter as bf16 hi + lo parts
  *    and the bound is vq_gemv's (inside 2e-3 * sum_k |w x| + 1e-6 for any x
  *    when k_in <= 16384).
  *   x         : bf16 bits [m][k_in];  m >= 1, m * k_in and m * n_out below

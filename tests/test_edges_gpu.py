@@ -357,11 +357,13 @@ def _mixed_tokens(m, k, seed):
 
 
 # (n, k, stages, widths, scale block, stage scales) on the few-token unit
-# kernel (at least 128 units of 16 rows, K % 256 == 0, scale blocks of 128
-# columns or more): 12+12, one 8-bit stage, a 12+4 ladder with stage scales,
-# three 8-bit stages
+# kernel (K % 256 == 0, scale blocks of 128 columns or more; with more than
+# 16 tokens any row count up to eight 16-row units per CU): 12+12, one 8-bit
+# stage, a 12+4 ladder with stage scales, three 8-bit stages, and row counts
+# that leave most CUs idle (64, 13 and one unit, ragged)
 FEW_SHAPES = [(2048, 1024, 2, 12, 128, None), (2304, 2048, 1, 8, 2048, None), (2064, 768, 2, [12, 4], 128, (0.5, 1.5)),
-              (2176, 512, 3, 8, 128, None)]
+              (2176, 512, 3, 8, 128, None), (1024, 4096, 2, 12, 128, None), (200, 512, 1, 8, 128, None),
+              (9, 256, 2, 12, 256, None)]
 
 
 @pytest.mark.parametrize("shape", FEW_SHAPES, ids=lambda s: "x".join(str(v) for v in s[:4]))
@@ -369,7 +371,8 @@ FEW_SHAPES = [(2048, 1024, 2, 12, 128, None), (2304, 2048, 1, 8, 2048, None), (2
 def test_gemm_tokens_any_x(vq, shape, m):
     """17-64 bf16 tokens on the few-token unit kernel (two to four token
     blocks) meet the 2e-3 bound for any x: one-hot, wide-range, sparse and
-    dense tokens, every output against the oracle."""
+    dense tokens, every output against the oracle (bf16 weights alone miss
+    it on the one-hot tokens)."""
     import torch
     n, k, st, bits, bs, ssr = shape
     sw = vqsynth.random_weight(n, k, st, bits, bs, seed=n + k + m, stage_scale_range=ssr)
