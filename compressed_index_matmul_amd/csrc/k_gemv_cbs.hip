@@ -302,13 +302,18 @@ __global__ __launch_bounds__(kCbsWaves * 64) void k_gemv_cbs(CbsArgs a) {
     // last are duplicates whose sums are dropped): guarded rows let the
     // compiler defer every row's dot products to a join block and keep all
     // the gathered vectors live.
-    pass(0u, std::true_type{});
-    for (int p = 1; p < a.passes; ++p) {
-      __syncthreads();  // every wave is done with slice p - 1
-      stage(p);
-      wait_vmem<0>();
-      __syncthreads();
-      pass(0u - 16u * (uint32_t)(p * a.slice), std::false_type{});
+    // One copy of the pass code serves every pass: its waits for the index
+    // loads are no-ops once the loads have landed, and a single copy keeps
+    // the kernel small enough that the instruction cache holds it beside
+    // the other kernels of a decode step.
+    for (int p = 0; p < a.passes; ++p) {
+      if (p > 0) {
+        __syncthreads();  // every wave is done with slice p - 1
+        stage(p);
+        wait_vmem<0>();
+        __syncthreads();
+      }
+      pass(0u - 16u * (uint32_t)(p * a.slice), std::true_type{});
     }
     // Per row: the lane's sum times its rescale factor, reduced across the
     // wave in a fixed order; the K parts of a row are then added in order
