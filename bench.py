@@ -51,6 +51,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, published
 CUS, BF16_FLOP_PER_CLK_CU = 256, 4096  # the published peak is CUs x flop/clk x engine clock
 MALL_DEFEAT_BYTES = 512 << 20  # rotate through at least this many weight bytes
+MAX_COPIES = 128  # at most this many copies (the tiny and SmolLM weights stay warm in the 256 MB Infinity Cache)
 REPLAYS = 5                    # timed graph replays; the median is reported
 COPY_BYTES = 1 << 30           # the plain copy used for HBM calibration (4x the Infinity Cache)
 
@@ -157,8 +158,9 @@ def run_decode_leg(vq, workload, steps, warmup, batch=1, rht=False, fused=False)
         xs.append(x_device(st, cfg["x_dtype"]))
         if rht:
             signs.append(torch.from_numpy(vqsynth.make_signs(sw.k_in, kids[len(ws) + i])).cuda())
-    set_bytes = sum(compressed_bytes(sw) for sw in ws)
-    ncopies = copies_for(set_bytes)
+    # enough copies that each linear timed alone also rotates through
+    # MALL_DEFEAT_BYTES of its own weights (capped for the tiny ones)
+    ncopies = min(MAX_COPIES, max(copies_for(compressed_bytes(sw)) for sw in ws))
     sets = upload_set(ws, ncopies)
     ys = [torch.empty((batch, sw.n_out), dtype=torch.float32, device="cuda") for sw in ws]
     xr = [torch.empty((batch, sw.k_in), dtype=torch.float32, device="cuda") for sw in ws] if rht else None
