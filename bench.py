@@ -123,6 +123,13 @@ def copies_for(bytes_per_set):
     return max(2, -(-MALL_DEFEAT_BYTES // max(1, bytes_per_set)))
 
 
+def weight_copies(sws):
+    """Copies of a set of linears such that each linear timed alone also
+    rotates through MALL_DEFEAT_BYTES of its own weights (at most
+    MAX_COPIES: the tiny and SmolLM weights stay in the cache)."""
+    return min(MAX_COPIES, max(copies_for(compressed_bytes(sw)) for sw in sws))
+
+
 def upload_set(sws, ncopies):
     """ncopies identical copies of the weights at distinct device addresses."""
     base = [device_weight_(sw) for sw in sws]
@@ -158,9 +165,7 @@ def run_decode_leg(vq, workload, steps, warmup, batch=1, rht=False, fused=False)
         xs.append(x_device(st, cfg["x_dtype"]))
         if rht:
             signs.append(torch.from_numpy(vqsynth.make_signs(sw.k_in, kids[len(ws) + i])).cuda())
-    # enough copies that each linear timed alone also rotates through
-    # MALL_DEFEAT_BYTES of its own weights (capped for the tiny ones)
-    ncopies = min(MAX_COPIES, max(copies_for(compressed_bytes(sw)) for sw in ws))
+    ncopies = weight_copies(ws)
     sets = upload_set(ws, ncopies)
     ys = [torch.empty((batch, sw.n_out), dtype=torch.float32, device="cuda") for sw in ws]
     xr = [torch.empty((batch, sw.k_in), dtype=torch.float32, device="cuda") for sw in ws] if rht else None
