@@ -5,7 +5,7 @@ power-of-two rescale per token (exact), each weight is decoded to fp16 with
 relative error at most 2^-10 + 2^-22 (two stages: sum, then scale, each
 rounded once), and fp16 x fp16 products accumulate in fp32, so every output
 meets |y - y_ref| <= 2e-3 sum|w x| + 1e-6 for any x with K <= 16384 (the
-spec bound), one-hot tokens included.  Every output is compared,
+matmul acceptance bound), one-hot tokens included.  Every output is compared,
 which covers every accumulator block of every tile, ragged ones included."""
 import numpy as np
 import pytest
