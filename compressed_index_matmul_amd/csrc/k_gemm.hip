@@ -169,9 +169,63 @@ __global__ __launch_bounds__(256) void k_x_f16(const uint16_t *x, int m, int m_p
   }
 }
 
+// The same conversion with the row held in registers (CPL 16-byte chunks per
+// lane, k <= 512 CPL): the row is read once, every load issued before the
+// maximum is taken.  Output bit-identical to k_x_f16.
+template <int CPL>
+__global__ __launch_bounds__(256) void k_x_f16_reg(const uint16_t *x, int m, int m_pad, int k, uint16_t *xh,
+                                                   float *xf) {
+  const int lane = threadIdx.x & 63;
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);  // wave-uniform
+  if (tok >= m_pad) return;
+  const int chunks = k / 8;
+  const uint4 *row = reinterpret_cast<const uint4 *>(x + (size_t)min(tok, m - 1) * k);
+  uint4 v[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = lane + 64 * j;
+    v[j] = (tok < m && c < chunks) ? row[c] : make_uint4(0u, 0u, 0u, 0u);  // padding tokens: zeros
+  }
+  float mx = 0.f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(fabsf(bf2f(w4[e] & 0xffffu)), fabsf(bf2f(w4[e] >> 16))));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const int e = (mx > 0.f && mx <= 3.0e38f) ? 14 - ilogbf(mx) : 0;
+  if (lane == 0) xf[tok] = ldexpf(1.f, -e);
+  const size_t steps = (size_t)k / 32;
+  const size_t blk = (size_t)(tok / 16) * steps * 64 + (tok % 16);
+  uint4 *out = reinterpret_cast<uint4 *>(xh);
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = lane + 64 * j;
+    if (c < chunks) {
+      const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+      uint32_t h[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        h[q] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)ldexpf(bf2f(w4[q] & 0xffffu), e),
+                                                  (_Float16)ldexpf(bf2f(w4[q] >> 16), e)});
+      out[blk + ((size_t)(c / 4) * 64 + 16 * (c % 4))] = make_uint4(h[0], h[1], h[2], h[3]);
+    }
+  }
+}
+
 namespace {
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// x -> fp16 in fragment order: rows of up to 8192 columns from registers.
+void launch_x_f16(const uint16_t *x, int m, int m_pad, int k, uint16_t *xh, float *xf, hipStream_t s) {
+  const dim3 grid(m_pad / 4), block(256);
+  if (k <= 4096) hipLaunchKernelGGL(k_x_f16_reg<8>, grid, block, 0, s, x, m, m_pad, k, xh, xf);
+  else if (k <= 8192) hipLaunchKernelGGL(k_x_f16_reg<16>, grid, block, 0, s, x, m, m_pad, k, xh, xf);
+  else hipLaunchKernelGGL(k_x_f16, grid, block, 0, s, x, m, m_pad, k, xh, xf);
+}
 
 // Formats with a 256-token tile kernel of one or two stages (the fp16
 // variants exist for these): 8/12-bit one stage, 12+12, 8+8, 12+4, 8+4, with
@@ -239,7 +293,7 @@ hipError_t launch_gemm(const WView &w, const uint16_t *x, int m, float *y, void 
     const int m_pad = (m + 15) & ~15;
     uint16_t *xh = static_cast<uint16_t *>(ws);
     float *xf = reinterpret_cast<float *>(static_cast<char *>(ws) + align256((size_t)m_pad * w.k * 2));
-    hipLaunchKernelGGL(k_x_f16, dim3(m_pad / 4), dim3(256), 0, s, x, m, m_pad, w.k, xh, xf);
+    launch_x_f16(x, m, m_pad, w.k, xh, xf, s);
     a.xh = xh;
     a.xf = xf;
     a.m_pad = m_pad;
