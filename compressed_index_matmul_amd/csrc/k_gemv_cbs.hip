@@ -30,8 +30,10 @@
 // of K part q holds pairs q 64 U + l + 64 j, j < U (columns 16 pair ..
 // 16 pair + 16).  K / (1024 U) K parts and 8 / that many row sets make up
 // the 8 waves; a wave holds up to ROWS rows (ROWS x U index registers).
-// Taken for one 16-bit stage (a stage scale allowed) with one scale per
-// row, K % 1024 == 0 with K / 1024 = U times 1, 2, 4 or 8.
+// Taken for one 16-bit stage, or a 16-bit stage plus a residual stage of
+// 8-bit indices (its 4 KiB codebook in LDS beside the slice, one more pass
+// after the slices; RES), stage scales allowed, with one scale per row,
+// K % 1024 == 0 with K / 1024 = U times 1, 2, 4 or 8.
 #include <type_traits>
 
 #include "gemv_kernels.h"
@@ -57,6 +59,9 @@ struct CbsArgs {
   int slice;            // codebook entries per pass (multiple of 64, <= kCbsMaxSlice)
   int passes;           // slices covering the 65,536 entries
   float r0;             // stage scale (1 without)
+  const uint8_t *idx8;  // a residual stage of 8-bit indices [n][G], or null: none
+  const uint16_t *cb8;  // its fp16 codebook [256][8]
+  float r1;             // its stage scale
   const int8_t *signs;  // the input transform's signs, or null: none
   int mb;               // its largest block
 };
@@ -93,9 +98,10 @@ __device__ __forceinline__ float dot8(const uint4 c, const uint32_t (&x)[4], flo
   return acc;
 }
 
-template <int U, int ROWS>
+template <int U, int ROWS, bool RES>
 __global__ __launch_bounds__(kCbsWaves * 64) void k_gemv_cbs(CbsArgs a) {
   __shared__ uint4 s_cb[kCbsMaxSlice + 1];
+  __shared__ uint4 s_res[RES ? 256 : 1];  // the residual stage's codebook (4 KiB beside the slice)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -111,6 +117,10 @@ __global__ __launch_bounds__(kCbsWaves * 64) void k_gemv_cbs(CbsArgs a) {
   const int chunks = (rows_max + ROWS - 1) / ROWS;
   const uint32_t zero_off = 16u * (uint32_t)a.slice;  // the all-zero entry after the slice
   if (tid == 0) s_cb[a.slice] = make_uint4(0u, 0u, 0u, 0u);
+  // the residual codebook lands with the first barrier (LDS-direct copies
+  // among the outstanding loads make it wait for all of them)
+  if constexpr (RES)
+    if (wave < 4) lds_direct_16(reinterpret_cast<const uint4 *>(a.cb8) + wave * 64 + lane, s_res + wave * 64);
 
   const buf_t bidx = make_buf(a.idx, 2u * (uint32_t)a.n * (uint32_t)a.G);
   const uint32_t pair0 = (uint32_t)(kpart * 64 * U + lane);  // the lane's first pair of a row
@@ -315,6 +325,46 @@ __global__ __launch_bounds__(kCbsWaves * 64) void k_gemv_cbs(CbsArgs a) {
       }
       pass(0u - 16u * (uint32_t)(p * a.slice), std::true_type{});
     }
+    // The residual stage (GLQ page, "Advanced > Bit widths": a 16-bit primary
+    // plus an 8-bit residual; each stage's sum times its stage scale): one
+    // more pass over the codebook in LDS, its index bytes (the pair's two
+    // groups in one 16-bit load) loaded now into the registers the 16-bit
+    // indices held, each row taken as its loads land.
+    float acc1[RES ? ROWS : 1];
+    if constexpr (RES) {
+      const buf_t bres = make_buf(a.idx8, (uint32_t)a.n * (uint32_t)a.G);
+      uint32_t R[ROWS][U];
+#pragma unroll
+      for (int i = 0; i < ROWS; ++i) {
+        const int ri = min(blk_lo + rset + nrs * min(i0 + i, max(nr - 1, 0)), a.n - 1);
+        const uint32_t rb = (uint32_t)ri * (uint32_t)a.G;
+#pragma unroll
+        for (int j = 0; j < U; ++j) R[i][j] = buf_u16(bres, 2u * (pair0 + 64u * j), rb);
+        acc1[i] = 0.f;
+      }
+      sched_fence();
+      static_for<0, ROWS>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int later = (ROWS - 1 - i) * U;  // loads issued after row i
+        wait_vmem<(later < 63 ? later : 63)>();
+        uint4 v[2][U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          v[0][j] = s_res[R[i][j] & 0xffu];
+          v[1][j] = s_res[(R[i][j] >> 8) & 0xffu];
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          acc1[i] = dot8(v[0][j], X[j][0], acc1[i]);
+          acc1[i] = dot8(v[1][j], X[j][1], acc1[i]);
+        }
+        // the sum is made here: left free, the compiler sinks the dot
+        // products into the guarded reduction and keeps every gathered
+        // vector live until then
+        asm volatile("" : "+v"(acc1[i]));
+        sched_fence();
+      });
+    }
     // Per row: the lane's sum times its rescale factor, reduced across the
     // wave in a fixed order; the K parts of a row are then added in order
     // 0, 1, ... through LDS, times the row scale.
@@ -323,7 +373,9 @@ __global__ __launch_bounds__(kCbsWaves * 64) void k_gemv_cbs(CbsArgs a) {
 #pragma unroll
     for (int i = 0; i < ROWS; ++i) {
       if (i < nrc) {
-        const float t = wave_sum(acc[i] * f);
+        float ai = acc[i];
+        if constexpr (RES) ai = a.r0 * acc[i] + a.r1 * acc1[i];  // each stage's sum times its scale
+        const float t = wave_sum(ai * f);
         if (lane == 0) s_part[(rset * a.kp + kpart) * ROWS + i] = t;
       }
     }
@@ -337,7 +389,7 @@ __global__ __launch_bounds__(kCbsWaves * 64) void k_gemv_cbs(CbsArgs a) {
         float s = 0.f;
         for (int q = 0; q < a.kp; ++q) s += s_part[(rs * a.kp + q) * ROWS + i];
         const int r = blk_lo + rs + nrs * row_i;
-        a.y[r] = s * (h2f(a.sc[r]) * a.r0);
+        a.y[r] = s * (h2f(a.sc[r]) * (RES ? 1.f : a.r0));
       }
     }
   }
@@ -354,7 +406,8 @@ void launch_u(const CbsArgs &a0, int cus, hipStream_t s) {
   int grid = (a.n + nrs - 1) / nrs;  // at least one row per row set where possible
   if (grid > cus) grid = cus;
   a.per_wg = (a.n + grid - 1) / grid;
-  hipLaunchKernelGGL((k_gemv_cbs<U, cbs_rows<U>()>), dim3(grid), dim3(kCbsWaves * 64), 0, s, a);
+  if (a.idx8) hipLaunchKernelGGL((k_gemv_cbs<U, cbs_rows<U>(), true>), dim3(grid), dim3(kCbsWaves * 64), 0, s, a);
+  else hipLaunchKernelGGL((k_gemv_cbs<U, cbs_rows<U>(), false>), dim3(grid), dim3(kCbsWaves * 64), 0, s, a);
 }
 
 // Largest K whose fp32 copy fits the LDS for the in-kernel input transform.
@@ -377,7 +430,8 @@ int cbs_pairs(int k) {
 }  // namespace
 
 bool gemv_cbs_takes(const WView &w) {
-  if (w.S != 1 || w.sb[0] != 16 || w.nblk != 1) return false;
+  const bool res = w.S == 2 && w.sb[1] == 8;  // a residual stage of 8-bit indices
+  if ((w.S != 1 && !res) || w.sb[0] != 16 || w.nblk != 1) return false;
   if ((int64_t)w.n * w.k < ((int64_t)1 << 25)) return false;  // small weights: L2 gathers
   return cbs_pairs(w.k) != 0;
 }
@@ -402,6 +456,11 @@ bool launch_gemv_cbs(const WView &w, const void *x, int xt, float *y, int cus, h
   a.slice = kCbsMaxSlice;
   a.passes = kCbsPasses;
   a.r0 = w.rs[0];
+  if (w.S == 2) {  // the 8-bit residual stage (gemv_cbs_takes)
+    a.idx8 = w.lo[1];
+    a.cb8 = w.cb[1];
+    a.r1 = w.rs[1];
+  }
   a.signs = signs;
   a.mb = max_block;
   switch (u) {

@@ -139,3 +139,53 @@ def test_cbs_gemv_rht(vq, n, k, xdt, mb):
     rows = np.array(sorted(set(sample_rows(n, 48, mb).tolist()) | block_edges(n)))
     y_ref, bound = oracle.matmul_ref(oracle_w64(sw, rows), oracle.rht_ref(x64, signs, mb))
     assert_within(y.cpu().numpy()[:, rows], y_ref, bound, f"rht {n}x{k} {xdt} mb={mb}")
+
+
+# A 16-bit primary plus an 8-bit residual stage (GLQ page, "Advanced > Bit
+# widths": the 16 + 8 ladder) on the sliced kernel, the residual's codebook in
+# LDS beside the slice and its pass after the slices: every pairs-per-lane
+# instance (U = 4, 7, 4, 1, 2, 8), with and without stage scales, bf16 and
+# fp32 x.
+RES_CASES = [(4096, 8192, "bf16", (0.2, 0.4), 31), (8192, 28672, "f32", (0.2, 0.4), 32),
+             (4100, 16384, "bf16", None, 33), (32768, 1024, "f32", (0.5, 1.5), 34),
+             (16384, 2048, "bf16", None, 35), (512, 65536, "bf16", (0.2, 0.4), 36)]
+
+
+@pytest.mark.parametrize("n,k,xdt,ss,seed", RES_CASES)
+def test_cbs_gemv_residual(vq, n, k, xdt, ss, seed):
+    import torch
+    print(f"cbs 16+8 {n}x{k} {xdt} {ss}", flush=True)
+    sw = vqsynth.random_weight(n, k, 2, [16, 8], None, seed=100 + seed, cb_sd=(0.02, 0.02), stage_scale_range=ss)
+    xs, x64 = vqsynth.make_x(1, k, xdt, np.random.SeedSequence(200 + seed))
+    y = vq.vq_gemv(device_weight(sw), x_to_device(xs, xdt))
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set(sample_rows(n, 64, seed).tolist()) | block_edges(n)))
+    check_rows(sw, y.cpu().numpy(), x64, rows, f"16+8 {n}x{k} {xdt}")
+
+
+def test_cbs_gemv_residual_every_output(vq):
+    """Every output of a 16 + 8 weight with stage scales (4096 x 8192)."""
+    import torch
+    n, k = 4096, 8192
+    sw = vqsynth.random_weight(n, k, 2, [16, 8], None, seed=141, cb_sd=(0.02, 0.02), stage_scale_range=(0.2, 0.4))
+    xs, x64 = vqsynth.make_x(1, k, "bf16", np.random.SeedSequence(142))
+    y = vq.vq_gemv(device_weight(sw), x_to_device(xs, "bf16"))
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    for r0 in range(0, n, 1024):
+        check_rows(sw, got, x64, np.arange(r0, r0 + 1024), f"16+8 every output, rows {r0}..")
+
+
+@pytest.mark.parametrize("n,k,seed", [(4096, 8192, 51), (8192, 28672, 52)])
+def test_cbs_gemv_residual_rht_fused(vq, n, k, seed):
+    """The input transform inside the kernel, then the 16 + 8 product."""
+    import torch
+    sw = vqsynth.random_weight(n, k, 2, [16, 8], None, seed=100 + seed, cb_sd=(0.02, 0.02),
+                               stage_scale_range=(0.2, 0.4))
+    xs, x64 = vqsynth.make_x(1, k, "bf16", np.random.SeedSequence(200 + seed))
+    signs = vqsynth.make_signs(k, np.random.SeedSequence(300 + seed))
+    y = vq.vq_gemv_rht(device_weight(sw), x_to_device(xs, "bf16"), torch.from_numpy(signs).cuda(), 8192)
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set(sample_rows(n, 64, seed).tolist()) | block_edges(n)))
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw, rows), oracle.rht_ref(x64, signs, 8192))
+    assert_within(y.cpu().numpy()[:, rows], y_ref, bound, f"16+8 fused transform {n}x{k}")
