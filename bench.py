@@ -606,6 +606,7 @@ def main():
                 ("mlp70b_e8p3_rht_gemv_b1", lambda: run_decode_leg(vq, "mlp70b_e8p3", short, 3, rht=True)),
                 ("mlp70b_e8p3_rht_fused_gemv_b1", lambda: run_decode_leg(vq, "mlp70b_e8p3", short, 3,
                                                                          rht=True, fused=True)),
+                ("mlp70b_e8p4_rht_gemv_b1", lambda: run_decode_leg(vq, "mlp70b_e8p4", short, 3, rht=True)),
                 # sparse correction (0.5 % of the weights) on the Llama-3-8B format
                 ("llama8b_sparse_gemv_b1", lambda: run_decode_leg(vq, "llama8b_sparse", steps, warmup)),
                 ("llama8b_sparse_gemv_b16", lambda: run_decode_leg(vq, "llama8b_sparse", steps, warmup,

@@ -32,7 +32,8 @@
 // the 8 waves; a wave holds up to ROWS rows (ROWS x U index registers).
 // Taken for one 16-bit stage, or a 16-bit stage plus a residual stage of
 // 8-bit indices (its 4 KiB codebook in LDS beside the slice, one more pass
-// after the slices; RES), stage scales allowed, with one scale per row,
+// after the slices; RES) or of 16-bit indices (its codebook streamed through
+// the slices after the first's; ST2), stage scales allowed, one scale per row,
 // K % 1024 == 0 with K / 1024 = U times 1, 2, 4 or 8.
 #include <type_traits>
 
@@ -61,7 +62,9 @@ struct CbsArgs {
   float r0;             // stage scale (1 without)
   const uint8_t *idx8;  // a residual stage of 8-bit indices [n][G], or null: none
   const uint16_t *cb8;  // its fp16 codebook [256][8]
-  float r1;             // its stage scale
+  const uint16_t *idx2; // or a second stage of 16-bit indices [n][G], or null: none
+  const uint16_t *cb2;  // its fp16 codebook [65536][8]
+  float r1;             // the second stage's scale (nonzero with idx2)
   const int8_t *signs;  // the input transform's signs, or null: none
   int mb;               // its largest block
 };
@@ -98,8 +101,11 @@ __device__ __forceinline__ float dot8(const uint4 c, const uint32_t (&x)[4], flo
   return acc;
 }
 
-template <int U, int ROWS, bool RES>
+// MODE 0: one 16-bit stage; 1: plus an 8-bit residual stage (RES); 2: plus
+// a second 16-bit stage (ST2), streamed through the slices after the first.
+template <int U, int ROWS, int MODE>
 __global__ __launch_bounds__(kCbsWaves * 64) void k_gemv_cbs(CbsArgs a) {
+  constexpr bool RES = MODE == 1, ST2 = MODE == 2;
   __shared__ uint4 s_cb[kCbsMaxSlice + 1];
   __shared__ uint4 s_res[RES ? 256 : 1];  // the residual stage's codebook (4 KiB beside the slice)
   const int tid = threadIdx.x;
@@ -123,17 +129,18 @@ __global__ __launch_bounds__(kCbsWaves * 64) void k_gemv_cbs(CbsArgs a) {
     if (wave < 4) lds_direct_16(reinterpret_cast<const uint4 *>(a.cb8) + wave * 64 + lane, s_res + wave * 64);
 
   const buf_t bidx = make_buf(a.idx, 2u * (uint32_t)a.n * (uint32_t)a.G);
+  const buf_t bidx2 = make_buf(ST2 ? a.idx2 : a.idx, 2u * (uint32_t)a.n * (uint32_t)a.G);
   const uint32_t pair0 = (uint32_t)(kpart * 64 * U + lane);  // the lane's first pair of a row
   const uint4 *cb = reinterpret_cast<const uint4 *>(a.cb);
 
   // Slice p into LDS: 64 entries per wave and LDS-direct load (lane l's 16
   // bytes at the wave's LDS base + 16 l).  The last slice may end early:
   // lanes past entry 65535 reload it into slots no index reaches.
-  auto stage = [&](int p) {
+  auto stage = [&](int p, const uint4 *cbp) {
     const int e0 = p * a.slice;
     for (int c = wave; c * 64 < a.slice; c += kCbsWaves) {  // wave-uniform
       const int e = min(e0 + c * 64 + lane, 65535);
-      lds_direct_16(cb + e, s_cb + c * 64);
+      lds_direct_16(cbp + e, s_cb + c * 64);
     }
   };
 
@@ -293,19 +300,23 @@ __global__ __launch_bounds__(kCbsWaves * 64) void k_gemv_cbs(CbsArgs a) {
     // Slice 0 lands before the index loads are issued: the barrier's release
     // fence waits for every outstanding load once the LDS-direct copies are
     // among them, so only the slice is outstanding here.
-    stage(0);
+    stage(0, cb);
     __syncthreads();
     // index loads of the chunk's rows (past the wave's last row: that row
     // again, or any valid row for a wave without rows; never used)
+    auto load_idx = [&](const buf_t bi) {
 #pragma unroll
-    for (int i = 0; i < ROWS; ++i) {
-      const int ri = min(blk_lo + rset + nrs * min(i0 + i, max(nr - 1, 0)), a.n - 1);
-      const uint32_t rb = 2u * (uint32_t)ri * (uint32_t)a.G;
+      for (int i = 0; i < ROWS; ++i) {
+        const int ri = min(blk_lo + rset + nrs * min(i0 + i, max(nr - 1, 0)), a.n - 1);
+        const uint32_t rb = 2u * (uint32_t)ri * (uint32_t)a.G;
 #pragma unroll
-      for (int j = 0; j < U; ++j) I[i][j] = buf_u32(bidx, 4u * (pair0 + 64u * j), rb);
-      acc[i] = 0.f;
-    }
-    sched_fence();
+        for (int j = 0; j < U; ++j) I[i][j] = buf_u32(bi, 4u * (pair0 + 64u * j), rb);
+      }
+      sched_fence();
+    };
+    load_idx(bidx);
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) acc[i] = 0.f;
     // Pass 0 takes each row as its indices arrive (the loads after row i
     // may still be in flight), so it overlaps the index stream from HBM.
     // Every pass runs all ROWS rows without a branch (rows past the wave's
@@ -316,12 +327,28 @@ __global__ __launch_bounds__(kCbsWaves * 64) void k_gemv_cbs(CbsArgs a) {
     // loads are no-ops once the loads have landed, and a single copy keeps
     // the kernel small enough that the instruction cache holds it beside
     // the other kernels of a decode step.
-    for (int p = 0; p < a.passes; ++p) {
-      if (p > 0) {
-        __syncthreads();  // every wave is done with slice p - 1
-        stage(p);
+    // With a second 16-bit stage (ST2) its slices follow the first stage's;
+    // at the switch its indices are loaded into the same registers, and the
+    // row sums so far are multiplied by r0 / r1, so that the stages share one
+    // accumulator and the final r1 gives r0 (stage 0) + r1 (stage 1).
+    const int npass = ST2 ? 2 * a.passes : a.passes;
+    for (int q = 0; q < npass; ++q) {
+      int p = q;
+      if constexpr (ST2) p = q < a.passes ? q : q - a.passes;
+      if (q > 0) {
+        __syncthreads();  // every wave is done with the previous slice
+        if constexpr (ST2) stage(p, q < a.passes ? cb : reinterpret_cast<const uint4 *>(a.cb2));
+        else stage(p, cb);
         wait_vmem<0>();
         __syncthreads();
+        if constexpr (ST2) {
+          if (q == a.passes) {  // uniform
+            load_idx(bidx2);
+            const float fold = a.r0 / a.r1;
+#pragma unroll
+            for (int i = 0; i < ROWS; ++i) acc[i] *= fold;
+          }
+        }
       }
       pass(0u - 16u * (uint32_t)(p * a.slice), std::true_type{});
     }
@@ -389,7 +416,7 @@ __global__ __launch_bounds__(kCbsWaves * 64) void k_gemv_cbs(CbsArgs a) {
         float s = 0.f;
         for (int q = 0; q < a.kp; ++q) s += s_part[(rs * a.kp + q) * ROWS + i];
         const int r = blk_lo + rs + nrs * row_i;
-        a.y[r] = s * (h2f(a.sc[r]) * (RES ? 1.f : a.r0));
+        a.y[r] = s * (h2f(a.sc[r]) * (RES ? 1.f : ST2 ? a.r1 : a.r0));
       }
     }
   }
@@ -406,8 +433,9 @@ void launch_u(const CbsArgs &a0, int cus, hipStream_t s) {
   int grid = (a.n + nrs - 1) / nrs;  // at least one row per row set where possible
   if (grid > cus) grid = cus;
   a.per_wg = (a.n + grid - 1) / grid;
-  if (a.idx8) hipLaunchKernelGGL((k_gemv_cbs<U, cbs_rows<U>(), true>), dim3(grid), dim3(kCbsWaves * 64), 0, s, a);
-  else hipLaunchKernelGGL((k_gemv_cbs<U, cbs_rows<U>(), false>), dim3(grid), dim3(kCbsWaves * 64), 0, s, a);
+  if (a.idx8) hipLaunchKernelGGL((k_gemv_cbs<U, cbs_rows<U>(), 1>), dim3(grid), dim3(kCbsWaves * 64), 0, s, a);
+  else if (a.idx2) hipLaunchKernelGGL((k_gemv_cbs<U, cbs_rows<U>(), 2>), dim3(grid), dim3(kCbsWaves * 64), 0, s, a);
+  else hipLaunchKernelGGL((k_gemv_cbs<U, cbs_rows<U>(), 0>), dim3(grid), dim3(kCbsWaves * 64), 0, s, a);
 }
 
 // Largest K whose fp32 copy fits the LDS for the in-kernel input transform.
@@ -430,8 +458,8 @@ int cbs_pairs(int k) {
 }  // namespace
 
 bool gemv_cbs_takes(const WView &w) {
-  const bool res = w.S == 2 && w.sb[1] == 8;  // a residual stage of 8-bit indices
-  if ((w.S != 1 && !res) || w.sb[0] != 16 || w.nblk != 1) return false;
+  const bool two = w.S == 2 && (w.sb[1] == 8 || w.sb[1] == 16);  // an 8- or 16-bit second stage
+  if ((w.S != 1 && !two) || w.sb[0] != 16 || w.nblk != 1) return false;
   if ((int64_t)w.n * w.k < ((int64_t)1 << 25)) return false;  // small weights: L2 gathers
   return cbs_pairs(w.k) != 0;
 }
@@ -456,9 +484,13 @@ bool launch_gemv_cbs(const WView &w, const void *x, int xt, float *y, int cus, h
   a.slice = kCbsMaxSlice;
   a.passes = kCbsPasses;
   a.r0 = w.rs[0];
-  if (w.S == 2) {  // the 8-bit residual stage (gemv_cbs_takes)
+  if (w.S == 2 && w.sb[1] == 8) {  // an 8-bit residual stage (gemv_cbs_takes)
     a.idx8 = w.lo[1];
     a.cb8 = w.cb[1];
+    a.r1 = w.rs[1];
+  } else if (w.S == 2 && w.rs[1] != 0.f) {  // a second 16-bit stage (one scaled by 0 adds nothing)
+    a.idx2 = w.i16[1];
+    a.cb2 = w.cb[1];
     a.r1 = w.rs[1];
   }
   a.signs = signs;

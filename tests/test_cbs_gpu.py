@@ -189,3 +189,53 @@ def test_cbs_gemv_residual_rht_fused(vq, n, k, seed):
     rows = np.array(sorted(set(sample_rows(n, 64, seed).tolist()) | block_edges(n)))
     y_ref, bound = oracle.matmul_ref(oracle_w64(sw, rows), oracle.rht_ref(x64, signs, 8192))
     assert_within(y.cpu().numpy()[:, rows], y_ref, bound, f"16+8 fused transform {n}x{k}")
+
+
+# Two 16-bit stages (GLQ page, "Advanced > Bit widths": the 16 + 16 ladder):
+# the second stage's codebook streams through the slices after the first's,
+# its indices loaded into the same registers at the switch.  A second stage
+# scaled by 0 adds nothing and runs as one stage.
+ST2_CASES = [(4096, 8192, "bf16", (0.2, 0.4), 61), (8192, 28672, "f32", None, 62),
+             (32768, 1024, "bf16", (0.5, 1.5), 63), (512, 65536, "f32", (0.2, 0.4), 64)]
+
+
+@pytest.mark.parametrize("n,k,xdt,ss,seed", ST2_CASES)
+def test_cbs_gemv_two_16bit_stages(vq, n, k, xdt, ss, seed):
+    import torch
+    print(f"cbs 16+16 {n}x{k} {xdt} {ss}", flush=True)
+    sw = vqsynth.random_weight(n, k, 2, [16, 16], None, seed=100 + seed, cb_sd=(0.02, 0.006), stage_scale_range=ss)
+    xs, x64 = vqsynth.make_x(1, k, xdt, np.random.SeedSequence(200 + seed))
+    y = vq.vq_gemv(device_weight(sw), x_to_device(xs, xdt))
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set(sample_rows(n, 64, seed).tolist()) | block_edges(n)))
+    check_rows(sw, y.cpu().numpy(), x64, rows, f"16+16 {n}x{k} {xdt}")
+
+
+def test_cbs_gemv_two_16bit_stages_every_output(vq):
+    """Every output of a 16 + 16 weight with stage scales (4096 x 8192),
+    and the same weight with the second stage scaled by 0."""
+    import torch
+    n, k = 4096, 8192
+    sw = vqsynth.random_weight(n, k, 2, [16, 16], None, seed=171, cb_sd=(0.02, 0.02), stage_scale_range=(0.2, 0.4))
+    xs, x64 = vqsynth.make_x(1, k, "bf16", np.random.SeedSequence(172))
+    for r1 in (None, 0.0):
+        if r1 is not None:
+            sw.stage_scales = np.array([sw.stage_scales[0], r1], np.float32)
+        y = vq.vq_gemv(device_weight(sw), x_to_device(xs, "bf16"))
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        for r0 in range(0, n, 1024):
+            check_rows(sw, got, x64, np.arange(r0, r0 + 1024), f"16+16 r1={r1} rows {r0}..")
+
+
+def test_cbs_gemv_two_16bit_stages_rht_fused(vq):
+    import torch
+    n, k = 8192, 28672
+    sw = vqsynth.random_weight(n, k, 2, [16, 16], None, seed=181, cb_sd=(0.02, 0.02), stage_scale_range=(0.2, 0.4))
+    xs, x64 = vqsynth.make_x(1, k, "bf16", np.random.SeedSequence(182))
+    signs = vqsynth.make_signs(k, np.random.SeedSequence(183))
+    y = vq.vq_gemv_rht(device_weight(sw), x_to_device(xs, "bf16"), torch.from_numpy(signs).cuda(), 8192)
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set(sample_rows(n, 64, 184).tolist()) | block_edges(n)))
+    y_ref, bound = oracle.matmul_ref(oracle_w64(sw, rows), oracle.rht_ref(x64, signs, 8192))
+    assert_within(y.cpu().numpy()[:, rows], y_ref, bound, "16+16 fused transform")

@@ -42,6 +42,7 @@ scales, drawn after everything else so the formats above are unchanged):
                      primary and an 8-bit residual stage whose codebook has
                      the primary's spread, brought down by a residual scale
                      drawn from U(0.2, 0.4); input transform as mlp70b.
+* ``mlp70b_e8p4``    the same with a 16-bit residual stage (GLQ's 4 bpw ladder).
 """
 
 from __future__ import annotations
@@ -114,6 +115,9 @@ WORKLOADS: Dict[str, dict] = {
                             batches=(1, 16), rht=None, seed=9, lowrank=32),
     "mlp70b_e8p3": dict(shapes=[("gate_up", 28672, 8192), ("down", 8192, 28672)], stages=2, bits=(16, 8),
                         cb_sd=(0.02, 0.02), scale_block=None, x_dtype="bf16", batches=(1,), rht=8192, seed=7,
+                        stage_scales=(0.2, 0.4)),
+    "mlp70b_e8p4": dict(shapes=[("gate_up", 28672, 8192), ("down", 8192, 28672)], stages=2, bits=(16, 16),
+                        cb_sd=(0.02, 0.02), scale_block=None, x_dtype="bf16", batches=(1,), rht=8192, seed=10,
                         stage_scales=(0.2, 0.4)),
 }
 
