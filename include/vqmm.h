@@ -354,8 +354,8 @@ int rht_apply_shards(const void *x, int32_t x_dtype, int32_t batch, int32_t n, i
  * for 1..16 tokens, with no buffer for the transformed x: every workgroup
  * transforms its own copy in LDS.  Taken for the weights the 16-bit decode
  * kernels serve, without a sparse or low-rank correction:
- *  - one 16-bit stage, or a 16-bit stage plus one 8-bit residual stage,
- *    stage scales allowed, with one scale per row, n_out * k_in >= 2^25,
+ *  - one 16-bit stage, or a 16-bit stage plus one 8- or 16-bit residual
+ *    stage, stage scales allowed, with one scale per row, n_out * k_in >= 2^25,
  *    k_in a multiple of 1024 up to 37632 whose 1024-column count is 1, 2, 4
  *    or 8 times one of 1, 2, 4, 7, 8 (the codebook-sliced kernel), or
  *  - a 16-bit first stage, at most one 8- or 16-bit residual stage, stage
