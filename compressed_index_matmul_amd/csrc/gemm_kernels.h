@@ -1408,10 +1408,31 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_few(GemmArgs a, int units
       }
     }
   };
+  // With two or more token blocks, x of a pair of K steps (2u, 2u + 1) is
+  // loaded with the odd token rows taking the other step first, so that each
+  // load reads both halves of the 128-byte lines of its sixteen rows (every
+  // row reading the same half costs the stream up to 30 %); swap_pair puts
+  // the steps back in place before their use.  One block (16 tokens or
+  // fewer) keeps the plain order: it gained nothing at 16 tokens, and with
+  // fewer the rows past the last token (which repeat it) would touch both
+  // halves of its lines.
+  constexpr bool kPair = TB >= 2;
+  const bool odd_row = (r16 & 1) != 0;
   auto load_step = [&](int i, FewStep<TB> &X) {
-    const int ks = ks0 + min(i, steps - 1);
+    const int ks = ks0 + min(i, steps - 1);  // ks0 is even
+    const uint32_t sel = kPair ? (uint32_t)(ks & 1) ^ (uint32_t)odd_row : 0u;
+    const uint32_t kb = kPair ? (uint32_t)(ks & ~1) : (uint32_t)ks;
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) X.av[tb] = buf_u128(bx, vx[tb], 64u * ks);
+    for (int tb = 0; tb < TB; ++tb) X.av[tb] = buf_u128(bx, vx[tb] + 64u * sel, 64u * kb);
+  };
+  auto swap_pair = [&](FewStep<TB> &A, FewStep<TB> &B) {
+    if constexpr (!kPair) return;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const uint4 u = A.av[tb], v = B.av[tb];
+      A.av[tb] = odd_row ? v : u;
+      B.av[tb] = odd_row ? u : v;
+    }
   };
   // decode the lane's group in step s (0..3) of quad Q and multiply with
   // every token block
@@ -1484,18 +1505,22 @@ __global__ __launch_bounds__(kSWaves * 64) void k_gemm_few(GemmArgs a, int units
       sched_fence();
       const int k = 8 * i;
       load_step(k + 3, X3);
+      swap_pair(X0, X1);
       step(Q0, 0, X0);
       load_step(k + 4, X0);
       step(Q0, 1, X1);
       load_step(k + 5, X1);
+      swap_pair(X2, X3);
       step(Q0, 2, X2);
       load_step(k + 6, X2);
       step(Q0, 3, X3);
       load_step(k + 7, X3);
+      swap_pair(X0, X1);
       step(Q1, 0, X0);
       load_step(k + 8, X0);
       step(Q1, 1, X1);
       load_step(k + 9, X1);
+      swap_pair(X2, X3);
       step(Q1, 2, X2);
       load_step(k + 10, X2);
       step(Q1, 3, X3);
